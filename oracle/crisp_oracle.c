@@ -1,0 +1,460 @@
+/*
+ * CRISP sparse-prefill oracle: a plain, slow CPU implementation written from
+ * the paper "CRISP: Cliff-awaRe Input-adaptive Sparse Prefilling with
+ * Structural-Mass-Motivated Routing" (arXiv 2609.01925).
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the test-suite, the smoke check and the
+ * benchmark's CPU-baseline leg may load this library.  The HIP library never
+ * links, includes or calls it, and it shares no source with that library.
+ *
+ * Arithmetic: bf16 inputs are widened exactly; every score, softmax, sum and
+ * attention output is computed in IEEE double.  Where a floating-point value
+ * decides an integer result (the routing bit, a selected block, the PE
+ * cut-off), the decision is taken on the value rounded to float, with the
+ * threshold formula evaluated in float in the order the paper writes it --
+ * the precision the GPU kernels decide in.
+ *
+ * Layouts: Q is [hq][n][d], K and V are [hkv][n][d], row-major bf16 bit
+ * patterns (uint16).  Query head h reads KV head h / (hq / hkv).
+ *
+ * Pins: every function here is checked by tests against brute force in numpy,
+ * closed forms and invariants (see the test-suite); none is "parity unpinned".
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+static float bf16_to_f32(uint16_t b)
+{
+    uint32_t u = (uint32_t)b << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return f;
+}
+
+/* Widen one [n][d] slab of bf16 to float (exact). */
+static float *widen(const uint16_t *src, int64_t count)
+{
+    float *dst = (float *)malloc((size_t)count * sizeof(float));
+    if (!dst) return NULL;
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < count; ++i) dst[i] = bf16_to_f32(src[i]);
+    return dst;
+}
+
+static double dot(const float *a, const float *b, int d)
+{
+    double s = 0.0;
+    for (int c = 0; c < d; ++c) s += (double)a[c] * (double)b[c];
+    return s;
+}
+
+/*
+ * Proxy attention of one query head (Alg. 2, lines 3-5): the representative
+ * query block Q^ is the last b = B query rows; A^ = Softmax(Q^ K^T / sqrt(d)).
+ * Causal reading: row i sits at position q_i = n - B + i and sees keys
+ * k <= q_i; entries with k > q_i are exactly 0.
+ * Output ahat is [B][n], doubles.
+ */
+static void proxy_rows(const float *qh, const float *kg, int n, int d, int B, double *ahat)
+{
+    const double scale = 1.0 / sqrt((double)d);
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int i = 0; i < B; ++i) {
+        const int64_t qi = (int64_t)n - B + i;
+        const float *qrow = qh + qi * d;
+        double *row = ahat + (int64_t)i * n;
+        double m = -INFINITY;
+        for (int64_t k = 0; k <= qi; ++k) {
+            double s = scale * dot(qrow, kg + k * d, d);
+            row[k] = s;
+            if (s > m) m = s;
+        }
+        double l = 0.0;
+        for (int64_t k = 0; k <= qi; ++k) {
+            row[k] = exp(row[k] - m);
+            l += row[k];
+        }
+        for (int64_t k = 0; k <= qi; ++k) row[k] /= l;
+        for (int64_t k = qi + 1; k < n; ++k) row[k] = 0.0;
+    }
+}
+
+/*
+ * Directional block scores (Alg. 3, lines 3 and 5) and C_struct (Eq. 2).
+ *   a_v = colmean(A^): a_v[k] = (1/B) sum_i A^[i,k]
+ *   a_s = diagmean(A^): the diagonal through (i,k) is indexed by the key it
+ *         meets in the last query row, sigma = k + (B-1-i), so that slash
+ *         position n-1 is offset 0 (recency) and position 0 the farthest
+ *         diagonal (sink region); a_s[sigma] = (1/B) sum over valid (i,k).
+ *   p_d = blockpool(a_d): sum over the B positions of each block.
+ *   C_struct = (1/B) sum_i sum_{k in anchor} A^[i,k], anchor = first w_sink
+ *              keys and last w_local keys (a set: overlaps counted once).
+ */
+static void block_scores(const double *ahat, int n, int B, int w_sink, int w_local,
+                         double *pv, double *ps, double *cstruct)
+{
+    const int nb = n / B;
+#pragma omp parallel for schedule(static)
+    for (int j = 0; j < nb; ++j) {
+        double sv = 0.0, ss = 0.0;
+        for (int i = 0; i < B; ++i) {
+            const int64_t qi = (int64_t)n - B + i;
+            const double *row = ahat + (int64_t)i * n;
+            for (int c = 0; c < B; ++c) {
+                int64_t k = (int64_t)j * B + c;
+                sv += row[k]; /* zero where k > q_i */
+                int64_t sigma = (int64_t)j * B + c;
+                int64_t kk = sigma - (B - 1 - i);
+                if (kk >= 0 && kk <= qi) ss += row[kk];
+            }
+        }
+        pv[j] = sv / B;
+        ps[j] = ss / B;
+    }
+    double cs = 0.0;
+    for (int i = 0; i < B; ++i) {
+        const double *row = ahat + (int64_t)i * n;
+        for (int64_t k = 0; k < n; ++k)
+            if (k < w_sink || k >= (int64_t)n - w_local) cs += row[k];
+    }
+    *cstruct = cs / B;
+}
+
+/* Single-head proxy map, exported for the brute-force pins. */
+int orc_proxy_map(const uint16_t *q, const uint16_t *k, int n, int hq, int hkv, int d, int B,
+                  int h, double *ahat)
+{
+    if (n < B || n % B || hq % hkv || h < 0 || h >= hq) return 1;
+    const int g = h / (hq / hkv);
+    float *qh = widen(q + (int64_t)h * n * d, (int64_t)n * d);
+    float *kg = widen(k + (int64_t)g * n * d, (int64_t)n * d);
+    if (!qh || !kg) { free(qh); free(kg); return 2; }
+    proxy_rows(qh, kg, n, d, B, ahat);
+    free(qh);
+    free(kg);
+    return 0;
+}
+
+int orc_block_scores(const double *ahat, int n, int B, int w_sink, int w_local,
+                     double *pv, double *ps, double *cstruct)
+{
+    if (n < B || n % B) return 1;
+    block_scores(ahat, n, B, w_sink, w_local, pv, ps, cstruct);
+    return 0;
+}
+
+/*
+ * PatSearch (Alg. 2) for every query head: proxy map, block scores,
+ * C_struct (Eq. 2) and the routing rule "VS iff C_struct >= tau_proxy"
+ * (Alg. 2, lines 9-13), the comparison taken in float.
+ * pattern: 1 = VS, 0 = PE.
+ */
+int orc_route(const uint16_t *q, const uint16_t *k, int n, int hq, int hkv, int d, int B,
+              float tau, int w_sink, int w_local,
+              double *pv, double *ps, double *cstruct, uint8_t *pattern)
+{
+    if (n < B || n % B || hq % hkv) return 1;
+    const int nb = n / B, G = hq / hkv;
+    double *ahat = (double *)malloc((size_t)B * n * sizeof(double));
+    float *qlast = (float *)malloc((size_t)n * d * sizeof(float));
+    if (!ahat || !qlast) { free(ahat); free(qlast); return 2; }
+    for (int g = 0; g < hkv; ++g) {
+        float *kg = widen(k + (int64_t)g * n * d, (int64_t)n * d);
+        if (!kg) { free(ahat); free(qlast); return 2; }
+        for (int h = g * G; h < (g + 1) * G; ++h) {
+            /* only the last B query rows are read; widen those */
+            const uint16_t *qh = q + (int64_t)h * n * d;
+            for (int64_t e = (int64_t)(n - B) * d; e < (int64_t)n * d; ++e)
+                qlast[e] = bf16_to_f32(qh[e]);
+            proxy_rows(qlast, kg, n, d, B, ahat);
+            block_scores(ahat, n, B, w_sink, w_local, pv + (int64_t)h * nb, ps + (int64_t)h * nb,
+                         cstruct + h);
+            pattern[h] = ((float)cstruct[h] >= tau) ? 1 : 0;
+        }
+        free(kg);
+    }
+    free(ahat);
+    free(qlast);
+    return 0;
+}
+
+/* ---- ordering helpers: (value desc, index asc) on float-rounded values ---- */
+typedef struct { float v; int64_t i; } vi_t;
+
+static int cmp_desc(const void *a, const void *b)
+{
+    const vi_t *x = (const vi_t *)a, *y = (const vi_t *)b;
+    if (x->v > y->v) return -1;
+    if (x->v < y->v) return 1;
+    return (x->i < y->i) ? -1 : (x->i > y->i);
+}
+
+static int cmp_int(const void *a, const void *b)
+{
+    int32_t x = *(const int32_t *)a, y = *(const int32_t *)b;
+    return (x > y) - (x < y);
+}
+
+/*
+ * Sink-aware selection in one direction (Alg. 3, lines 7-12; Eq. 3 and 4):
+ *   r = max(1 - p[0] - p[Nb-1], 0);  mu = r / (Nb - 2);  theta = alpha * mu
+ *   k = #{j : p[j] > theta}, counted over all Nb blocks
+ *   k = clip(k, k_min, Nb);  S = top-k(p), ties to the lower block index.
+ * All in float, in that order.  Writes the selected blocks in ascending
+ * order to sel and returns their number; theta_out receives theta and
+ * kth_out the k-th largest value (the decisive value when the clip binds).
+ * Nb <= 2 (mu undefined): every block is selected.
+ */
+int orc_vs_select(const double *p, int nb, float alpha, int kmin, int32_t *sel,
+                  float *theta_out, float *kth_out, int *clipped_out)
+{
+    if (nb <= 2) {
+        for (int j = 0; j < nb; ++j) sel[j] = j;
+        *theta_out = 0.0f;
+        *kth_out = 0.0f;
+        *clipped_out = 0;
+        return nb;
+    }
+    float *pf = (float *)malloc((size_t)nb * sizeof(float));
+    vi_t *ord = (vi_t *)malloc((size_t)nb * sizeof(vi_t));
+    for (int j = 0; j < nb; ++j) pf[j] = (float)p[j];
+    float r = 1.0f - pf[0];
+    r = r - pf[nb - 1];
+    if (r < 0.0f) r = 0.0f;
+    float mu = r / (float)(nb - 2);
+    float theta = alpha * mu;
+    int count = 0;
+    for (int j = 0; j < nb; ++j) count += (pf[j] > theta);
+    int kk = count < kmin ? kmin : count;
+    if (kk > nb) kk = nb;
+    for (int j = 0; j < nb; ++j) { ord[j].v = pf[j]; ord[j].i = j; }
+    qsort(ord, nb, sizeof(vi_t), cmp_desc);
+    for (int t = 0; t < kk; ++t) sel[t] = (int32_t)ord[t].i;
+    qsort(sel, kk, sizeof(int32_t), cmp_int);
+    *theta_out = theta;
+    *kth_out = ord[kk - 1].v;
+    *clipped_out = (count < kk);
+    free(pf);
+    free(ord);
+    return kk;
+}
+
+/*
+ * Cumulative-gamma selection in one direction, the FlexPrefill rule the
+ * paper compares against (Alg. 6, lines 2-5): p already sums to one, order
+ * it (desc, ties to the lower index), keep the shortest prefix whose
+ * running sum reaches gamma.  kmin > 0 additionally clips the size to at
+ * least kmin (FlexPrefill as configured in Section 5, "Setup").
+ */
+int orc_gamma_select(const double *p, int nb, float gamma, int kmin, int32_t *sel)
+{
+    vi_t *ord = (vi_t *)malloc((size_t)nb * sizeof(vi_t));
+    for (int j = 0; j < nb; ++j) { ord[j].v = (float)p[j]; ord[j].i = j; }
+    qsort(ord, nb, sizeof(vi_t), cmp_desc);
+    double cum = 0.0;
+    int kk = nb;
+    for (int t = 0; t < nb; ++t) {
+        cum += (double)ord[t].v;
+        if (cum >= (double)gamma) { kk = t + 1; break; }
+    }
+    if (kk < kmin) kk = kmin < nb ? kmin : nb;
+    for (int t = 0; t < kk; ++t) sel[t] = (int32_t)ord[t].i;
+    qsort(sel, kk, sizeof(int32_t), cmp_int);
+    free(ord);
+    return kk;
+}
+
+/*
+ * Pooled map of one query head for the PE path (Alg. 4, lines 3-6):
+ *   Qbar[qb] = mean of Q over the B tokens of query block qb (all queries),
+ *   Kbar[kb] = mean of K over key block kb,
+ *   Abar = row softmax of Qbar Kbar^T / sqrt(d) over the causal key blocks
+ *          kb <= qb (entries kb > qb are 0),
+ *   Abar = Abar / sum(Abar).
+ * abar is [Nb][Nb], doubles.
+ */
+int orc_pe_map(const uint16_t *q, const uint16_t *k, int n, int hq, int hkv, int d, int B,
+               int h, double *abar)
+{
+    if (n < B || n % B || hq % hkv || h < 0 || h >= hq) return 1;
+    const int nb = n / B, g = h / (hq / hkv);
+    const double scale = 1.0 / sqrt((double)d);
+    double *qbar = (double *)calloc((size_t)nb * d, sizeof(double));
+    double *kbar = (double *)calloc((size_t)nb * d, sizeof(double));
+    if (!qbar || !kbar) { free(qbar); free(kbar); return 2; }
+    const uint16_t *qh = q + (int64_t)h * n * d, *kg = k + (int64_t)g * n * d;
+#pragma omp parallel for schedule(static)
+    for (int b = 0; b < nb; ++b) {
+        for (int t = 0; t < B; ++t) {
+            int64_t pos = (int64_t)b * B + t;
+            for (int c = 0; c < d; ++c) {
+                qbar[(int64_t)b * d + c] += (double)bf16_to_f32(qh[pos * d + c]);
+                kbar[(int64_t)b * d + c] += (double)bf16_to_f32(kg[pos * d + c]);
+            }
+        }
+        for (int c = 0; c < d; ++c) {
+            qbar[(int64_t)b * d + c] /= B;
+            kbar[(int64_t)b * d + c] /= B;
+        }
+    }
+#pragma omp parallel for schedule(dynamic, 4)
+    for (int qb = 0; qb < nb; ++qb) {
+        double *row = abar + (int64_t)qb * nb;
+        double m = -INFINITY;
+        for (int kb = 0; kb <= qb; ++kb) {
+            double s = 0.0;
+            for (int c = 0; c < d; ++c) s += qbar[(int64_t)qb * d + c] * kbar[(int64_t)kb * d + c];
+            row[kb] = scale * s;
+            if (row[kb] > m) m = row[kb];
+        }
+        double l = 0.0;
+        for (int kb = 0; kb <= qb; ++kb) { row[kb] = exp(row[kb] - m); l += row[kb]; }
+        for (int kb = 0; kb <= qb; ++kb) row[kb] /= l;
+        for (int kb = qb + 1; kb < nb; ++kb) row[kb] = 0.0;
+    }
+    double total = 0.0;
+    for (int64_t e = 0; e < (int64_t)nb * nb; ++e) total += abar[e];
+    for (int64_t e = 0; e < (int64_t)nb * nb; ++e) abar[e] /= total;
+    free(qbar);
+    free(kbar);
+    return 0;
+}
+
+/*
+ * gamma-cumsum over the flattened pooled map (Alg. 4, lines 8-10):
+ * order the causal entries by (value desc, flat index qb*Nb+kb asc) on the
+ * float-rounded values, K* = min{k : running sum >= gamma}, S = first K*.
+ * selmask[qb*Nb+kb] = 1 for the selected entries.  Returns K*; vstar gets
+ * the K*-th value and cum_before the running sum of the first K*-1 entries.
+ */
+int64_t orc_pe_select(const double *abar, int nb, float gamma, uint8_t *selmask,
+                      float *vstar, double *cum_before)
+{
+    const int64_t ncausal = (int64_t)nb * (nb + 1) / 2;
+    vi_t *ord = (vi_t *)malloc((size_t)ncausal * sizeof(vi_t));
+    int64_t t = 0;
+    for (int qb = 0; qb < nb; ++qb)
+        for (int kb = 0; kb <= qb; ++kb) {
+            ord[t].v = (float)abar[(int64_t)qb * nb + kb];
+            ord[t].i = (int64_t)qb * nb + kb;
+            ++t;
+        }
+    qsort(ord, ncausal, sizeof(vi_t), cmp_desc);
+    double cum = 0.0, before = 0.0;
+    int64_t kstar = ncausal;
+    for (t = 0; t < ncausal; ++t) {
+        before = cum;
+        cum += (double)ord[t].v;
+        if (cum >= (double)gamma) { kstar = t + 1; break; }
+    }
+    memset(selmask, 0, (size_t)nb * nb);
+    for (t = 0; t < kstar; ++t) selmask[ord[t].i] = 1;
+    *vstar = ord[kstar - 1].v;
+    *cum_before = before;
+    free(ord);
+    return kstar;
+}
+
+/*
+ * Block index lists of one head: the mask M_S of Eq. 1 at block level.
+ * VS (Alg. 3, line 14): S_v holds key-block columns; S_s holds slash blocks,
+ *   slash block j being the diagonal band of offset block Nb-1-j, which for
+ *   query block qb lands on key block qb-(Nb-1-j); {0, Nb-1} are the sink
+ *   column and the recency diagonal (key block qb).
+ *   R(qb) = sorted unique {0, qb} u {v in S_v : v <= qb}
+ *           u {qb-(Nb-1-j) : j in S_s, qb-(Nb-1-j) >= 0}.
+ * PE (Alg. 4 plus the first and last blocks, as VS):
+ *   R(qb) = {kb : selmask[qb][kb]} u {0, qb}.
+ * row_ptr gets Nb+1 offsets starting at base; returns the entry count.
+ */
+int64_t orc_expand(int nb, int vs, const int32_t *sv, int nv, const int32_t *ss, int ns,
+                   const uint8_t *pe_mask, int64_t base, int32_t *row_ptr, int32_t *col_idx)
+{
+    uint8_t *mark = (uint8_t *)malloc((size_t)nb);
+    int64_t pos = base;
+    for (int qb = 0; qb < nb; ++qb) {
+        memset(mark, 0, (size_t)nb);
+        mark[0] = 1;
+        mark[qb] = 1;
+        if (vs) {
+            for (int t = 0; t < nv; ++t)
+                if (sv[t] <= qb) mark[sv[t]] = 1;
+            for (int t = 0; t < ns; ++t) {
+                int kb = qb - (nb - 1 - ss[t]);
+                if (kb >= 0) mark[kb] = 1;
+            }
+        } else {
+            for (int kb = 0; kb <= qb; ++kb)
+                if (pe_mask[(int64_t)qb * nb + kb]) mark[kb] = 1;
+        }
+        row_ptr[qb] = (int32_t)pos;
+        for (int kb = 0; kb <= qb; ++kb)
+            if (mark[kb]) col_idx[pos++] = kb;
+    }
+    row_ptr[nb] = (int32_t)pos;
+    free(mark);
+    return pos - base;
+}
+
+/*
+ * Masked attention, Eq. 1: O = Softmax(Q K^T / sqrt(d) + M_S) V, where for a
+ * query at position t in block qb the allowed keys are the tokens of the
+ * listed key blocks that are not in its future (k <= t).
+ * row_ptr is [hq][Nb+1] (absolute offsets into col_idx); rows lists the
+ * (h*Nb + qb) query blocks to compute; out is [nrows][B][d] doubles.
+ */
+int orc_attend(const uint16_t *q, const uint16_t *k, const uint16_t *v, int n, int hq, int hkv,
+               int d, int B, const int32_t *row_ptr, const int32_t *col_idx,
+               const int32_t *rows, int nrows, double *out)
+{
+    if (n < B || n % B || hq % hkv) return 1;
+    const int nb = n / B, G = hq / hkv;
+    const double scale = 1.0 / sqrt((double)d);
+    for (int g = 0; g < hkv; ++g) {
+        int any = 0;
+        for (int r = 0; r < nrows; ++r) any |= (rows[r] / nb) / G == g;
+        if (!any) continue;
+        float *kg = widen(k + (int64_t)g * n * d, (int64_t)n * d);
+        float *vg = widen(v + (int64_t)g * n * d, (int64_t)n * d);
+        if (!kg || !vg) { free(kg); free(vg); return 2; }
+#pragma omp parallel for schedule(dynamic, 1) collapse(2)
+        for (int r = 0; r < nrows; ++r) {
+            for (int t = 0; t < B; ++t) {
+                const int h = rows[r] / nb, qb = rows[r] % nb;
+                if (h / G != g) continue;
+                const int64_t qpos = (int64_t)qb * B + t;
+                float qrow[1024];
+                const uint16_t *qsrc = q + ((int64_t)h * n + qpos) * d;
+                for (int c = 0; c < d; ++c) qrow[c] = bf16_to_f32(qsrc[c]);
+                const int32_t *list = col_idx + row_ptr[h * (nb + 1) + qb];
+                const int len = row_ptr[h * (nb + 1) + qb + 1] - row_ptr[h * (nb + 1) + qb];
+                double m = -INFINITY;
+                for (int e = 0; e < len; ++e)
+                    for (int c = 0; c < B; ++c) {
+                        int64_t key = (int64_t)list[e] * B + c;
+                        if (key > qpos) continue;
+                        double s = scale * dot(qrow, kg + key * d, d);
+                        if (s > m) m = s;
+                    }
+                double l = 0.0;
+                double *o = out + ((int64_t)r * B + t) * d;
+                for (int c = 0; c < d; ++c) o[c] = 0.0;
+                for (int e = 0; e < len; ++e)
+                    for (int c = 0; c < B; ++c) {
+                        int64_t key = (int64_t)list[e] * B + c;
+                        if (key > qpos) continue;
+                        double w = exp(scale * dot(qrow, kg + key * d, d) - m);
+                        l += w;
+                        const float *vr = vg + key * d;
+                        for (int x = 0; x < d; ++x) o[x] += w * (double)vr[x];
+                    }
+                for (int x = 0; x < d; ++x) o[x] /= l;
+            }
+        }
+        free(kg);
+        free(vg);
+    }
+    return 0;
+}

@@ -1,0 +1,423 @@
+"""Pins of the CPU oracle against what the paper and the mathematics fix.
+
+None of these re-types the oracle's own loops: proxy maps and attention are
+checked against numpy / torch softmax with explicit masks, diagonal scores
+against numpy.trace, selections against exhaustive search over subsets, and
+several quantities against closed forms (uniform logits; the two-level model
+of Appendix C of the CRISP paper).
+"""
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import oracle as O
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def bf16(x):
+    return torch.as_tensor(np.asarray(x, dtype=np.float32)).to(torch.bfloat16)
+
+
+def rand_qkv(n, hq, hkv, d, seed, scale=1.0):
+    g = torch.Generator().manual_seed(seed)
+    q = (torch.randn(hq, n, d, generator=g) * scale).to(torch.bfloat16)
+    k = (torch.randn(hkv, n, d, generator=g) * scale).to(torch.bfloat16)
+    v = torch.randn(hkv, n, d, generator=g).to(torch.bfloat16)
+    return q, k, v
+
+
+def brute_proxy(q, k, h, G, B):
+    """A^ by numpy: masked logits, softmax along keys (float64)."""
+    n, d = q.shape[1], q.shape[2]
+    qh = q[h, n - B:].double().numpy()
+    kg = k[h // G].double().numpy()
+    s = qh @ kg.T / math.sqrt(d)
+    pos = np.arange(n)
+    qi = n - B + np.arange(B)
+    s[pos[None, :] > qi[:, None]] = -np.inf
+    s -= s.max(axis=1, keepdims=True)
+    e = np.exp(s)
+    return e / e.sum(axis=1, keepdims=True)
+
+
+def brute_scores(ahat, B):
+    """colmean / diagmean via numpy.trace / blockpool by reshape."""
+    Bq, n = ahat.shape
+    nb = n // B
+    a_v = ahat.mean(axis=0)
+    a_s = np.array([np.trace(ahat, offset=sig - (Bq - 1)) for sig in range(n)]) / Bq
+    return a_v.reshape(nb, B).sum(1), a_s.reshape(nb, B).sum(1)
+
+
+# ------------------------------------------------------------------ golden
+def test_paper_defaults_match_golden():
+    gd = json.load(open(os.path.join(GOLDEN, "paper_defaults.json")))
+    assert O.TAU_PROXY == gd["tau_proxy"]["value"]
+    assert O.GAMMA == gd["gamma_pe"]["value"]
+    assert O.K_MIN_TOKENS == gd["k_min_tokens"]["value"]
+    assert O.K_MIN_TOKENS // gd["block_size"]["value"] == gd["k_min_blocks"]["value"]
+    assert O.W_SINK == gd["w_sink"]["value"] == gd["block_size"]["value"]
+    assert O.W_LOCAL == gd["w_local"]["value"] == gd["block_size"]["value"]
+
+
+# ------------------------------------------------------------ proxy + scores
+@pytest.mark.parametrize("n,d,B", [(256, 16, 32), (384, 128, 128), (512, 128, 128), (512, 16, 64)])
+def test_proxy_and_scores_bruteforce(n, d, B):
+    hq, hkv = 4, 2
+    q, k, _ = rand_qkv(n, hq, hkv, d, seed=n + d + B, scale=1.5)
+    for h in range(hq):
+        a_or = O.proxy_map(q, k, n, hq, hkv, d, h, B)
+        a_bf = brute_proxy(q, k, h, hq // hkv, B)
+        np.testing.assert_allclose(a_or, a_bf, rtol=1e-12, atol=1e-15)
+        pv, ps, cs = O.block_scores(a_or, B, B, B)
+        pv_bf, ps_bf = brute_scores(a_bf, B)
+        np.testing.assert_allclose(pv, pv_bf, rtol=1e-11, atol=1e-15)
+        np.testing.assert_allclose(ps, ps_bf, rtol=1e-11, atol=1e-15)
+        # Eq. 2 with w_sink = w_local = B is the first plus the last block
+        anchor = np.zeros(n, bool)
+        anchor[:B] = True
+        anchor[n - B:] = True
+        assert cs == pytest.approx(a_bf[:, anchor].sum(1).mean(), rel=1e-12)
+        if n // B > 1:
+            assert cs == pytest.approx(pv[0] + pv[-1], rel=1e-12)
+
+
+def test_slash_tile_split_identity():
+    """(i, k) in key tile t lands in slash block t if c <= i, else t+1."""
+    n, d, B = 512, 16, 64
+    q, k, _ = rand_qkv(n, 1, 1, d, seed=5)
+    a = brute_proxy(q, k, 0, 1, B)
+    nb = n // B
+    ps = np.zeros(nb + 1)
+    for t in range(nb):
+        tile = a[:, t * B:(t + 1) * B]
+        lo = np.tril(tile).sum()        # c <= i
+        up = np.triu(tile, 1).sum()     # c > i
+        ps[t] += lo / B
+        ps[t + 1] += up / B
+    _, ps_bf = brute_scores(a, B)
+    assert ps[nb] == pytest.approx(0.0, abs=1e-15)
+    np.testing.assert_allclose(ps[:nb], ps_bf, rtol=1e-11, atol=1e-15)
+
+
+@pytest.mark.parametrize("n,B", [(1024, 128), (256, 32)])
+def test_score_invariants(n, B):
+    d = 64
+    q, k, _ = rand_qkv(n, 2, 1, d, seed=11, scale=2.0)
+    r = O.route(q, k, n, 2, 1, d, B, 0.2, B, B)
+    for h in range(2):
+        a = O.proxy_map(q, k, n, 2, 1, d, h, B)
+        np.testing.assert_allclose(a.sum(1), 1.0, atol=1e-12)
+        assert r.p_v[h].sum() == pytest.approx(1.0, abs=1e-12)
+        assert r.p_s[h].sum() == pytest.approx(1.0, abs=1e-12)
+        assert r.p_s[h][0] <= r.p_v[h][0] + 1e-15
+        assert np.all(r.p_v[h] >= 0) and np.all(r.p_s[h] >= 0)
+
+
+def test_uniform_logits_closed_form():
+    """Q = 0: row i is uniform over its q_i + 1 visible keys."""
+    n, B = 4096, 128
+    q = torch.zeros(1, n, 128, dtype=torch.bfloat16)
+    _, k, _ = rand_qkv(n, 1, 1, 128, seed=3)
+    r = O.route(q, k, n, 1, 1)
+    qi = n - B + np.arange(B)
+    pv0 = np.mean(B / (qi + 1.0))
+    pvl = np.mean((np.arange(B) + 1.0) / (qi + 1.0))
+    assert r.p_v[0][0] == pytest.approx(pv0, rel=1e-12)
+    assert r.p_v[0][-1] == pytest.approx(pvl, rel=1e-12)
+    assert r.c_struct[0] == pytest.approx(pv0 + pvl, rel=1e-12)
+    assert r.c_struct[0] == pytest.approx(0.047, abs=0.001)
+    assert r.pattern[0] == 0                  # diffuse: PE (Alg. 2 lines 9-13)
+
+
+def test_one_hot_sink_routes_vs():
+    n, d = 4096, 16
+    q = torch.zeros(1, n, d)
+    k = torch.zeros(1, n, d)
+    q[0, :, 0] = 8.0
+    k[0, 0, 0] = 15.0                          # logit 8*15/4 = 30 on token 0
+    r = O.route(q.to(torch.bfloat16), k.to(torch.bfloat16), n, 1, 1, d)
+    assert r.c_struct[0] > 0.999999
+    assert r.pattern[0] == 1
+
+
+def two_level(n, d, B, k_sig, a=4.0, b_sig=3.0, b_bg=1.0, sig_pos=None):
+    """Appendix C model: identical query rows; k_sig keys at logit z, the rest at z - Delta."""
+    q = torch.zeros(1, n, d)
+    q[0, :, 0] = a
+    k = torch.zeros(1, n, d)
+    k[0, :, 0] = b_bg
+    pos = np.arange(k_sig) if sig_pos is None else np.asarray(sig_pos)
+    k[0, pos, 0] = b_sig
+    s = 1.0 / math.sqrt(d)
+    z, zb = a * b_sig * s, a * b_bg * s
+    return q.to(torch.bfloat16), k.to(torch.bfloat16), z, z - zb, pos
+
+
+def test_two_level_model_appendix_c():
+    n, d, B, ks = 2048, 16, 128, 4
+    q, k, z, delta, pos = two_level(n, d, B, ks)
+    a = O.proxy_map(q, k, n, 1, 1, d, 0, B)
+    # last row sees all n keys: background mass eps of Appendix C
+    eps = math.exp(-delta) / (ks + (n - ks) * math.exp(-delta))
+    assert a[B - 1, n - 1] == pytest.approx(eps, rel=1e-12)
+    assert a[B - 1, 0] == pytest.approx(1.0 / (ks + (n - ks) * math.exp(-delta)), rel=1e-12)
+    # every row: m = q_i + 1 visible keys
+    pv, ps, cs = O.block_scores(a, B, B, B)
+    qi = n - B + np.arange(B)
+    zrow = ks + (qi + 1 - ks) * math.exp(-delta)
+    pv_exact = np.zeros(n // B)
+    pv_exact[0] = np.mean((ks + (B - ks) * math.exp(-delta)) / zrow)
+    pv_exact[1:-1] = np.mean(B * math.exp(-delta) / zrow)
+    pv_exact[-1] = np.mean((np.arange(B) + 1) * math.exp(-delta) / zrow)
+    np.testing.assert_allclose(pv, pv_exact, rtol=1e-11)
+
+
+def test_gamma_noise_count_appendix_c():
+    """gamma-cumsum takes ceil(gamma_res / eps_blk) background blocks (App. C),
+    a count that grows with n while the sink mass a_sink falls."""
+    d, B, ks = 16, 128, 8
+    counts = []
+    for n in (4096, 8192, 16384):
+        q, k, z, delta, pos = two_level(n, d, B, ks, b_sig=9.0, b_bg=1.0)
+        assert delta == pytest.approx(8.0)
+        r = O.route(q, k, n, 1, 1, d, B)
+        pv = r.p_v[0]
+        qi = n - B + np.arange(B)
+        zrow = ks + (qi + 1 - ks) * math.exp(-delta)
+        a_sink = np.mean((ks + (B - ks) * math.exp(-delta)) / zrow)
+        eps_blk = np.mean(B * math.exp(-delta) / zrow)
+        assert pv[0] == pytest.approx(a_sink, rel=1e-12)
+        gres = 0.95 - a_sink
+        assert 0 < gres < (n // B - 2) * eps_blk
+        sel = O.gamma_select(pv, 0.95)
+        n_garbage = len([j for j in sel if j != 0])
+        assert n_garbage == math.ceil(gres / eps_blk)
+        counts.append(n_garbage)
+    assert counts[0] < counts[1] < counts[2]
+
+
+# -------------------------------------------------------------- VS select
+def brute_vs(p, alpha, kmin):
+    pf = p.astype(np.float32)
+    nb = len(pf)
+    r = max(np.float32(1.0) - pf[0] - pf[-1], np.float32(0.0))
+    mu = np.float32(r) / np.float32(nb - 2)
+    th = np.float32(alpha) * mu
+    cnt = int((pf > th).sum())
+    kk = min(max(cnt, kmin), nb)
+    best, best_key = None, None
+    for sub in itertools.combinations(range(nb), kk):
+        key = (float(np.sum(pf[list(sub)], dtype=np.float64)), [-j for j in sub])
+        if best is None or key > best_key:
+            best, best_key = sub, key
+    return sorted(best)
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_vs_select_bruteforce_subsets(seed):
+    rng = np.random.default_rng(seed)
+    nb = int(rng.integers(5, 12))
+    p = rng.random(nb) ** 3
+    p[0] += rng.random() * 3
+    p /= p.sum()
+    for alpha in (0.5, 1.0, 1.5, 3.0):
+        for kmin in (1, 2, 4):
+            got = O.vs_select(p, alpha, kmin).sel.tolist()
+            assert got == brute_vs(p, alpha, kmin), (alpha, kmin)
+
+
+def test_vs_select_handbuilt():
+    # floor case: r = 1 - 0.5 - 0.1 = 0.4, mu = 0.4 / 8 = 0.05
+    p = np.array([0.5, 0.2, 0.01, 0.06, 0.01, 0.04, 0.01, 0.05, 0.02, 0.1])
+    s = O.vs_select(p, 1.0, 2)
+    assert s.sel.tolist() == [0, 1, 3, 9]     # 0.05 is not > 0.05
+    assert s.theta == pytest.approx(0.05, rel=1e-6) and not s.clipped
+    # clipped case: top-k_min with ties to the lower index
+    p2 = np.array([0.9, 0.01, 0.02, 0.02, 0.01, 0.02, 0.01, 0.01])
+    s2 = O.vs_select(p2 / p2.sum(), 100.0, 4)
+    assert s2.clipped and s2.sel.tolist() == [0, 2, 3, 5]
+    # r clamped at 0: every positive block passes
+    p3 = np.array([0.7, 0.05, 0.02, 0.01, 0.4])
+    s3 = O.vs_select(p3, 1.0, 1)
+    assert s3.theta == 0.0 and s3.sel.tolist() == [0, 1, 2, 3, 4]
+
+
+def test_vs_select_alpha_extremes():
+    rng = np.random.default_rng(7)
+    p = rng.random(64)
+    p /= p.sum()
+    assert O.vs_select(p, 0.0, 8).sel.tolist() == list(range(64))   # all p > 0
+    top8 = sorted(np.argsort(-p, kind="stable")[:8].tolist())
+    assert O.vs_select(p, 1e30, 8).sel.tolist() == top8
+
+
+def test_vs_select_tiny_nb_selects_all():
+    for nb in (1, 2):
+        assert O.vs_select(np.ones(nb) / nb, 1.0, 8).sel.tolist() == list(range(nb))
+
+
+# ----------------------------------------------------------- gamma select
+@pytest.mark.parametrize("seed", range(8))
+def test_gamma_select_minimal_cardinality(seed):
+    rng = np.random.default_rng(100 + seed)
+    nb = 10
+    p = rng.random(nb) ** 2
+    p /= p.sum()
+    sel = O.gamma_select(p, 0.95)
+    pf = p.astype(np.float32).astype(np.float64)
+    assert pf[sel].sum() >= np.float64(np.float32(0.95))
+    for kk in range(1, len(sel)):
+        for sub in itertools.combinations(range(nb), kk):
+            assert pf[list(sub)].sum() < np.float64(np.float32(0.95))
+    clipped = O.gamma_select(p, 0.95, kmin_blocks=nb)
+    assert clipped.tolist() == list(range(nb))
+
+
+# ---------------------------------------------------------------- PE path
+def brute_pe_map(q, k, h, G, B):
+    n, d = q.shape[1], q.shape[2]
+    nb = n // B
+    qb = q[h].double().numpy().reshape(nb, B, d).mean(1)
+    kb = k[h // G].double().numpy().reshape(nb, B, d).mean(1)
+    s = qb @ kb.T / math.sqrt(d)
+    s[np.triu(np.ones((nb, nb), bool), 1)] = -np.inf
+    s -= s.max(1, keepdims=True)
+    e = np.exp(s)
+    a = e / e.sum(1, keepdims=True)
+    return a / a.sum()
+
+
+@pytest.mark.parametrize("n,d,B", [(512, 16, 32), (1024, 128, 128)])
+def test_pe_map_bruteforce(n, d, B):
+    q, k, _ = rand_qkv(n, 4, 2, d, seed=21, scale=3.0)
+    for h in range(4):
+        np.testing.assert_allclose(O.pe_map(q, k, n, 4, 2, d, h, B), brute_pe_map(q, k, h, 2, B),
+                                   rtol=1e-11, atol=1e-16)
+
+
+@pytest.mark.parametrize("seed", range(10))
+def test_pe_select_exhaustive(seed):
+    rng = np.random.default_rng(200 + seed)
+    nb = 4
+    a = np.tril(rng.random((nb, nb)) ** 3)
+    a /= a.sum()
+    gamma = float(rng.choice([0.5, 0.8, 0.95]))
+    s = O.pe_select(a, gamma)
+    vals = a.astype(np.float32).astype(np.float64)
+    causal = [(i, j) for i in range(nb) for j in range(i + 1)]
+    g32 = np.float64(np.float32(gamma))
+    best = min(kk for kk in range(1, len(causal) + 1)
+               for sub in itertools.combinations(causal, kk)
+               if sum(vals[e] for e in sub) >= g32)
+    assert s.kstar == best
+    assert s.mask.sum() == best
+    assert sum(vals[e] for e in causal if s.mask[e]) >= g32
+    assert np.all(np.triu(s.mask, 1) == 0)
+
+
+def test_pe_uniform_closed_form():
+    """Q = 0: entry (qb, kb) = 1 / ((qb+1) Nb); K* follows by counting."""
+    n, B, d = 2048, 128, 128
+    nb = n // B
+    q = torch.zeros(1, n, d, dtype=torch.bfloat16)
+    _, k, _ = rand_qkv(n, 1, 1, d, seed=4)
+    a = O.pe_map(q, k, n, 1, 1, d, 0, B)
+    exact = np.tril(1.0 / ((np.arange(nb)[:, None] + 1.0) * nb) * np.ones((nb, nb)))
+    np.testing.assert_allclose(a, exact, rtol=1e-13)
+    gamma = 0.3
+    s = O.pe_select(a, gamma)
+    # rows 0..r-1 hold r/Nb; row r's entries hold 1/((r+1)Nb) each
+    g = float(np.float32(gamma))
+    r = int(math.floor(g * nb))
+    need = math.ceil((g * nb - r) * (r + 1) - 1e-9)
+    assert s.kstar == r * (r + 1) // 2 + need
+    # ties in row r resolve to the lowest flat index: its first `need` entries
+    assert s.mask[r, :need].all() and not s.mask[r, need:].any()
+
+
+# ------------------------------------------------------------------ expand
+@pytest.mark.parametrize("seed", range(6))
+def test_expand_bruteforce(seed):
+    rng = np.random.default_rng(300 + seed)
+    nb = int(rng.integers(3, 40))
+    sv = np.sort(rng.choice(nb, size=int(rng.integers(1, nb)), replace=False))
+    ss = np.sort(rng.choice(nb, size=int(rng.integers(1, nb)), replace=False))
+    row_ptr, col, cnt = O.expand(nb, True, sv, ss)
+    ref = np.zeros((nb, nb), bool)
+    for qb in range(nb):
+        for kb in range(qb + 1):
+            off = qb - kb                       # diagonal offset block
+            ref[qb, kb] = (kb == 0 or kb == qb or kb in set(sv.tolist())
+                           or (nb - 1 - off) in set(ss.tolist()))
+    for qb in range(nb):
+        row = col[row_ptr[qb]:row_ptr[qb + 1]]
+        assert row.tolist() == np.nonzero(ref[qb])[0].tolist()
+        assert row[0] == 0 and row[-1] == qb and np.all(np.diff(row) > 0)
+    assert cnt == ref.sum()
+    # PE rows: selected pairs plus {0, qb}
+    pm = np.tril(rng.random((nb, nb)) < 0.3).astype(np.uint8)
+    rp2, col2, _ = O.expand(nb, False, pe_mask=pm)
+    for qb in range(nb):
+        want = set(np.nonzero(pm[qb, :qb + 1])[0].tolist()) | {0, qb}
+        assert col2[rp2[qb]:rp2[qb + 1]].tolist() == sorted(want)
+
+
+# ------------------------------------------------------------------ attend
+def sdpa64(q, k, v, G, mask):
+    """torch float64 softmax attention with an explicit boolean mask."""
+    qd = q.double()
+    kd = k.double().repeat_interleave(G, 0)
+    vd = v.double().repeat_interleave(G, 0)
+    return torch.nn.functional.scaled_dot_product_attention(qd, kd, vd, attn_mask=mask)
+
+
+@pytest.mark.parametrize("n,d,B", [(256, 16, 32), (512, 128, 128)])
+def test_attend_dense_is_textbook(n, d, B):
+    hq, hkv = 4, 2
+    nb = n // B
+    q, k, v = rand_qkv(n, hq, hkv, d, seed=31, scale=1.2)
+    rp, ci = O.full_causal_lists(hq, nb)
+    rows = np.arange(hq * nb)
+    out = O.attend(q, k, v, n, hq, hkv, d, rp, ci, rows, B).reshape(hq, n, d)
+    causal = torch.ones(n, n, dtype=torch.bool).tril()
+    ref = sdpa64(q, k, v, hq // hkv, causal).numpy()
+    np.testing.assert_allclose(out, ref, rtol=1e-10, atol=1e-12)
+    # row 0 attends to key 0 only
+    np.testing.assert_array_equal(out[:, 0], v.double().numpy().repeat(hq // hkv, 0)[:, 0])
+
+
+def test_attend_sparse_matches_explicit_mask():
+    n, d, B = 512, 16, 32
+    hq, hkv = 2, 1
+    nb = n // B
+    q, k, v = rand_qkv(n, hq, hkv, d, seed=41, scale=1.5)
+    rng = np.random.default_rng(9)
+    per = nb * (nb + 1) // 2
+    row_ptr = np.zeros((hq, nb + 1), np.int32)
+    col = np.zeros(hq * per, np.int32)
+    mask = torch.zeros(hq, n, n, dtype=torch.bool)
+    for h in range(hq):
+        sv = np.sort(rng.choice(nb, 3, replace=False))
+        ss = np.sort(rng.choice(nb, 3, replace=False))
+        rp, _, _ = O.expand(nb, True, sv, ss, base=h * per, col_idx=col)
+        row_ptr[h] = rp
+        for qb in range(nb):
+            for kb in col[rp[qb]:rp[qb + 1]]:
+                mask[h, qb * B:(qb + 1) * B, kb * B:(kb + 1) * B] = True
+    mask &= torch.ones(n, n, dtype=torch.bool).tril()
+    out = O.attend(q, k, v, n, hq, hkv, d, row_ptr, col, np.arange(hq * nb), B).reshape(hq, n, d)
+    ref = sdpa64(q, k, v, 2, mask).numpy()
+    np.testing.assert_allclose(out, ref, rtol=1e-10, atol=1e-12)
+    # a subset of rows in any order gives the same values
+    rows = np.array([5, 0, nb + 3])
+    sub = O.attend(q, k, v, n, hq, hkv, d, row_ptr, col, rows, B)
+    for t, r in enumerate(rows):
+        h, qb = divmod(int(r), nb)
+        np.testing.assert_allclose(sub[t], out[h, qb * B:(qb + 1) * B], rtol=1e-12)
