@@ -1,0 +1,164 @@
+"""Thin ctypes binding of the CRISP HIP library (include/crisp.h).
+
+Argument marshalling only: every step runs in the HIP kernels of
+``_lib/libcrisp.so``.  Tensors are torch tensors used as device memory; the
+stream is torch's current HIP stream unless one is given.  There is no CPU
+fallback: if the library is missing the import-time loader raises.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+import re
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "_lib", "libcrisp.so")
+HEADER = os.path.join(os.path.dirname(PKG), "include", "crisp.h")
+
+CRISP_OK = 0
+CRISP_ERR_INVALID_ARG = 1
+CRISP_ERR_SHAPE = 2
+CRISP_ERR_UNSUPPORTED = 3
+CRISP_ERR_WORKSPACE = 4
+CRISP_ERR_HIP = 5
+
+
+class CrispError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        self.code = code
+        super().__init__(f"{where}: {status_string(code)} (code {code})")
+
+
+class crisp_opts(C.Structure):
+    _fields_ = [("tau_proxy", C.c_float), ("gamma", C.c_float), ("k_min_tokens", C.c_int),
+                ("w_sink", C.c_int), ("w_local", C.c_int)]
+
+
+def default_opts() -> crisp_opts:
+    """The paper's defaults (Section 5, "Setup"; Section 3.2)."""
+    return crisp_opts(0.2, 0.95, 1024, 128, 128)
+
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"CRISP HIP library not built: {LIB_PATH} "
+                              "(run python -m dynamic_sparse_attention_map_amd.build)")
+        L = C.CDLL(LIB_PATH)
+        P, i, f, sz, i64 = C.c_void_p, C.c_int, C.c_float, C.c_size_t, C.c_int64
+        L.crisp_status_string.argtypes = [i]
+        L.crisp_status_string.restype = C.c_char_p
+        L.crisp_workspace_size.argtypes = [i, i, i, i, i, C.POINTER(sz), C.POINTER(i64)]
+        L.crisp_route.argtypes = [P, P, i, i, i, i, i, P, P, sz, P, P, P, P, P]
+        L.crisp_select.argtypes = [P, P, P, P, P, i, i, i, i, i, f, P, P, sz, P, P, P, P, P, i64, P]
+        L.crisp_attend.argtypes = [P, P, P, P, P, i, i, i, i, i, P, sz, P, P]
+        L.crisp_attend_dense.argtypes = [P, P, P, i, i, i, i, i, P, sz, P, P]
+        L.crisp_prefill.argtypes = [P, P, P, i, i, i, i, i, f, P, P, sz, P, P]
+        L.crisp_set_stage_events.argtypes = [P, i]
+        for name in ("crisp_workspace_size", "crisp_route", "crisp_select", "crisp_attend",
+                     "crisp_attend_dense", "crisp_prefill", "crisp_set_stage_events"):
+            getattr(L, name).restype = i
+        _lib = L
+    return _lib
+
+
+def header_symbols() -> list:
+    """Function names declared in include/crisp.h."""
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"\b(crisp_[a-z_]+)\s*\(", text)))
+
+
+def status_string(code: int) -> str:
+    return lib().crisp_status_string(code).decode()
+
+
+def _check(rc: int, where: str):
+    if rc != CRISP_OK:
+        raise CrispError(rc, where)
+
+
+def _ptr(t):
+    return None if t is None else C.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        return C.c_void_p(torch.cuda.current_stream().cuda_stream)
+    if isinstance(stream, int):
+        return C.c_void_p(stream)
+    return C.c_void_p(stream.cuda_stream)
+
+
+def _opts(opts):
+    return None if opts is None else C.byref(opts)
+
+
+def _shape(q, k):
+    hq, n, d = q.shape
+    hkv = k.shape[0]
+    return n, hq, hkv, d
+
+
+def crisp_workspace_size(seq_len, n_heads, n_kv_heads, head_dim=128, block_size=128):
+    ws = C.c_size_t(0)
+    cap = C.c_int64(0)
+    _check(lib().crisp_workspace_size(seq_len, n_heads, n_kv_heads, head_dim, block_size,
+                                      C.byref(ws), C.byref(cap)), "crisp_workspace_size")
+    return int(ws.value), int(cap.value)
+
+
+def alloc_workspace(seq_len, n_heads, n_kv_heads, device="cuda"):
+    """A caller-owned workspace (torch allocates it; the library never does)."""
+    import torch
+    ws_bytes, _ = crisp_workspace_size(seq_len, n_heads, n_kv_heads)
+    return torch.empty(ws_bytes, dtype=torch.uint8, device=device)
+
+
+def crisp_route(q, k, ws, pattern, c_struct, p_v, p_s, opts=None, block_size=128, stream=None):
+    n, hq, hkv, d = _shape(q, k)
+    _check(lib().crisp_route(_ptr(q), _ptr(k), n, hq, hkv, d, block_size, _opts(opts), _ptr(ws),
+                             ws.numel(), _ptr(pattern), _ptr(c_struct), _ptr(p_v), _ptr(p_s),
+                             _stream(stream)), "crisp_route")
+
+
+def crisp_select(q, k, pattern, p_v, p_s, alpha, ws, sel_v, sel_s, sel_counts, row_ptr, col_idx,
+                 opts=None, block_size=128, stream=None):
+    n, hq, hkv, d = _shape(q, k)
+    _check(lib().crisp_select(_ptr(q), _ptr(k), _ptr(pattern), _ptr(p_v), _ptr(p_s), n, hq, hkv, d,
+                              block_size, float(alpha), _opts(opts), _ptr(ws), ws.numel(),
+                              _ptr(sel_v), _ptr(sel_s), _ptr(sel_counts), _ptr(row_ptr),
+                              _ptr(col_idx), col_idx.numel(), _stream(stream)), "crisp_select")
+
+
+def crisp_attend(q, k, v, row_ptr, col_idx, ws, out, block_size=128, stream=None):
+    n, hq, hkv, d = _shape(q, k)
+    _check(lib().crisp_attend(_ptr(q), _ptr(k), _ptr(v), _ptr(row_ptr), _ptr(col_idx), n, hq, hkv, d,
+                              block_size, _ptr(ws), ws.numel(), _ptr(out), _stream(stream)),
+           "crisp_attend")
+
+
+def crisp_attend_dense(q, k, v, ws, out, block_size=128, stream=None):
+    n, hq, hkv, d = _shape(q, k)
+    _check(lib().crisp_attend_dense(_ptr(q), _ptr(k), _ptr(v), n, hq, hkv, d, block_size, _ptr(ws),
+                                    ws.numel(), _ptr(out), _stream(stream)), "crisp_attend_dense")
+
+
+def crisp_prefill(q, k, v, alpha, ws, out, opts=None, block_size=128, stream=None):
+    n, hq, hkv, d = _shape(q, k)
+    _check(lib().crisp_prefill(_ptr(q), _ptr(k), _ptr(v), n, hq, hkv, d, block_size, float(alpha),
+                               _opts(opts), _ptr(ws), ws.numel(), _ptr(out), _stream(stream)),
+           "crisp_prefill")
+
+
+def crisp_set_stage_events(events):
+    """events: five torch.cuda.Event (created with enable_timing) or None."""
+    if events is None:
+        _check(lib().crisp_set_stage_events(None, 0), "crisp_set_stage_events")
+        return
+    arr = (C.c_void_p * len(events))(*[C.c_void_p(e.cuda_event) for e in events])
+    _check(lib().crisp_set_stage_events(arr, len(events)), "crisp_set_stage_events")

@@ -1,0 +1,228 @@
+// Block-sparse causal GQA attention (Eq. 1) on bf16 matrix cores.
+//
+// One work-group of 4 wavefronts computes one (query head, query block):
+// 128 queries, 32 per wavefront.  The listed key blocks are streamed as
+// 64-key sub-tiles through double-buffered LDS (K row-major, V transposed),
+// and each wavefront runs
+//     S^T = K Q^T          (32x32x16 bf16 MFMA, fp32 accumulate)
+//     online softmax       (exp2 domain, fp32 running max / sum)
+//     O^T += V^T P^T       (P rounded to bf16, fp32 accumulate)
+// Computing S^T rather than S leaves each lane holding one query's scores
+// in exactly the register order the P^T operand of the second product
+// needs, so P never leaves registers.  The causal mask is applied only on
+// the diagonal key block; sub-tiles that lie entirely in a wavefront's
+// future are skipped.
+#include "crisp_common.h"
+#include "crisp_kernels.h"
+
+namespace crisp {
+
+namespace {
+
+constexpr int kKT = 64;                   // keys per sub-tile
+constexpr int kKPitch = kD + 8;           // K tile row pitch (bf16), 272 bytes
+constexpr int kVPitch = kKT + 4;          // V^T tile row pitch (bf16), 136 bytes
+constexpr int kKStage = kKT * kKPitch;    // bf16 elements
+constexpr int kVStage = kD * kVPitch;
+constexpr int kStage = kKStage + kVStage;
+
+// grid: ceil(Nb*hkv / 8) * 8 * G work-groups.  Work-group b runs on XCD b % 8
+// (round-robin dispatch); its j = b / 8-th slot there takes chunk
+// (j / G) * 8 + b % 8 and head j % G of that chunk, where chunk c covers the
+// G query heads of KV head c % hkv at query block Nb-1-c/hkv.  Each XCD thus
+// keeps whole GQA groups (sharing K/V in its L2) and every XCD walks the
+// query blocks from the longest causal row down.
+__global__ void __launch_bounds__(256, 2)
+attend_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+              const uint16_t* __restrict__ vt, const int32_t* __restrict__ row_ptr,
+              const int32_t* __restrict__ col_idx, int n, int nb, int hkv, int G,
+              float scale_log2, uint16_t* __restrict__ out)
+{
+    __shared__ __attribute__((aligned(16))) uint16_t lds[2 * kStage];
+
+    const int b = blockIdx.x;
+    const int slot = b >> 3;
+    const int chunk = (slot / G) * 8 + (b & 7);
+    if (chunk >= nb * hkv) return;
+    const int qb = nb - 1 - chunk / hkv;
+    const int g = chunk % hkv;
+    const int h = g * G + slot % G;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, w = tid >> 6;
+    const int l32 = lane & 31, hi = lane >> 5;
+
+    int len, lbase = 0;
+    if (row_ptr) {
+        lbase = row_ptr[h * (nb + 1) + qb];
+        len = row_ptr[h * (nb + 1) + qb + 1] - lbase;
+    } else {
+        len = qb + 1;
+    }
+
+    const int qc = 32 * w + l32;                       // query within the block
+    const size_t qrow = (size_t)h * n + (size_t)qb * kB + qc;
+    bf16x8 qf[8];
+    for (int s = 0; s < 8; ++s)
+        qf[s] = *reinterpret_cast<const bf16x8*>(q + qrow * kD + 16 * s + 8 * hi);
+
+    f32x16 o[4];
+    for (int dt = 0; dt < 4; ++dt) o[dt] = f32x16{};
+    float m_run = -INFINITY, l_run = 0.f;
+
+    const uint16_t* kg = k + (size_t)g * n * kD;
+    const uint16_t* vg = vt + (size_t)g * kD * n;
+    const int ntiles = 2 * len;
+
+    // staging: 4 x 16 bytes of K and 4 x 16 bytes of V^T per thread
+    u32x4 pk[4], pv[4];
+    // a listed block outside [0, qb] is ignored (never addressed)
+    auto block_of = [&](int t) {
+        const int kb = row_ptr ? col_idx[lbase + (t >> 1)] : (t >> 1);
+        return (kb >= 0 && kb <= qb) ? kb : -1;
+    };
+    auto load_tile = [&](int t) {
+        const int kb = max(block_of(t), 0);
+        const size_t key0 = (size_t)kb * kB + (t & 1) * kKT;
+        for (int i = 0; i < 4; ++i) {
+            const int e = tid + 256 * i;
+            const int row = e >> 4, ch = e & 15;              // 64 keys x 16 chunks
+            pk[i] = *reinterpret_cast<const u32x4*>(kg + (key0 + row) * kD + 8 * ch);
+            const int dr = e >> 3, vc = e & 7;                // 128 d-rows x 8 chunks
+            pv[i] = *reinterpret_cast<const u32x4*>(vg + (size_t)dr * n + key0 + 8 * vc);
+        }
+    };
+    auto store_tile = [&](int stage) {
+        uint16_t* ks = lds + stage * kStage;
+        uint16_t* vs = ks + kKStage;
+        for (int i = 0; i < 4; ++i) {
+            const int e = tid + 256 * i;
+            *reinterpret_cast<u32x4*>(ks + (e >> 4) * kKPitch + 8 * (e & 15)) = pk[i];
+            *reinterpret_cast<u32x2*>(vs + (e >> 3) * kVPitch + 8 * (e & 7)) = u32x2{pv[i][0], pv[i][1]};
+            *reinterpret_cast<u32x2*>(vs + (e >> 3) * kVPitch + 8 * (e & 7) + 4) = u32x2{pv[i][2], pv[i][3]};
+        }
+    };
+
+    if (ntiles > 0) {
+        load_tile(0);
+        store_tile(0);
+    }
+    for (int t = 0; t < ntiles; ++t) {
+        if (t + 1 < ntiles) load_tile(t + 1);
+        __syncthreads();
+        const int kb = block_of(t);
+        const int sub = t & 1;
+        const bool diag = (kb == qb);
+        // keys 64..127 of the diagonal block lie after every query < 64
+        const bool skip = kb < 0 || (diag && sub == 1 && w < 2);
+        if (!skip) {
+            const uint16_t* ks = lds + (t & 1) * kStage;
+            const uint16_t* vs = ks + kKStage;
+            f32x16 s[2];
+            s[0] = f32x16{};
+            s[1] = f32x16{};
+            for (int st = 0; st < 8; ++st)
+                for (int a = 0; a < 2; ++a) {
+                    const bf16x8 kf = *reinterpret_cast<const bf16x8*>(ks + (32 * a + l32) * kKPitch + 16 * st + 8 * hi);
+                    s[a] = mfma32(kf, qf[st], s[a]);
+                }
+            float tmax = -INFINITY;
+            for (int a = 0; a < 2; ++a)
+                for (int r = 0; r < 16; ++r) {
+                    float x = s[a][r] * scale_log2;
+                    if (diag) {
+                        const int kc = kKT * sub + 32 * a + 8 * (r >> 2) + 4 * hi + (r & 3);
+                        if (kc > qc) x = -INFINITY;
+                    }
+                    s[a][r] = x;
+                    tmax = fmaxf(tmax, x);
+                }
+            tmax = fmaxf(tmax, swap_half(tmax));
+            // a row with no visible key so far keeps m = -inf; use 0 as its
+            // reference so every exp2 below is exp2(-inf) = 0, never NaN
+            const float m_new = fmaxf(m_run, tmax);
+            const float m_ref = (m_new == -INFINITY) ? 0.f : m_new;
+            const float alpha = exp2f(m_run - m_ref);
+            m_run = m_new;
+            l_run *= alpha;
+            for (int dt = 0; dt < 4; ++dt)
+                for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
+            bf16x8 pf[4];
+            for (int a = 0; a < 2; ++a)
+                for (int r = 0; r < 16; ++r) {
+                    const float p = exp2f(s[a][r] - m_ref);
+                    l_run += p;
+                    pf[2 * a + (r >> 3)][r & 7] = (__bf16)p;
+                }
+            for (int dt = 0; dt < 4; ++dt) {
+                const uint16_t* vrow = vs + (32 * dt + l32) * kVPitch;
+                for (int u = 0; u < 4; ++u) {
+                    const int kk = 32 * (u >> 1) + 16 * (u & 1) + 4 * hi;
+                    const u32x2 lo = *reinterpret_cast<const u32x2*>(vrow + kk);
+                    const u32x2 hi2 = *reinterpret_cast<const u32x2*>(vrow + kk + 8);
+                    const u32x4 vv = {lo[0], lo[1], hi2[0], hi2[1]};
+                    o[dt] = mfma32(__builtin_bit_cast(bf16x8, vv), pf[u], o[dt]);
+                }
+            }
+        }
+        if (t + 1 < ntiles) store_tile((t + 1) & 1);
+    }
+
+    const float l = l_run + swap_half(l_run);
+    const float inv = (l > 0.f) ? 1.0f / l : 0.f;
+    uint16_t* orow = out + qrow * kD;
+    for (int dt = 0; dt < 4; ++dt)
+        for (int j = 0; j < 4; ++j) {
+            bf16x4 v4;
+            for (int r = 0; r < 4; ++r) v4[r] = (__bf16)(o[dt][4 * j + r] * inv);
+            *reinterpret_cast<bf16x4*>(orow + 32 * dt + 8 * j + 4 * hi) = v4;
+        }
+}
+
+// vt[g][d][key] = v[g][key][d]; grid (n/64, hkv), 256 threads.
+__global__ void __launch_bounds__(256)
+v_transpose_kernel(const uint16_t* __restrict__ v, int n, uint16_t* __restrict__ vt)
+{
+    __shared__ uint16_t tile[64][kD + 8];
+    const int g = blockIdx.y, key0 = blockIdx.x * 64, tid = threadIdx.x;
+    const uint16_t* src = v + ((size_t)g * n + key0) * kD;
+    for (int i = 0; i < 4; ++i) {
+        const int e = tid + 256 * i;
+        const int row = e >> 4, ch = e & 15;
+        *reinterpret_cast<u32x4*>(&tile[row][8 * ch]) =
+            *reinterpret_cast<const u32x4*>(src + (size_t)row * kD + 8 * ch);
+    }
+    __syncthreads();
+    uint16_t* dst = vt + (size_t)g * kD * n + key0;
+    for (int i = 0; i < 4; ++i) {
+        const int e = tid + 256 * i;
+        const int d = e >> 3, c8 = e & 7;
+        u32x4 val;
+        for (int x = 0; x < 4; ++x)
+            val[x] = (uint32_t)tile[8 * c8 + 2 * x][d] | ((uint32_t)tile[8 * c8 + 2 * x + 1][d] << 16);
+        *reinterpret_cast<u32x4*>(dst + (size_t)d * n + 8 * c8) = val;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_v_transpose(const uint16_t* v, int n, int hkv, uint16_t* vt, hipStream_t stream)
+{
+    hipLaunchKernelGGL(v_transpose_kernel, dim3(n / 64, hkv), dim3(256), 0, stream, v, n, vt);
+    return hipGetLastError();
+}
+
+hipError_t launch_attend(const uint16_t* q, const uint16_t* k, const uint16_t* vt,
+                         const int32_t* row_ptr, const int32_t* col_idx, int n, int hq, int hkv,
+                         uint16_t* out, hipStream_t stream)
+{
+    const int nb = n / kB, G = hq / hkv;
+    const long long chunks = (long long)nb * hkv;
+    const long long groups = ((chunks + 7) / 8) * 8 * G;
+    const float scale_log2 = kLog2e / sqrtf((float)kD);
+    hipLaunchKernelGGL(attend_kernel, dim3((unsigned)groups), dim3(256), 0, stream, q, k, vt, row_ptr,
+                       col_idx, n, nb, hkv, G, scale_log2, out);
+    return hipGetLastError();
+}
+
+}  // namespace crisp

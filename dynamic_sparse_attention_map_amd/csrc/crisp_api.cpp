@@ -1,0 +1,332 @@
+// C ABI of the CRISP sparse-prefill library: argument validation, workspace
+// carving and kernel launches.  Declared in include/crisp.h.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+
+#include "crisp.h"
+#include "crisp_kernels.h"
+
+using namespace crisp;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+struct Shape {
+    int n, hq, hkv, nb, G;
+};
+
+// Workspace layout.  The scratch region S is shared by the route partials,
+// the select scratch and the transposed V (stages run in that order on one
+// stream); region P after it holds crisp_prefill's intermediates.
+struct Layout {
+    size_t part_m, part_lo, part_up;                       // route (in S)
+    size_t qbar, kbar, abar, hist_mass, hist_count, state, bitmap;   // select (in S)
+    size_t vt;                                             // attend (in S)
+    size_t route_end, select_end, attend_end;              // bytes of S each stage needs
+    size_t pattern, c_struct, p_v, p_s, sel_v, sel_s, counts, row_ptr, col_idx;  // P
+    size_t total;
+    int64_t csr_capacity;
+};
+
+Layout make_layout(const Shape& s)
+{
+    Layout L{};
+    const size_t hq = s.hq, hkv = s.hkv, nb = s.nb, n = s.n;
+    const size_t tri = nb * (nb + 1) / 2;
+    size_t o = 0;
+    auto take = [&](size_t bytes) {
+        const size_t at = o;
+        o = align_up(o + bytes);
+        return at;
+    };
+    const size_t part = hq * nb * kB * sizeof(float);
+    L.part_m = take(part);
+    L.part_lo = take(part);
+    L.part_up = take(part);
+    L.route_end = o;
+    o = 0;
+    L.qbar = take(hq * nb * kD * sizeof(float));
+    L.kbar = take(hkv * nb * kD * sizeof(float));
+    L.abar = take(hq * tri * sizeof(float));
+    L.hist_mass = take(hq * 256 * sizeof(unsigned long long));
+    L.hist_count = take(hq * 256 * sizeof(uint32_t));
+    L.state = take(hq * sizeof(PeState));
+    L.bitmap = take(hq * 2 * nb);
+    L.select_end = o;
+    o = 0;
+    L.vt = take(hkv * kD * n * sizeof(uint16_t));
+    L.attend_end = o;
+    o = L.route_end;
+    if (L.select_end > o) o = L.select_end;
+    if (L.attend_end > o) o = L.attend_end;
+    L.pattern = take(hq);
+    L.c_struct = take(hq * sizeof(float));
+    L.p_v = take(hq * nb * sizeof(float));
+    L.p_s = take(hq * nb * sizeof(float));
+    L.sel_v = take(hq * nb * sizeof(int32_t));
+    L.sel_s = take(hq * nb * sizeof(int32_t));
+    L.counts = take(hq * 3 * sizeof(int32_t));
+    L.row_ptr = take(hq * (nb + 1) * sizeof(int32_t));
+    L.csr_capacity = (int64_t)(hq * tri);
+    L.col_idx = take(hq * tri * sizeof(int32_t));
+    L.total = o;
+    return L;
+}
+
+int check_shape(int seq_len, int n_heads, int n_kv_heads, int head_dim, int block_size, Shape* s)
+{
+    if (head_dim != kD || block_size != kB) return CRISP_ERR_UNSUPPORTED;
+    if (seq_len <= 0 || n_heads <= 0 || n_kv_heads <= 0) return CRISP_ERR_SHAPE;
+    if (seq_len % block_size != 0 || n_heads % n_kv_heads != 0) return CRISP_ERR_SHAPE;
+    const int nb = seq_len / block_size;
+    if (nb > kMaxBlocks) return CRISP_ERR_UNSUPPORTED;
+    const long long tri = (long long)nb * (nb + 1) / 2;
+    if ((long long)n_heads * tri >= (1LL << 31)) return CRISP_ERR_UNSUPPORTED;
+    s->n = seq_len;
+    s->hq = n_heads;
+    s->hkv = n_kv_heads;
+    s->nb = nb;
+    s->G = n_heads / n_kv_heads;
+    return CRISP_OK;
+}
+
+bool bad_ptr(const void* p, size_t align = 16)
+{
+    return p == nullptr || (reinterpret_cast<uintptr_t>(p) % align) != 0;
+}
+
+struct Opts {
+    float tau, gamma;
+    int kmin_blocks;
+};
+
+int check_opts(const crisp_opts* o, Opts* out)
+{
+    crisp_opts d = {0.2f, 0.95f, 1024, kB, kB};
+    if (o) d = *o;
+    if (!std::isfinite(d.tau_proxy)) return CRISP_ERR_INVALID_ARG;
+    if (!(d.gamma > 0.0f && d.gamma <= 1.0f)) return CRISP_ERR_INVALID_ARG;
+    if (d.k_min_tokens < 0 || d.k_min_tokens % kB != 0) return CRISP_ERR_INVALID_ARG;
+    if (d.w_sink != kB || d.w_local != kB) return CRISP_ERR_UNSUPPORTED;
+    out->tau = d.tau_proxy;
+    out->gamma = d.gamma;
+    out->kmin_blocks = d.k_min_tokens / kB;
+    return CRISP_OK;
+}
+
+thread_local hipEvent_t g_events[5];
+thread_local bool g_events_on = false;
+
+void mark(int i, hipStream_t stream)
+{
+    if (g_events_on) (void)hipEventRecord(g_events[i], stream);
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? CRISP_OK : CRISP_ERR_HIP; }
+
+template <typename T>
+T* at(void* ws, size_t off)
+{
+    return reinterpret_cast<T*>(static_cast<char*>(ws) + off);
+}
+
+int do_route(const Shape& s, const Opts& op, const void* q, const void* k, void* ws,
+             const Layout& L, uint8_t* pattern, float* c_struct, float* p_v, float* p_s,
+             hipStream_t stream)
+{
+    return hip_status(launch_route(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+                                   s.n, s.hq, s.hkv, op.tau, at<float>(ws, L.part_m),
+                                   at<float>(ws, L.part_lo), at<float>(ws, L.part_up), p_v, p_s,
+                                   c_struct, pattern, stream));
+}
+
+int do_select(const Shape& s, const Opts& op, float alpha, const void* q, const void* k,
+              const uint8_t* pattern, const float* p_v, const float* p_s, void* ws,
+              const Layout& L, int32_t* sel_v, int32_t* sel_s, int32_t* counts,
+              int32_t* row_ptr, int32_t* col_idx, hipStream_t stream)
+{
+    SelectScratch sc;
+    sc.qbar = at<float>(ws, L.qbar);
+    sc.kbar = at<float>(ws, L.kbar);
+    sc.abar = at<float>(ws, L.abar);
+    sc.hist_mass = at<unsigned long long>(ws, L.hist_mass);
+    sc.hist_count = at<uint32_t>(ws, L.hist_count);
+    sc.state = at<PeState>(ws, L.state);
+    sc.bitmap = at<uint8_t>(ws, L.bitmap);
+    return hip_status(launch_select(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+                                    pattern, p_v, p_s, s.n, s.hq, s.hkv, alpha, op.kmin_blocks,
+                                    op.gamma, sc, sel_v, sel_s, counts, row_ptr, col_idx, stream));
+}
+
+int do_attend(const Shape& s, const void* q, const void* k, const void* v, const int32_t* row_ptr,
+              const int32_t* col_idx, void* ws, const Layout& L, void* out, hipStream_t stream)
+{
+    uint16_t* vt = at<uint16_t>(ws, L.vt);
+    mark(2, stream);
+    hipError_t e = launch_v_transpose(static_cast<const uint16_t*>(v), s.n, s.hkv, vt, stream);
+    if (e != hipSuccess) return CRISP_ERR_HIP;
+    mark(3, stream);
+    e = launch_attend(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), vt, row_ptr,
+                      col_idx, s.n, s.hq, s.hkv, static_cast<uint16_t*>(out), stream);
+    mark(4, stream);
+    return hip_status(e);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* crisp_status_string(int code)
+{
+    switch (code) {
+    case CRISP_OK: return "ok";
+    case CRISP_ERR_INVALID_ARG: return "invalid argument (null or misaligned pointer, or bad option)";
+    case CRISP_ERR_SHAPE: return "bad shape (seq_len % block_size, n_heads % n_kv_heads, or non-positive size)";
+    case CRISP_ERR_UNSUPPORTED: return "unsupported (head_dim, block_size and anchor windows must be 128; N_b <= 4096)";
+    case CRISP_ERR_WORKSPACE: return "workspace or CSR capacity too small";
+    case CRISP_ERR_HIP: return "HIP launch error";
+    default: return "unknown status";
+    }
+}
+
+int crisp_workspace_size(int seq_len, int n_heads, int n_kv_heads, int head_dim, int block_size,
+                         size_t* ws_bytes, int64_t* csr_capacity)
+{
+    Shape s;
+    const int rc = check_shape(seq_len, n_heads, n_kv_heads, head_dim, block_size, &s);
+    if (rc) return rc;
+    if (!ws_bytes || !csr_capacity) return CRISP_ERR_INVALID_ARG;
+    const Layout L = make_layout(s);
+    *ws_bytes = L.total;
+    *csr_capacity = L.csr_capacity;
+    return CRISP_OK;
+}
+
+int crisp_set_stage_events(void* const* events, int count)
+{
+    if (events == nullptr) {
+        g_events_on = false;
+        return CRISP_OK;
+    }
+    if (count != 5) return CRISP_ERR_INVALID_ARG;
+    for (int i = 0; i < 5; ++i) {
+        if (!events[i]) return CRISP_ERR_INVALID_ARG;
+        g_events[i] = static_cast<hipEvent_t>(events[i]);
+    }
+    g_events_on = true;
+    return CRISP_OK;
+}
+
+int crisp_route(const void* q, const void* k, int seq_len, int n_heads, int n_kv_heads,
+                int head_dim, int block_size, const crisp_opts* opts, void* ws, size_t ws_bytes,
+                uint8_t* pattern, float* c_struct, float* p_v, float* p_s, void* stream)
+{
+    Shape s;
+    int rc = check_shape(seq_len, n_heads, n_kv_heads, head_dim, block_size, &s);
+    if (rc) return rc;
+    Opts op;
+    if ((rc = check_opts(opts, &op))) return rc;
+    if (bad_ptr(q) || bad_ptr(k) || bad_ptr(ws, kAlign) || !pattern || bad_ptr(c_struct, 4) ||
+        bad_ptr(p_v, 4) || bad_ptr(p_s, 4))
+        return CRISP_ERR_INVALID_ARG;
+    const Layout L = make_layout(s);
+    if (ws_bytes < L.route_end) return CRISP_ERR_WORKSPACE;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    mark(0, st);
+    rc = do_route(s, op, q, k, ws, L, pattern, c_struct, p_v, p_s, st);
+    mark(1, st);
+    return rc;
+}
+
+int crisp_select(const void* q, const void* k, const uint8_t* pattern, const float* p_v,
+                 const float* p_s, int seq_len, int n_heads, int n_kv_heads, int head_dim,
+                 int block_size, float alpha, const crisp_opts* opts, void* ws, size_t ws_bytes,
+                 int32_t* sel_v, int32_t* sel_s, int32_t* sel_counts, int32_t* row_ptr,
+                 int32_t* col_idx, int64_t csr_capacity, void* stream)
+{
+    Shape s;
+    int rc = check_shape(seq_len, n_heads, n_kv_heads, head_dim, block_size, &s);
+    if (rc) return rc;
+    Opts op;
+    if ((rc = check_opts(opts, &op))) return rc;
+    if (!std::isfinite(alpha) || alpha < 0.0f) return CRISP_ERR_INVALID_ARG;
+    if (bad_ptr(q) || bad_ptr(k) || bad_ptr(ws, kAlign) || !pattern || bad_ptr(p_v, 4) ||
+        bad_ptr(p_s, 4) || bad_ptr(sel_v, 4) || bad_ptr(sel_s, 4) || bad_ptr(sel_counts, 4) ||
+        bad_ptr(row_ptr, 4) || bad_ptr(col_idx, 4))
+        return CRISP_ERR_INVALID_ARG;
+    const Layout L = make_layout(s);
+    if (ws_bytes < L.select_end || csr_capacity < L.csr_capacity) return CRISP_ERR_WORKSPACE;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    mark(1, st);
+    rc = do_select(s, op, alpha, q, k, pattern, p_v, p_s, ws, L, sel_v, sel_s, sel_counts, row_ptr,
+                   col_idx, st);
+    mark(2, st);
+    return rc;
+}
+
+int crisp_attend(const void* q, const void* k, const void* v, const int32_t* row_ptr,
+                 const int32_t* col_idx, int seq_len, int n_heads, int n_kv_heads, int head_dim,
+                 int block_size, void* ws, size_t ws_bytes, void* out, void* stream)
+{
+    Shape s;
+    const int rc = check_shape(seq_len, n_heads, n_kv_heads, head_dim, block_size, &s);
+    if (rc) return rc;
+    if (bad_ptr(q) || bad_ptr(k) || bad_ptr(v) || bad_ptr(out) || bad_ptr(ws, kAlign) ||
+        bad_ptr(row_ptr, 4) || bad_ptr(col_idx, 4))
+        return CRISP_ERR_INVALID_ARG;
+    const Layout L = make_layout(s);
+    if (ws_bytes < L.attend_end) return CRISP_ERR_WORKSPACE;
+    return do_attend(s, q, k, v, row_ptr, col_idx, ws, L, out, static_cast<hipStream_t>(stream));
+}
+
+int crisp_attend_dense(const void* q, const void* k, const void* v, int seq_len, int n_heads,
+                       int n_kv_heads, int head_dim, int block_size, void* ws, size_t ws_bytes,
+                       void* out, void* stream)
+{
+    Shape s;
+    const int rc = check_shape(seq_len, n_heads, n_kv_heads, head_dim, block_size, &s);
+    if (rc) return rc;
+    if (bad_ptr(q) || bad_ptr(k) || bad_ptr(v) || bad_ptr(out) || bad_ptr(ws, kAlign))
+        return CRISP_ERR_INVALID_ARG;
+    const Layout L = make_layout(s);
+    if (ws_bytes < L.attend_end) return CRISP_ERR_WORKSPACE;
+    return do_attend(s, q, k, v, nullptr, nullptr, ws, L, out, static_cast<hipStream_t>(stream));
+}
+
+int crisp_prefill(const void* q, const void* k, const void* v, int seq_len, int n_heads,
+                  int n_kv_heads, int head_dim, int block_size, float alpha,
+                  const crisp_opts* opts, void* ws, size_t ws_bytes, void* out, void* stream)
+{
+    Shape s;
+    int rc = check_shape(seq_len, n_heads, n_kv_heads, head_dim, block_size, &s);
+    if (rc) return rc;
+    Opts op;
+    if ((rc = check_opts(opts, &op))) return rc;
+    if (!std::isfinite(alpha) || alpha < 0.0f) return CRISP_ERR_INVALID_ARG;
+    if (bad_ptr(q) || bad_ptr(k) || bad_ptr(v) || bad_ptr(out) || bad_ptr(ws, kAlign))
+        return CRISP_ERR_INVALID_ARG;
+    const Layout L = make_layout(s);
+    if (ws_bytes < L.total) return CRISP_ERR_WORKSPACE;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    uint8_t* pattern = at<uint8_t>(ws, L.pattern);
+    float* p_v = at<float>(ws, L.p_v);
+    float* p_s = at<float>(ws, L.p_s);
+    int32_t* row_ptr = at<int32_t>(ws, L.row_ptr);
+    int32_t* col_idx = at<int32_t>(ws, L.col_idx);
+    mark(0, st);
+    rc = do_route(s, op, q, k, ws, L, pattern, at<float>(ws, L.c_struct), p_v, p_s, st);
+    if (rc) return rc;
+    mark(1, st);
+    rc = do_select(s, op, alpha, q, k, pattern, p_v, p_s, ws, L, at<int32_t>(ws, L.sel_v),
+                   at<int32_t>(ws, L.sel_s), at<int32_t>(ws, L.counts), row_ptr, col_idx, st);
+    if (rc) return rc;
+    return do_attend(s, q, k, v, row_ptr, col_idx, ws, L, out, st);
+}
+
+}  // extern "C"

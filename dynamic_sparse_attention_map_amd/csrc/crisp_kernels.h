@@ -1,0 +1,58 @@
+// Internal launchers of the CRISP HIP kernels (not part of the C ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace crisp {
+
+constexpr int kD = 128;            // head_dim
+constexpr int kB = 128;            // block size B (tokens per block)
+constexpr int kMaxBlocks = 4096;   // largest N_b (seq_len 524288 at B = 128)
+
+// Per-head state of the PE radix select (device memory, 64 bytes).
+struct PeState {
+    unsigned long long need;        // fixed-point mass still to cover
+    unsigned long long tfix;        // fixed-point value of the cut-off entry
+    uint32_t key_prefix;            // resolved high digits of the cut-off key
+    uint32_t flat_prefix;           // resolved high digits of the cut-off flat index
+    uint32_t before;                // entries strictly before the cut-off key
+    uint32_t tie_need;              // cut-off-valued entries still to take
+    uint32_t key_star;              // cut-off key (ascending order = value desc)
+    uint32_t flat_star;             // last kept flat index among key_star entries
+    uint32_t kstar;                 // K*
+    uint32_t done;
+    uint32_t pad[4];
+};
+
+// Fixed point used for masses: value * 2^62 truncated (values are <= 1).
+constexpr double kFix = 4611686018427387904.0;
+
+hipError_t launch_route(const uint16_t* q, const uint16_t* k, int n, int hq, int hkv, float tau,
+                        float* part_m, float* part_lo, float* part_up, float* p_v, float* p_s,
+                        float* c_struct, uint8_t* pattern, hipStream_t stream);
+
+struct SelectScratch {
+    float* qbar;                    // [hq][Nb][128]
+    float* kbar;                    // [hkv][Nb][128]
+    float* abar;                    // [hq][Nb(Nb+1)/2] triangular rows
+    unsigned long long* hist_mass;  // [hq][256]
+    uint32_t* hist_count;           // [hq][256]
+    PeState* state;                 // [hq]
+    uint8_t* bitmap;                // [hq][2][Nb]
+};
+
+hipError_t launch_select(const uint16_t* q, const uint16_t* k, const uint8_t* pattern,
+                         const float* p_v, const float* p_s, int n, int hq, int hkv, float alpha,
+                         int kmin_blocks, float gamma, const SelectScratch& s, int32_t* sel_v,
+                         int32_t* sel_s, int32_t* sel_counts, int32_t* row_ptr, int32_t* col_idx,
+                         hipStream_t stream);
+
+hipError_t launch_v_transpose(const uint16_t* v, int n, int hkv, uint16_t* vt, hipStream_t stream);
+
+// row_ptr / col_idx == nullptr: dense causal lists.
+hipError_t launch_attend(const uint16_t* q, const uint16_t* k, const uint16_t* vt,
+                         const int32_t* row_ptr, const int32_t* col_idx, int n, int hq, int hkv,
+                         uint16_t* out, hipStream_t stream);
+
+}  // namespace crisp

@@ -260,7 +260,7 @@ def generate(spec: Spec, threads: int = 8) -> Inputs:
 
     # stripe candidate positions: distinct key blocks in [1, nb-3], random offset
     ncand = spec.n_candidates
-    lo_b, hi_b = 1, max(1, nb - 3)
+    lo_b, hi_b = (1, nb - 3) if nb >= 4 else (0, nb - 1)
     stripe_pos = np.zeros((hkv, ncand), dtype=np.int64)
     cluster = np.zeros((hkv, nb), dtype=np.float64)
     for gi in range(hkv):

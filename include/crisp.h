@@ -1,0 +1,165 @@
+/*
+ * crisp.h -- C ABI of the MI355X (gfx950) CRISP sparse-prefill library.
+ *
+ * CRISP ("Cliff-awaRe Input-adaptive Sparse Prefilling with Structural-Mass-
+ * Motivated Routing", arXiv 2609.01925) prefills one attention layer in three
+ * steps per query head (Alg. 1): route the head with the structural proxy
+ * C_struct (Alg. 2, Eq. 2), select a block index set -- the sink-aware noise
+ * floor on vertical-slash heads (Alg. 3, Eq. 3-4) or gamma-cumsum over a
+ * pooled map on pooled-estimation heads (Alg. 4) -- and run block-sparse
+ * causal attention over that set (Eq. 1).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Tensors: bf16, contiguous, batch 1.  q is [n_heads][seq_len][head_dim];
+ *   k, v are [n_kv_heads][seq_len][head_dim]; query head h reads KV head
+ *   h / (n_heads / n_kv_heads) (grouped-query attention).  out has q's shape.
+ * Device pointers: every array argument is device memory, 16-byte aligned
+ *   (the workspace 256-byte aligned).  opts is a host pointer (may be NULL).
+ * Sizes: head_dim == 128 and block_size == 128 (B in the paper); seq_len a
+ *   positive multiple of block_size; n_heads a multiple of n_kv_heads;
+ *   N_b = seq_len / block_size.
+ * Ownership: the caller allocates and owns all memory, including the
+ *   workspace (size from crisp_workspace_size).  The library keeps no
+ *   pointer after a call returns and never allocates device memory.
+ * Streams: stream is a hipStream_t (NULL = the default stream).  Every call
+ *   is asynchronous on it; results are valid once the stream has reached
+ *   them.  Calls on different streams need distinct workspaces.
+ * Errors: every call returns CRISP_OK (0) or a positive CRISP_ERR_* code.
+ *   Arguments are validated on the host before anything is launched; on a
+ *   validation error nothing is launched and no output is touched.
+ *   CRISP_ERR_HIP reports a failed launch (hipGetLastError after a launch);
+ *   outputs are then unspecified.  No call aborts or throws.
+ */
+#ifndef CRISP_H
+#define CRISP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum crisp_status {
+    CRISP_OK = 0,
+    CRISP_ERR_INVALID_ARG = 1, /* NULL or misaligned pointer, bad option value   */
+    CRISP_ERR_SHAPE = 2,       /* seq_len % block_size, n_heads % n_kv_heads, ... */
+    CRISP_ERR_UNSUPPORTED = 3, /* head_dim / block_size / anchor windows != 128   */
+    CRISP_ERR_WORKSPACE = 4,   /* workspace or CSR capacity too small             */
+    CRISP_ERR_HIP = 5          /* a kernel launch failed                          */
+};
+
+/*
+ * Hyper-parameters (Section 5, "Setup"; Section 3.2).  NULL selects the
+ * paper's defaults {0.2, 0.95, 1024, 128, 128}.
+ *   tau_proxy     routing threshold: VS iff C_struct >= tau_proxy (Alg. 2)
+ *   gamma         PE coverage target (Alg. 4), in (0, 1]
+ *   k_min_tokens  minimum budget per VS direction, in tokens (a multiple of
+ *                 block_size; clip(k, k_min, N_b) of Alg. 3)
+ *   w_sink        anchor windows of C_struct (Eq. 2); must equal block_size,
+ *   w_local       which makes them exactly the first and last key block
+ */
+typedef struct crisp_opts {
+    float tau_proxy;
+    float gamma;
+    int k_min_tokens;
+    int w_sink;
+    int w_local;
+} crisp_opts;
+
+/* Static text for a status code. */
+const char *crisp_status_string(int code);
+
+/*
+ * Worst-case sizes for one layer shape, so that no call needs a host sync.
+ *   ws_bytes      workspace for crisp_prefill; it also suffices for every
+ *                 other call of the same shape
+ *   csr_capacity  col_idx entries crisp_select may write:
+ *                 n_heads * N_b * (N_b + 1) / 2
+ * Host-only, pure.  Returns CRISP_ERR_SHAPE / _UNSUPPORTED like the others.
+ */
+int crisp_workspace_size(int seq_len, int n_heads, int n_kv_heads, int head_dim, int block_size,
+                         size_t *ws_bytes, int64_t *csr_capacity);
+
+/*
+ * PatSearch (Alg. 2) for every query head.  The representative queries are
+ * the last block_size rows; A^ = Softmax(Q^ K^T / sqrt(d)) with the causal
+ * mask.  Outputs (device):
+ *   p_v, p_s   float [n_heads][N_b]  block-pooled column / diagonal means of
+ *              A^ (Alg. 3 lines 3-5); each row sums to 1.  Diagonal (slash)
+ *              block j collects the diagonals that meet the last query row
+ *              at keys j*B .. j*B+B-1, so block N_b-1 is the recency band and
+ *              block 0 the farthest diagonals.
+ *   c_struct   float [n_heads]  anchor mass, Eq. 2 (= p_v[0] + p_v[N_b-1])
+ *   pattern    uint8 [n_heads]  1 = vertical-slash, 0 = pooled estimation
+ * A^ itself is never materialised.
+ */
+int crisp_route(const void *q, const void *k, int seq_len, int n_heads, int n_kv_heads,
+                int head_dim, int block_size, const crisp_opts *opts, void *ws, size_t ws_bytes,
+                uint8_t *pattern, float *c_struct, float *p_v, float *p_s, void *stream);
+
+/*
+ * Index selection (Alg. 3 for pattern 1, Alg. 4 for pattern 0) and block-list
+ * expansion, reading crisp_route's outputs.
+ *   sel_v, sel_s  int32 [n_heads][N_b]  ascending selected vertical / slash
+ *                 blocks of VS heads (Eq. 3-4, clip to [k_min, N_b], top-k)
+ *   sel_counts    int32 [n_heads][3]    (k_v, k_s, K*): list lengths of VS
+ *                 heads, K* (pooled entries kept by gamma-cumsum) of PE heads
+ *   row_ptr       int32 [n_heads][N_b+1] absolute offsets into col_idx; the
+ *                 key blocks of (h, qb) are col_idx[row_ptr[h][qb] ..
+ *                 row_ptr[h][qb+1]), ascending, unique, all <= qb, always
+ *                 containing 0 and qb.  Head h's lists start at
+ *                 h * N_b * (N_b + 1) / 2.
+ *   col_idx       int32 [csr_capacity]
+ * VS rows: {0, qb} u {v in S_v : v <= qb} u {qb - (N_b-1-j) : j in S_s, >= 0}.
+ * PE rows: the kept (qb, kb) entries of the pooled map, plus {0, qb}.
+ * alpha is the noise-floor multiplier of Eq. 4 (>= 0; 1.0 recommended).
+ */
+int crisp_select(const void *q, const void *k, const uint8_t *pattern, const float *p_v,
+                 const float *p_s, int seq_len, int n_heads, int n_kv_heads, int head_dim,
+                 int block_size, float alpha, const crisp_opts *opts, void *ws, size_t ws_bytes,
+                 int32_t *sel_v, int32_t *sel_s, int32_t *sel_counts, int32_t *row_ptr,
+                 int32_t *col_idx, int64_t csr_capacity, void *stream);
+
+/*
+ * Block-sparse causal attention on given lists, Eq. 1: for a query at
+ * position t in block qb, softmax over the keys k <= t of the listed key
+ * blocks of (h, qb), times V.  row_ptr / col_idx as written by crisp_select
+ * (any absolute layout with unique lists; row_ptr must stay inside col_idx).
+ * Listed blocks outside [0, qb] are ignored; a row with no valid block yields
+ * zeros.  Accumulates in fp32, writes bf16 out.
+ */
+int crisp_attend(const void *q, const void *k, const void *v, const int32_t *row_ptr,
+                 const int32_t *col_idx, int seq_len, int n_heads, int n_kv_heads, int head_dim,
+                 int block_size, void *ws, size_t ws_bytes, void *out, void *stream);
+
+/* Dense causal attention with the same kernel (every block 0..qb listed). */
+int crisp_attend_dense(const void *q, const void *k, const void *v, int seq_len, int n_heads,
+                       int n_kv_heads, int head_dim, int block_size, void *ws, size_t ws_bytes,
+                       void *out, void *stream);
+
+/*
+ * Alg. 1 end to end: crisp_route -> crisp_select -> crisp_attend, with
+ * every intermediate kept in the workspace and no host synchronisation.
+ */
+int crisp_prefill(const void *q, const void *k, const void *v, int seq_len, int n_heads,
+                  int n_kv_heads, int head_dim, int block_size, float alpha,
+                  const crisp_opts *opts, void *ws, size_t ws_bytes, void *out, void *stream);
+
+/*
+ * Stage timing for measurement: events is an array of `count` hipEvent_t
+ * (cast to void*) owned by the caller, or NULL to stop.  While set (per
+ * calling thread), each call records events[i] on its stream at the stage
+ * boundaries it crosses: 0 = route start, 1 = select start, 2 = attend
+ * start (before the V re-layout), 3 = attention kernel start, 4 = end.
+ * crisp_route records 0 and 1, crisp_select 1 and 2, crisp_attend and
+ * crisp_attend_dense 2, 3 and 4, crisp_prefill all five.  count must be 5.
+ */
+int crisp_set_stage_events(void *const *events, int count);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CRISP_H */

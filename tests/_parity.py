@@ -1,0 +1,198 @@
+"""GPU-vs-oracle comparison helpers for the CRISP parity tests.
+
+Contract (from the hot path's definition):
+* routing bits are bit-exact;
+* selected block sets are bit-exact except entries whose deciding value lies
+  within 1e-4 (relative) of the threshold, which are counted and reported;
+* given identical block lists, attention output has relative L2 <= 1e-2 and
+  max abs <= 2e-2 against the oracle, per head and overall.
+"""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import torch
+
+from dynamic_sparse_attention_map_amd import crisp
+from oracle import oracle as O
+
+B = 128
+BAND = 1e-4
+REL_L2 = 1e-2
+MAX_ABS = 2e-2
+
+
+def log(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def to_dev(inp):
+    return inp.q.cuda(), inp.k.cuda(), inp.v.cuda()
+
+
+def gpu_route(q, k, ws, opts=None):
+    hq, n, _ = q.shape
+    nb = n // B
+    dev = q.device
+    pattern = torch.zeros(hq, dtype=torch.uint8, device=dev)
+    cs = torch.zeros(hq, dtype=torch.float32, device=dev)
+    pv = torch.zeros(hq, nb, dtype=torch.float32, device=dev)
+    ps = torch.zeros(hq, nb, dtype=torch.float32, device=dev)
+    crisp.crisp_route(q, k, ws, pattern, cs, pv, ps, opts=opts)
+    return dict(pattern=pattern, c_struct=cs, p_v=pv, p_s=ps)
+
+
+def gpu_select(q, k, r, alpha, ws, opts=None):
+    hq, n, _ = q.shape
+    nb = n // B
+    dev = q.device
+    _, cap = crisp.crisp_workspace_size(n, hq, k.shape[0])
+    sel_v = torch.full((hq, nb), -1, dtype=torch.int32, device=dev)
+    sel_s = torch.full((hq, nb), -1, dtype=torch.int32, device=dev)
+    counts = torch.zeros(hq, 3, dtype=torch.int32, device=dev)
+    row_ptr = torch.zeros(hq, nb + 1, dtype=torch.int32, device=dev)
+    col_idx = torch.full((cap,), -1, dtype=torch.int32, device=dev)
+    crisp.crisp_select(q, k, r["pattern"], r["p_v"], r["p_s"], alpha, ws, sel_v, sel_s, counts,
+                       row_ptr, col_idx, opts=opts)
+    return dict(sel_v=sel_v, sel_s=sel_s, counts=counts, row_ptr=row_ptr, col_idx=col_idx)
+
+
+def host(d):
+    torch.cuda.synchronize()
+    return {k: v.cpu().numpy() for k, v in d.items()}
+
+
+def gpu_attend(q, k, v, row_ptr, col_idx, ws):
+    out = torch.empty_like(q)
+    crisp.crisp_attend(q, k, v, torch.as_tensor(row_ptr).cuda(), torch.as_tensor(col_idx).cuda(), ws, out)
+    return out
+
+
+def check_route(gr, orc: O.Route, margin=None):
+    """Routing bits exact; scores close (they are floats)."""
+    pat = gr["pattern"].astype(np.uint8)
+    assert np.array_equal(pat, orc.pattern), (pat, orc.pattern)
+    np.testing.assert_allclose(gr["c_struct"], orc.c_struct, rtol=1e-4, atol=1e-6)
+    np.testing.assert_allclose(gr["p_v"], orc.p_v, rtol=2e-4, atol=1e-7)
+    np.testing.assert_allclose(gr["p_s"], orc.p_s, rtol=2e-4, atol=1e-7)
+    if margin is not None:
+        assert np.all(np.abs(orc.c_struct - O.TAU_PROXY) >= margin), orc.c_struct
+
+
+def vs_exempt(p: np.ndarray, s: O.VSSel) -> set:
+    """Blocks whose deciding value is within BAND of the threshold."""
+    pf = p.astype(np.float32).astype(np.float64)
+    ref = s.kth if s.clipped else s.theta
+    if ref <= 0:
+        return set()
+    return set(np.nonzero(np.abs(pf - ref) <= BAND * ref)[0].tolist())
+
+
+def pe_exempt(abar: np.ndarray, s: O.PESel, gamma=O.GAMMA) -> set:
+    """(qb, kb) entries near the gamma cut-off."""
+    nb = abar.shape[0]
+    v32 = abar.astype(np.float32).astype(np.float64)
+    near = np.abs(v32 - s.vstar) <= BAND * s.vstar
+    ex = set(zip(*np.nonzero(np.tril(near))))
+    g = float(np.float32(gamma))
+    if abs(s.cum_before + s.vstar - g) <= BAND * g:
+        # K* is ambiguous by +1: the next entry in order is exempt too
+        idx = np.tril_indices(nb)
+        vals = v32[idx]
+        flat = idx[0] * nb + idx[1]
+        order = np.lexsort((flat, -vals))
+        if s.kstar < len(order):
+            e = order[s.kstar]
+            ex.add((int(idx[0][e]), int(idx[1][e])))
+    return {(int(a), int(b)) for a, b in ex}
+
+
+class Report:
+    def __init__(self, name):
+        self.name = name
+        self.compared = 0
+        self.mismatch = 0
+        self.exempt = 0
+
+    def add(self, got: set, want: set, universe: int, exempt: set):
+        diff = got ^ want
+        self.compared += universe
+        self.mismatch += len(diff)
+        bad = diff - exempt
+        self.exempt += len(diff & exempt)
+        return bad
+
+    def line(self):
+        return (f"[{self.name}] compared={self.compared} mismatches={self.mismatch} "
+                f"exempt={self.exempt} non_exempt={self.mismatch - self.exempt}")
+
+
+def check_select(inp, gr, gs, alpha, orc_route: O.Route, heads=None, rep=None, gamma=O.GAMMA):
+    """Sets (exempt-aware), counts, and exact expansion of the GPU's own sets."""
+    sp = inp.spec
+    n, hq, hkv = sp.n, sp.hq, sp.hkv
+    nb = n // B
+    rep = rep or Report(sp.name)
+    heads = range(hq) if heads is None else heads
+    for h in heads:
+        rp = gs["row_ptr"][h]
+        base = h * nb * (nb + 1) // 2
+        assert rp[0] == base, (h, rp[0], base)
+        if orc_route.pattern[h]:
+            kv, ks, kp = gs["counts"][h]
+            got_v = set(gs["sel_v"][h, :kv].tolist())
+            got_s = set(gs["sel_s"][h, :ks].tolist())
+            assert np.all(np.diff(gs["sel_v"][h, :kv]) > 0) and np.all(np.diff(gs["sel_s"][h, :ks]) > 0)
+            assert kp == 0
+            for dname, got, p in (("v", got_v, orc_route.p_v[h]), ("s", got_s, orc_route.p_s[h])):
+                s = O.vs_select(p, alpha)
+                bad = rep.add(got, set(s.sel.tolist()), nb, vs_exempt(p, s))
+                assert not bad, (h, dname, sorted(bad))
+            # expansion of the GPU's sets is exact
+            erp, eci, cnt = O.expand(nb, True, np.array(sorted(got_v)), np.array(sorted(got_s)), base=base,
+                                     col_idx=np.zeros(base + nb * (nb + 1) // 2, np.int32))
+            assert np.array_equal(rp, erp), h
+            assert np.array_equal(gs["col_idx"][base:base + cnt], eci[base:base + cnt]), h
+        else:
+            ab = O.pe_map(inp.q, inp.k, n, hq, hkv, 128, h)
+            s = O.pe_select(ab, gamma)
+            ex = pe_exempt(ab, s, gamma)
+            kv, ks, kp = gs["counts"][h]
+            assert kv == 0 and ks == 0
+            assert abs(int(kp) - s.kstar) <= len(ex), (h, kp, s.kstar)
+            for qb in range(nb):
+                got = set(gs["col_idx"][rp[qb]:rp[qb + 1]].tolist())
+                row = gs["col_idx"][rp[qb]:rp[qb + 1]]
+                assert np.all(np.diff(row) > 0) and row[0] == 0 and row[-1] == qb
+                want = set(np.nonzero(s.mask[qb, :qb + 1])[0].tolist()) | {0, qb}
+                exq = {kb for (a, kb) in ex if a == qb and kb not in (0, qb)}
+                bad = rep.add(got, want, qb + 1, exq)
+                assert not bad, (h, qb, sorted(bad))
+    return rep
+
+
+def check_outputs(got: np.ndarray, want: np.ndarray, label=""):
+    """got/want [rows, B, d] (same rows); per-row-group and overall bounds."""
+    g = got.astype(np.float64)
+    w = want.astype(np.float64)
+    err = g - w
+    rel = np.linalg.norm(err) / max(np.linalg.norm(w), 1e-30)
+    mx = float(np.abs(err).max()) if err.size else 0.0
+    log(f"[{label}] rel_l2={rel:.3e} max_abs={mx:.3e} rows={got.shape[0]}")
+    assert rel <= REL_L2, (label, rel)
+    assert mx <= MAX_ABS, (label, mx)
+    return rel, mx
+
+
+def sample_rows(nb, hq, per_head, seed):
+    """Stratified query blocks per head: 0, Nb-1 and uniform others."""
+    rng = np.random.default_rng(seed)
+    rows = []
+    for h in range(hq):
+        qbs = {0, nb - 1}
+        while len(qbs) < min(per_head, nb):
+            qbs.add(int(rng.integers(nb)))
+        rows += [h * nb + qb for qb in sorted(qbs)]
+    return np.array(rows, dtype=np.int32)
