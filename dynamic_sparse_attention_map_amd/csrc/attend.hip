@@ -26,21 +26,18 @@ constexpr int kKStage = kKT * kKPitch;    // bf16 elements
 constexpr int kVStage = kD * kVPitch;
 constexpr int kStage = kKStage + kVStage;
 
-// grid: ceil(Nb*hkv / 8) * 8 * G work-groups.  Work-group b runs on XCD b % 8
-// (round-robin dispatch); its j = b / 8-th slot there takes chunk
-// (j / G) * 8 + b % 8 and head j % G of that chunk, where chunk c covers the
-// G query heads of KV head c % hkv at query block Nb-1-c/hkv.  Each XCD thus
-// keeps whole GQA groups (sharing K/V in its L2) and every XCD walks the
-// query blocks from the longest causal row down.
-__global__ void __launch_bounds__(256, 2)
-attend_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
-              const uint16_t* __restrict__ vt, const int32_t* __restrict__ row_ptr,
-              const int32_t* __restrict__ col_idx, int n, int nb, int hkv, int G,
-              float scale_log2, uint16_t* __restrict__ out)
+// One query block of one head.  Work items are numbered like a grid of
+// ceil(Nb*hkv / 8) * 8 * G work-groups whose item b belongs to XCD b % 8:
+// its j = b / 8-th slot there takes chunk (j / G) * 8 + b % 8 and head j % G
+// of that chunk, where chunk c covers the G query heads of KV head c % hkv at
+// query block Nb-1-c/hkv.  Each XCD thus keeps whole GQA groups (sharing K/V
+// in its L2) and walks the query blocks from the longest causal row down.
+__device__ __forceinline__ void
+attend_row(int b, uint16_t* lds, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+           const uint16_t* __restrict__ vt, const int32_t* __restrict__ row_ptr,
+           const int32_t* __restrict__ col_idx, int n, int nb, int hkv, int G,
+           float scale_log2, uint16_t* __restrict__ out)
 {
-    __shared__ __attribute__((aligned(16))) uint16_t lds[2 * kStage];
-
-    const int b = blockIdx.x;
     const int slot = b >> 3;
     const int chunk = (slot / G) * 8 + (b & 7);
     if (chunk >= nb * hkv) return;
@@ -74,13 +71,28 @@ attend_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* vg = vt + (size_t)g * kD * n;
     const int ntiles = 2 * len;
 
-    // staging: 4 x 16 bytes of K and 4 x 16 bytes of V^T per thread
-    u32x4 pk[4], pv[4];
+    // The row's key-block list is held in registers, 64 entries per chunk:
+    // lane x of idx_cur holds entry 64*chunk + x, idx_nxt the next chunk
+    // (prefetched a whole chunk ahead).  Tile t reads entry t/2 with a
+    // wave-uniform readlane, so no K/V load waits on a list load.
+    int lchunk = 0, idx_cur = -1, idx_nxt = -1;
+    if (row_ptr) {
+        idx_cur = (lane < len) ? col_idx[lbase + lane] : -1;
+        idx_nxt = (64 + lane < len) ? col_idx[lbase + 64 + lane] : -1;
+    }
     // a listed block outside [0, qb] is ignored (never addressed)
     auto block_of = [&](int t) {
-        const int kb = row_ptr ? col_idx[lbase + (t >> 1)] : (t >> 1);
+        const int e = t >> 1;
+        int kb = e;
+        if (row_ptr) {
+            const int src = ((e >> 6) == lchunk) ? idx_cur : idx_nxt;
+            kb = __builtin_amdgcn_readlane(src, e & 63);
+        }
         return (kb >= 0 && kb <= qb) ? kb : -1;
     };
+
+    // staging: 4 x 16 bytes of K and 4 x 16 bytes of V^T per thread
+    u32x4 pk[4], pv[4];
     auto load_tile = [&](int t) {
         const int kb = max(block_of(t), 0);
         const size_t key0 = (size_t)kb * kB + (t & 1) * kKT;
@@ -108,6 +120,13 @@ attend_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
         store_tile(0);
     }
     for (int t = 0; t < ntiles; ++t) {
+        if (row_ptr && ((t >> 1) >> 6) != lchunk) {
+            // entering the next 64-entry chunk: rotate, prefetch the one after
+            lchunk = (t >> 1) >> 6;
+            idx_cur = idx_nxt;
+            const int nxt = 64 * (lchunk + 1) + lane;
+            idx_nxt = (nxt < len) ? col_idx[lbase + nxt] : -1;
+        }
         if (t + 1 < ntiles) load_tile(t + 1);
         __syncthreads();
         const int kb = block_of(t);
@@ -179,6 +198,44 @@ attend_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
         }
 }
 
+// Persistent work-groups (two per CU) drain eight per-XCD queues of work
+// items; a group starts on the queue of its own XCD (work-group b is placed
+// on XCD b % 8) and moves to the others once that one is empty.  ctr[x]
+// counts items taken from queue x and must be zero at launch.
+__global__ void __launch_bounds__(256, 2)
+attend_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+              const uint16_t* __restrict__ vt, const int32_t* __restrict__ row_ptr,
+              const int32_t* __restrict__ col_idx, int n, int nb, int hkv, int G,
+              float scale_log2, int per_xcd, int* __restrict__ ctr, uint16_t* __restrict__ out)
+{
+    __shared__ __attribute__((aligned(16))) uint16_t lds[2 * kStage];
+    __shared__ int s_item;
+    const int home = blockIdx.x & 7;
+    int next_q = 0;   // queues home+0 .. home+7 in turn; only thread 0 uses it
+    for (;;) {
+        if (threadIdx.x == 0) {
+            int item = -1;
+            while (next_q < 8) {
+                const int x = (home + next_q) & 7;
+                const int j = atomicAdd(&ctr[x], 1);
+                if (j < per_xcd) { item = 8 * j + x; break; }
+                ++next_q;
+            }
+            s_item = item;
+        }
+        __syncthreads();
+        const int item = s_item;
+        __syncthreads();
+        if (item < 0) break;
+        attend_row(item, lds, q, k, vt, row_ptr, col_idx, n, nb, hkv, G, scale_log2, out);
+    }
+}
+
+__global__ void zero_counters_kernel(int* __restrict__ ctr)
+{
+    if (threadIdx.x < 8) ctr[threadIdx.x] = 0;
+}
+
 // vt[g][d][key] = v[g][key][d]; grid (n/64, hkv), 256 threads.
 __global__ void __launch_bounds__(256)
 v_transpose_kernel(const uint16_t* __restrict__ v, int n, uint16_t* __restrict__ vt)
@@ -214,14 +271,22 @@ hipError_t launch_v_transpose(const uint16_t* v, int n, int hkv, uint16_t* vt, h
 
 hipError_t launch_attend(const uint16_t* q, const uint16_t* k, const uint16_t* vt,
                          const int32_t* row_ptr, const int32_t* col_idx, int n, int hq, int hkv,
-                         uint16_t* out, hipStream_t stream)
+                         int* counters, uint16_t* out, hipStream_t stream)
 {
     const int nb = n / kB, G = hq / hkv;
     const long long chunks = (long long)nb * hkv;
-    const long long groups = ((chunks + 7) / 8) * 8 * G;
+    const long long items = ((chunks + 7) / 8) * 8 * G;
+    const int per_xcd = (int)(items / 8);
+    int dev = 0, cus = 256;
+    if (hipGetDevice(&dev) == hipSuccess)
+        (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    const int groups = 2 * cus;   // two resident work-groups per CU
     const float scale_log2 = kLog2e / sqrtf((float)kD);
-    hipLaunchKernelGGL(attend_kernel, dim3((unsigned)groups), dim3(256), 0, stream, q, k, vt, row_ptr,
-                       col_idx, n, nb, hkv, G, scale_log2, out);
+    hipLaunchKernelGGL(zero_counters_kernel, dim3(1), dim3(64), 0, stream, counters);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(attend_kernel, dim3(groups), dim3(256), 0, stream, q, k, vt, row_ptr, col_idx,
+                       n, nb, hkv, G, scale_log2, per_xcd, counters, out);
     return hipGetLastError();
 }
 

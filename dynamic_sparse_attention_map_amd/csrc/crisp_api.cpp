@@ -27,7 +27,7 @@ struct Shape {
 struct Layout {
     size_t part_m, part_lo, part_up;                       // route (in S)
     size_t qbar, kbar, abar, hist_mass, hist_count, state, bitmap;   // select (in S)
-    size_t vt;                                             // attend (in S)
+    size_t vt, queue;                                      // attend (in S)
     size_t route_end, select_end, attend_end;              // bytes of S each stage needs
     size_t pattern, c_struct, p_v, p_s, sel_v, sel_s, counts, row_ptr, col_idx;  // P
     size_t total;
@@ -61,6 +61,7 @@ Layout make_layout(const Shape& s)
     L.select_end = o;
     o = 0;
     L.vt = take(hkv * kD * n * sizeof(uint16_t));
+    L.queue = take(8 * sizeof(int));
     L.attend_end = o;
     o = L.route_end;
     if (L.select_end > o) o = L.select_end;
@@ -173,7 +174,8 @@ int do_attend(const Shape& s, const void* q, const void* k, const void* v, const
     if (e != hipSuccess) return CRISP_ERR_HIP;
     mark(3, stream);
     e = launch_attend(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), vt, row_ptr,
-                      col_idx, s.n, s.hq, s.hkv, static_cast<uint16_t*>(out), stream);
+                      col_idx, s.n, s.hq, s.hkv, at<int>(ws, L.queue), static_cast<uint16_t*>(out),
+                      stream);
     mark(4, stream);
     return hip_status(e);
 }

@@ -51,8 +51,9 @@ hipError_t launch_select(const uint16_t* q, const uint16_t* k, const uint8_t* pa
 hipError_t launch_v_transpose(const uint16_t* v, int n, int hkv, uint16_t* vt, hipStream_t stream);
 
 // row_ptr / col_idx == nullptr: dense causal lists.
+// counters: 8 ints of device scratch (zeroed by the launch itself).
 hipError_t launch_attend(const uint16_t* q, const uint16_t* k, const uint16_t* vt,
                          const int32_t* row_ptr, const int32_t* col_idx, int n, int hq, int hkv,
-                         uint16_t* out, hipStream_t stream);
+                         int* counters, uint16_t* out, hipStream_t stream);
 
 }  // namespace crisp

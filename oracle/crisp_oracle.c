@@ -21,9 +21,13 @@
  * closed forms and invariants (see the test-suite); none is "parity unpinned".
  */
 #include <math.h>
+#include <omp.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
+
+/* Threads the OpenMP loops below run on. */
+int orc_threads(void) { return omp_get_max_threads(); }
 
 static float bf16_to_f32(uint16_t b)
 {

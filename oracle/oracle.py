@@ -59,8 +59,14 @@ def lib():
         L.orc_expand.argtypes = [i, i, P, i, P, i, P, i64, P, P]
         L.orc_expand.restype = i64
         L.orc_attend.argtypes = [P, P, P, i, i, i, i, i, P, P, P, i, P]
+        L.orc_threads.restype = i
         _lib = L
     return _lib
+
+
+def threads() -> int:
+    """OpenMP threads the oracle's parallel loops use."""
+    return int(lib().orc_threads())
 
 
 def _p(a: np.ndarray):
