@@ -66,6 +66,7 @@ attend_row(int b, uint16_t* lds, const uint16_t* __restrict__ q, const uint16_t*
     f32x16 o[4];
     for (int dt = 0; dt < 4; ++dt) o[dt] = f32x16{};
     float m_run = -INFINITY, l_run = 0.f;
+    const float rescale_gap = 8.0f / scale_log2;   // 2^8 in probability
 
     const uint16_t* kg = k + (size_t)g * n * kD;
     const uint16_t* vg = vt + (size_t)g * kD * n;
@@ -145,31 +146,41 @@ attend_row(int b, uint16_t* lds, const uint16_t* __restrict__ q, const uint16_t*
                     const bf16x8 kf = *reinterpret_cast<const bf16x8*>(ks + (32 * a + l32) * kKPitch + 16 * st + 8 * hi);
                     s[a] = mfma32(kf, qf[st], s[a]);
                 }
+            if (diag) {
+                // causal mask on the diagonal block only (wave-uniform branch;
+                // the empty asm keeps the compiler from if-converting it)
+                asm volatile("; diagonal mask");
+                for (int a = 0; a < 2; ++a)
+                    for (int r = 0; r < 16; ++r) {
+                        const int kc = kKT * sub + 32 * a + 8 * (r >> 2) + 4 * hi + (r & 3);
+                        if (kc > qc) s[a][r] = -INFINITY;
+                    }
+            }
+            // running max in raw-score units; the accumulator is rescaled only
+            // when the max grows by more than 2^8 in probability (exact: the
+            // final normalisation uses the same reference max)
             float tmax = -INFINITY;
             for (int a = 0; a < 2; ++a)
-                for (int r = 0; r < 16; ++r) {
-                    float x = s[a][r] * scale_log2;
-                    if (diag) {
-                        const int kc = kKT * sub + 32 * a + 8 * (r >> 2) + 4 * hi + (r & 3);
-                        if (kc > qc) x = -INFINITY;
-                    }
-                    s[a][r] = x;
-                    tmax = fmaxf(tmax, x);
-                }
+                for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, s[a][r]);
             tmax = fmaxf(tmax, swap_half(tmax));
-            // a row with no visible key so far keeps m = -inf; use 0 as its
-            // reference so every exp2 below is exp2(-inf) = 0, never NaN
-            const float m_new = fmaxf(m_run, tmax);
-            const float m_ref = (m_new == -INFINITY) ? 0.f : m_new;
-            const float alpha = exp2f(m_run - m_ref);
-            m_run = m_new;
-            l_run *= alpha;
-            for (int dt = 0; dt < 4; ++dt)
-                for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
+            const bool grow = tmax > m_run + rescale_gap;
+            if (__ballot(grow)) {
+                asm volatile("; rescale");
+                const float m_new = grow ? tmax : m_run;
+                const float alpha = (m_run == -INFINITY) ? 0.f
+                                  : __builtin_amdgcn_exp2f((m_run - m_new) * scale_log2);
+                m_run = m_new;
+                l_run *= alpha;
+                for (int dt = 0; dt < 4; ++dt)
+                    for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
+            }
+            // p = 2^(c (s - m)) as one FMA and one v_exp; a lane whose keys are
+            // all masked so far keeps m = -inf and uses 0 as its reference
+            const float neg_mc = (m_run == -INFINITY) ? 0.f : -m_run * scale_log2;
             bf16x8 pf[4];
             for (int a = 0; a < 2; ++a)
                 for (int r = 0; r < 16; ++r) {
-                    const float p = exp2f(s[a][r] - m_ref);
+                    const float p = __builtin_amdgcn_exp2f(fmaf(s[a][r], scale_log2, neg_mc));
                     l_run += p;
                     pf[2 * a + (r >> 3)][r & 7] = (__bf16)p;
                 }
