@@ -90,6 +90,8 @@ def main():
     ap.add_argument("--alpha", type=float, default=1.0)
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--no-dense", action="store_true", help="skip the dense timing")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="end with a 1 GiB device-to-device copy (reference for counter runs)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: every step is per query head and this build runs "
@@ -216,6 +218,13 @@ def main():
         "vs_heads": int(pattern_h.sum()), "pe_heads": int(hq - pattern_h.sum()),
         "roofline": roofline,
     }
+    if args.calibrate_copy:
+        src = torch.ones(1 << 29, dtype=torch.int16, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)             # reads and writes exactly 1 GiB
+        torch.cuda.synchronize()
+        del src, dst
     if not args.no_cpu:
         log("timing the CPU oracle on a bounded sample ...")
         res["cpu_baseline"] = cpu_baseline(inp, pairs, nb, hq, hkv, n)
