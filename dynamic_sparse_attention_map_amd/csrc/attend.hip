@@ -1,9 +1,11 @@
 // Block-sparse causal GQA attention (Eq. 1) on bf16 matrix cores.
 //
-// One work-group of 4 wavefronts computes one (query head, query block):
-// 128 queries, 32 per wavefront.  The listed key blocks are streamed as
-// 64-key sub-tiles through double-buffered LDS (K row-major, V transposed),
-// and each wavefront runs
+// One work-group of 8 wavefronts computes two adjacent query blocks of one
+// query head (256 queries, 32 per wavefront).  It walks the merged union of
+// the two blocks' key-block lists, so every K/V tile is fetched once for both
+// blocks; the listed blocks are streamed as 64-key sub-tiles through
+// double-buffered LDS (K row-major, V transposed), and each wavefront whose
+// block lists the tile runs
 //     S^T = K Q^T          (32x32x16 bf16 MFMA, fp32 accumulate)
 //     online softmax       (exp2 domain, fp32 running max / sum)
 //     O^T += V^T P^T       (P rounded to bf16, fp32 accumulate)
@@ -26,39 +28,118 @@ constexpr int kKStage = kKT * kKPitch;    // bf16 elements
 constexpr int kVStage = kD * kVPitch;
 constexpr int kStage = kKStage + kVStage;
 
-// One query block of one head.  Work items are numbered like a grid of
-// ceil(Nb*hkv / 8) * 8 * G work-groups whose item b belongs to XCD b % 8:
-// its j = b / 8-th slot there takes chunk (j / G) * 8 + b % 8 and head j % G
-// of that chunk, where chunk c covers the G query heads of KV head c % hkv at
-// query block Nb-1-c/hkv.  Each XCD thus keeps whole GQA groups (sharing K/V
-// in its L2) and walks the query blocks from the longest causal row down.
-__device__ __forceinline__ void
-attend_row(int b, uint16_t* lds, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
-           const uint16_t* __restrict__ vt, const int32_t* __restrict__ row_ptr,
-           const int32_t* __restrict__ col_idx, int n, int nb, int hkv, int G,
-           float scale_log2, uint16_t* __restrict__ out)
+constexpr int kThreads = 512;             // 8 wavefronts: two query blocks x 4
+constexpr int kEnd = 0x7fffffff;           // list exhausted
+
+// Register cache of one row's key-block list: lane x of cur holds entry
+// 64*chunk + x and nxt the next 64 (loaded a whole chunk ahead), so entries
+// are read with wave-uniform readlanes and no tile load waits on the list.
+struct ListCursor {
+    int lbase, len, pos, chunk, cur, nxt;
+    bool dense;                            // implicit list 0 .. len-1
+};
+
+__device__ __forceinline__ void cursor_init(ListCursor& c, const int32_t* __restrict__ col_idx,
+                                            int lbase, int len, bool dense, int lane)
 {
+    c.lbase = lbase;
+    c.len = len;
+    c.pos = 0;
+    c.chunk = 0;
+    c.dense = dense;
+    c.cur = c.nxt = -1;
+    if (!dense) {
+        c.cur = (lane < len) ? col_idx[lbase + lane] : -1;
+        c.nxt = (64 + lane < len) ? col_idx[lbase + 64 + lane] : -1;
+    }
+}
+
+__device__ __forceinline__ int cursor_peek(const ListCursor& c)
+{
+    if (c.pos >= c.len) return kEnd;
+    if (c.dense) return c.pos;
+    const int src = ((c.pos >> 6) == c.chunk) ? c.cur : c.nxt;
+    return __builtin_amdgcn_readlane(src, c.pos & 63);
+}
+
+__device__ __forceinline__ void cursor_advance(ListCursor& c, const int32_t* __restrict__ col_idx,
+                                               int lane)
+{
+    ++c.pos;
+    if (!c.dense && (c.pos >> 6) != c.chunk) {
+        c.chunk = c.pos >> 6;
+        c.cur = c.nxt;
+        const int e = 64 * (c.chunk + 1) + lane;
+        c.nxt = (e < c.len) ? col_idx[c.lbase + e] : -1;
+    }
+}
+
+// One step of the merged walk over the two rows' lists: the smallest next
+// key block and which of the two rows lists it.
+struct Entry {
+    int kb;            // kEnd when both lists are exhausted
+    bool hi, lo;
+};
+
+__device__ __forceinline__ Entry next_entry(ListCursor& chi, ListCursor& clo,
+                                            const int32_t* __restrict__ col_idx, int lane)
+{
+    const int a = cursor_peek(chi), b = cursor_peek(clo);
+    Entry e;
+    e.kb = min(a, b);
+    e.hi = (a == e.kb) && a != kEnd;
+    e.lo = (b == e.kb) && b != kEnd;
+    if (e.hi) cursor_advance(chi, col_idx, lane);
+    if (e.lo) cursor_advance(clo, col_idx, lane);
+    return e;
+}
+
+// Work items: like a grid of ceil(npairs*hkv / 8) * 8 * G items whose item b
+// belongs to XCD b % 8: its j = b / 8-th slot there takes chunk
+// (j / G) * 8 + b % 8 and head j % G of that chunk, where chunk c covers the G
+// query heads of KV head c % hkv at query-block pair c / hkv, the pair p
+// being blocks Nb-1-2p and Nb-2-2p.  Each XCD keeps whole GQA groups (sharing
+// K/V in its L2) and walks the pairs from the longest causal rows down.
+__device__ __forceinline__ void
+attend_pair(int b, uint16_t* lds, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+            const uint16_t* __restrict__ vt, const int32_t* __restrict__ row_ptr,
+            const int32_t* __restrict__ col_idx, int n, int nb, int hkv, int G,
+            float scale_log2, uint16_t* __restrict__ out)
+{
+    const int npairs = (nb + 1) >> 1;
     const int slot = b >> 3;
     const int chunk = (slot / G) * 8 + (b & 7);
-    if (chunk >= nb * hkv) return;
-    const int qb = nb - 1 - chunk / hkv;
+    if (chunk >= npairs * hkv) return;
+    const int pair = chunk / hkv;
     const int g = chunk % hkv;
     const int h = g * G + slot % G;
+    const int qb_hi = nb - 1 - 2 * pair;
+    const int qb_lo = qb_hi - 1;                   // -1: no second block
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, w = tid >> 6;
+    const int half = w >> 2, wq = w & 3;           // half 0: qb_hi, half 1: qb_lo
     const int l32 = lane & 31, hi = lane >> 5;
+    const int myqb = half ? qb_lo : qb_hi;
+    const bool active = myqb >= 0;
 
-    int len, lbase = 0;
+    ListCursor chi, clo;
     if (row_ptr) {
-        lbase = row_ptr[h * (nb + 1) + qb];
-        len = row_ptr[h * (nb + 1) + qb + 1] - lbase;
+        const int b_hi = row_ptr[h * (nb + 1) + qb_hi];
+        cursor_init(chi, col_idx, b_hi, row_ptr[h * (nb + 1) + qb_hi + 1] - b_hi, false, lane);
+        if (qb_lo >= 0) {
+            const int b_lo = row_ptr[h * (nb + 1) + qb_lo];
+            cursor_init(clo, col_idx, b_lo, row_ptr[h * (nb + 1) + qb_lo + 1] - b_lo, false, lane);
+        } else {
+            cursor_init(clo, col_idx, 0, 0, true, lane);
+        }
     } else {
-        len = qb + 1;
+        cursor_init(chi, col_idx, 0, qb_hi + 1, true, lane);
+        cursor_init(clo, col_idx, 0, qb_lo + 1, true, lane);
     }
 
-    const int qc = 32 * w + l32;                       // query within the block
-    const size_t qrow = (size_t)h * n + (size_t)qb * kB + qc;
+    const int qc = 32 * wq + l32;                         // query within its block
+    const size_t qrow = (size_t)h * n + (size_t)(active ? myqb : 0) * kB + qc;
     bf16x8 qf[8];
     for (int s = 0; s < 8; ++s)
         qf[s] = *reinterpret_cast<const bf16x8*>(q + qrow * kD + 16 * s + 8 * hi);
@@ -70,35 +151,13 @@ attend_row(int b, uint16_t* lds, const uint16_t* __restrict__ q, const uint16_t*
 
     const uint16_t* kg = k + (size_t)g * n * kD;
     const uint16_t* vg = vt + (size_t)g * kD * n;
-    const int ntiles = 2 * len;
 
-    // The row's key-block list is held in registers, 64 entries per chunk:
-    // lane x of idx_cur holds entry 64*chunk + x, idx_nxt the next chunk
-    // (prefetched a whole chunk ahead).  Tile t reads entry t/2 with a
-    // wave-uniform readlane, so no K/V load waits on a list load.
-    int lchunk = 0, idx_cur = -1, idx_nxt = -1;
-    if (row_ptr) {
-        idx_cur = (lane < len) ? col_idx[lbase + lane] : -1;
-        idx_nxt = (64 + lane < len) ? col_idx[lbase + 64 + lane] : -1;
-    }
-    // a listed block outside [0, qb] is ignored (never addressed)
-    auto block_of = [&](int t) {
-        const int e = t >> 1;
-        int kb = e;
-        if (row_ptr) {
-            const int src = ((e >> 6) == lchunk) ? idx_cur : idx_nxt;
-            kb = __builtin_amdgcn_readlane(src, e & 63);
-        }
-        return (kb >= 0 && kb <= qb) ? kb : -1;
-    };
-
-    // staging: 4 x 16 bytes of K and 4 x 16 bytes of V^T per thread
-    u32x4 pk[4], pv[4];
-    auto load_tile = [&](int t) {
-        const int kb = max(block_of(t), 0);
-        const size_t key0 = (size_t)kb * kB + (t & 1) * kKT;
-        for (int i = 0; i < 4; ++i) {
-            const int e = tid + 256 * i;
+    // staging: 2 x 16 bytes of K and 2 x 16 bytes of V^T per thread
+    u32x4 pk[2], pv[2];
+    auto load_tile = [&](int kb, int sub) {
+        const size_t key0 = (size_t)kb * kB + sub * kKT;
+        for (int i = 0; i < 2; ++i) {
+            const int e = tid + kThreads * i;
             const int row = e >> 4, ch = e & 15;              // 64 keys x 16 chunks
             pk[i] = *reinterpret_cast<const u32x4*>(kg + (key0 + row) * kD + 8 * ch);
             const int dr = e >> 3, vc = e & 7;                // 128 d-rows x 8 chunks
@@ -108,96 +167,133 @@ attend_row(int b, uint16_t* lds, const uint16_t* __restrict__ q, const uint16_t*
     auto store_tile = [&](int stage) {
         uint16_t* ks = lds + stage * kStage;
         uint16_t* vs = ks + kKStage;
-        for (int i = 0; i < 4; ++i) {
-            const int e = tid + 256 * i;
+        for (int i = 0; i < 2; ++i) {
+            const int e = tid + kThreads * i;
             *reinterpret_cast<u32x4*>(ks + (e >> 4) * kKPitch + 8 * (e & 15)) = pk[i];
             *reinterpret_cast<u32x2*>(vs + (e >> 3) * kVPitch + 8 * (e & 7)) = u32x2{pv[i][0], pv[i][1]};
             *reinterpret_cast<u32x2*>(vs + (e >> 3) * kVPitch + 8 * (e & 7) + 4) = u32x2{pv[i][2], pv[i][3]};
         }
     };
 
-    if (ntiles > 0) {
-        load_tile(0);
-        store_tile(0);
-    }
-    for (int t = 0; t < ntiles; ++t) {
-        if (row_ptr && ((t >> 1) >> 6) != lchunk) {
-            // entering the next 64-entry chunk: rotate, prefetch the one after
-            lchunk = (t >> 1) >> 6;
-            idx_cur = idx_nxt;
-            const int nxt = 64 * (lchunk + 1) + lane;
-            idx_nxt = (nxt < len) ? col_idx[lbase + nxt] : -1;
-        }
-        if (t + 1 < ntiles) load_tile(t + 1);
-        __syncthreads();
-        const int kb = block_of(t);
-        const int sub = t & 1;
-        const bool diag = (kb == qb);
+    // ---- tile stream: two 64-key sub-tiles per merged list entry ----
+    struct Tile {
+        int kb, sub;
+        bool act;      // this wavefront computes the tile
+        bool diag;     // the tile is in this wavefront's diagonal block
+    };
+    Entry ent = next_entry(chi, clo, col_idx, lane);
+    int ent_sub = 0;
+    auto pull = [&](Tile& d) -> bool {
+        if (ent.kb == kEnd) return false;
+        const bool uh = ent.hi && ent.kb >= 0 && ent.kb <= qb_hi;
+        const bool ul = ent.lo && ent.kb >= 0 && ent.kb <= qb_lo;
+        const bool mine = half ? ul : uh;
+        // a block no row can use is never addressed: block 0 is loaded instead
+        d.kb = (uh || ul) ? ent.kb : 0;
+        d.sub = ent_sub;
+        d.diag = mine && ent.kb == myqb;
         // keys 64..127 of the diagonal block lie after every query < 64
-        const bool skip = kb < 0 || (diag && sub == 1 && w < 2);
-        if (!skip) {
-            const uint16_t* ks = lds + (t & 1) * kStage;
-            const uint16_t* vs = ks + kKStage;
-            f32x16 s[2];
-            s[0] = f32x16{};
-            s[1] = f32x16{};
-            for (int st = 0; st < 8; ++st)
-                for (int a = 0; a < 2; ++a) {
-                    const bf16x8 kf = *reinterpret_cast<const bf16x8*>(ks + (32 * a + l32) * kKPitch + 16 * st + 8 * hi);
-                    s[a] = mfma32(kf, qf[st], s[a]);
-                }
-            if (diag) {
-                // causal mask on the diagonal block only (wave-uniform branch;
-                // the empty asm keeps the compiler from if-converting it)
-                asm volatile("; diagonal mask");
-                for (int a = 0; a < 2; ++a)
-                    for (int r = 0; r < 16; ++r) {
-                        const int kc = kKT * sub + 32 * a + 8 * (r >> 2) + 4 * hi + (r & 3);
-                        if (kc > qc) s[a][r] = -INFINITY;
-                    }
+        d.act = mine && !(d.diag && ent_sub == 1 && wq < 2);
+        if (ent_sub == 0) {
+            ent_sub = 1;
+        } else {
+            ent_sub = 0;
+            ent = next_entry(chi, clo, col_idx, lane);
+        }
+        return true;
+    };
+
+    f32x16 s[2];
+    bf16x8 pf[4];
+    // S^T = K Q^T for the tile in `stage`
+    auto qk = [&](int stage) {
+        const uint16_t* ks = lds + stage * kStage;
+        s[0] = f32x16{};
+        s[1] = f32x16{};
+        for (int st = 0; st < 8; ++st)
+            for (int a = 0; a < 2; ++a) {
+                const bf16x8 kf = *reinterpret_cast<const bf16x8*>(ks + (32 * a + l32) * kKPitch + 16 * st + 8 * hi);
+                s[a] = mfma32(kf, qf[st], s[a]);
             }
-            // running max in raw-score units; the accumulator is rescaled only
-            // when the max grows by more than 2^8 in probability (exact: the
-            // final normalisation uses the same reference max)
-            float tmax = -INFINITY;
-            for (int a = 0; a < 2; ++a)
-                for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, s[a][r]);
-            tmax = fmaxf(tmax, swap_half(tmax));
-            const bool grow = tmax > m_run + rescale_gap;
-            if (__ballot(grow)) {
-                asm volatile("; rescale");
-                const float m_new = grow ? tmax : m_run;
-                const float alpha = (m_run == -INFINITY) ? 0.f
-                                  : __builtin_amdgcn_exp2f((m_run - m_new) * scale_log2);
-                m_run = m_new;
-                l_run *= alpha;
-                for (int dt = 0; dt < 4; ++dt)
-                    for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
-            }
-            // p = 2^(c (s - m)) as one FMA and one v_exp; a lane whose keys are
-            // all masked so far keeps m = -inf and uses 0 as its reference
-            const float neg_mc = (m_run == -INFINITY) ? 0.f : -m_run * scale_log2;
-            bf16x8 pf[4];
+    };
+    // online softmax of s into bf16 probabilities pf
+    auto softmax = [&](bool diag, int sub) {
+        if (diag) {
+            // causal mask on the diagonal block only (wave-uniform branch)
+            asm volatile("; diagonal mask");
             for (int a = 0; a < 2; ++a)
                 for (int r = 0; r < 16; ++r) {
-                    const float p = __builtin_amdgcn_exp2f(fmaf(s[a][r], scale_log2, neg_mc));
-                    l_run += p;
-                    pf[2 * a + (r >> 3)][r & 7] = (__bf16)p;
+                    const int kc = kKT * sub + 32 * a + 8 * (r >> 2) + 4 * hi + (r & 3);
+                    if (kc > qc) s[a][r] = -INFINITY;
                 }
-            for (int dt = 0; dt < 4; ++dt) {
-                const uint16_t* vrow = vs + (32 * dt + l32) * kVPitch;
-                for (int u = 0; u < 4; ++u) {
-                    const int kk = 32 * (u >> 1) + 16 * (u & 1) + 4 * hi;
-                    const u32x2 lo = *reinterpret_cast<const u32x2*>(vrow + kk);
-                    const u32x2 hi2 = *reinterpret_cast<const u32x2*>(vrow + kk + 8);
-                    const u32x4 vv = {lo[0], lo[1], hi2[0], hi2[1]};
-                    o[dt] = mfma32(__builtin_bit_cast(bf16x8, vv), pf[u], o[dt]);
-                }
+        }
+        // running max in raw-score units; the accumulator is rescaled only
+        // when the max grows by more than 2^8 in probability (exact: the
+        // final normalisation uses the same reference max)
+        float tmax = -INFINITY;
+        for (int a = 0; a < 2; ++a)
+            for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, s[a][r]);
+        tmax = fmaxf(tmax, swap_half(tmax));
+        const bool grow = tmax > m_run + rescale_gap;
+        if (__ballot(grow)) {
+            asm volatile("; rescale");
+            const float m_new = grow ? tmax : m_run;
+            const float alpha = (m_run == -INFINITY) ? 0.f
+                              : __builtin_amdgcn_exp2f((m_run - m_new) * scale_log2);
+            m_run = m_new;
+            l_run *= alpha;
+            for (int dt = 0; dt < 4; ++dt)
+                for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
+        }
+        // p = 2^(c (s - m)) as one FMA and one v_exp; a lane whose keys are
+        // all masked so far keeps m = -inf and uses 0 as its reference
+        const float neg_mc = (m_run == -INFINITY) ? 0.f : -m_run * scale_log2;
+        for (int a = 0; a < 2; ++a)
+            for (int r = 0; r < 16; ++r) {
+                const float p = __builtin_amdgcn_exp2f(fmaf(s[a][r], scale_log2, neg_mc));
+                l_run += p;
+                pf[2 * a + (r >> 3)][r & 7] = (__bf16)p;
+            }
+    };
+    // O^T += V^T P^T for the tile in `stage`
+    auto pv_mfma = [&](int stage) {
+        const uint16_t* vs = lds + stage * kStage + kKStage;
+        for (int dt = 0; dt < 4; ++dt) {
+            const uint16_t* vrow = vs + (32 * dt + l32) * kVPitch;
+            for (int u = 0; u < 4; ++u) {
+                const int kk = 32 * (u >> 1) + 16 * (u & 1) + 4 * hi;
+                const u32x2 lo = *reinterpret_cast<const u32x2*>(vrow + kk);
+                const u32x2 hi2 = *reinterpret_cast<const u32x2*>(vrow + kk + 8);
+                const u32x4 vv = {lo[0], lo[1], hi2[0], hi2[1]};
+                o[dt] = mfma32(__builtin_bit_cast(bf16x8, vv), pf[u], o[dt]);
             }
         }
-        if (t + 1 < ntiles) store_tile((t + 1) & 1);
+    };
+
+    // Sequential schedule: tile t+1 is fetched into registers while tile t
+    // is computed, then stored into the other LDS stage.
+    Tile cur{0, 0, false, false}, nxt{0, 0, false, false};
+    if (pull(cur)) {
+        load_tile(cur.kb, cur.sub);
+        store_tile(0);
+        int stage = 0;
+        for (;;) {
+            const bool has_next = pull(nxt);
+            if (has_next) load_tile(nxt.kb, nxt.sub);
+            __syncthreads();
+            if (cur.act) {
+                qk(stage);
+                softmax(cur.diag, cur.sub);
+                pv_mfma(stage);
+            }
+            if (!has_next) break;
+            store_tile(stage ^ 1);
+            stage ^= 1;
+            cur = nxt;
+        }
     }
 
+    if (!active) return;
     const float l = l_run + swap_half(l_run);
     const float inv = (l > 0.f) ? 1.0f / l : 0.f;
     uint16_t* orow = out + qrow * kD;
@@ -209,11 +305,11 @@ attend_row(int b, uint16_t* lds, const uint16_t* __restrict__ q, const uint16_t*
         }
 }
 
-// Persistent work-groups (two per CU) drain eight per-XCD queues of work
+// Persistent work-groups (one per CU) drain eight per-XCD queues of work
 // items; a group starts on the queue of its own XCD (work-group b is placed
 // on XCD b % 8) and moves to the others once that one is empty.  ctr[x]
 // counts items taken from queue x and must be zero at launch.
-__global__ void __launch_bounds__(256, 2)
+__global__ void __launch_bounds__(kThreads)
 attend_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
               const uint16_t* __restrict__ vt, const int32_t* __restrict__ row_ptr,
               const int32_t* __restrict__ col_idx, int n, int nb, int hkv, int G,
@@ -238,7 +334,7 @@ attend_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
         const int item = s_item;
         __syncthreads();
         if (item < 0) break;
-        attend_row(item, lds, q, k, vt, row_ptr, col_idx, n, nb, hkv, G, scale_log2, out);
+        attend_pair(item, lds, q, k, vt, row_ptr, col_idx, n, nb, hkv, G, scale_log2, out);
     }
 }
 
@@ -285,18 +381,18 @@ hipError_t launch_attend(const uint16_t* q, const uint16_t* k, const uint16_t* v
                          int* counters, uint16_t* out, hipStream_t stream)
 {
     const int nb = n / kB, G = hq / hkv;
-    const long long chunks = (long long)nb * hkv;
+    const long long chunks = (long long)((nb + 1) / 2) * hkv;
     const long long items = ((chunks + 7) / 8) * 8 * G;
     const int per_xcd = (int)(items / 8);
     int dev = 0, cus = 256;
     if (hipGetDevice(&dev) == hipSuccess)
         (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-    const int groups = 2 * cus;   // two resident work-groups per CU
+    const int groups = cus;   // one resident work-group of 8 wavefronts per CU
     const float scale_log2 = kLog2e / sqrtf((float)kD);
     hipLaunchKernelGGL(zero_counters_kernel, dim3(1), dim3(64), 0, stream, counters);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(attend_kernel, dim3(groups), dim3(256), 0, stream, q, k, vt, row_ptr, col_idx,
+    hipLaunchKernelGGL(attend_kernel, dim3(groups), dim3(kThreads), 0, stream, q, k, vt, row_ptr, col_idx,
                        n, nb, hkv, G, scale_log2, per_xcd, counters, out);
     return hipGetLastError();
 }

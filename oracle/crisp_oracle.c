@@ -462,3 +462,54 @@ int orc_attend(const uint16_t *q, const uint16_t *k, const uint16_t *v, int n, i
     }
     return 0;
 }
+
+/*
+ * Eq. 1 for individual queries: qsel lists (h, position) pairs; out is
+ * [nsel][d] doubles.  Same arithmetic as orc_attend, one query at a time,
+ * for sampled checks of long sequences.
+ */
+int orc_attend_queries(const uint16_t *q, const uint16_t *k, const uint16_t *v, int n, int hq,
+                       int hkv, int d, int B, const int32_t *row_ptr, const int32_t *col_idx,
+                       const int32_t *qsel, int nsel, double *out)
+{
+    if (n < B || n % B || hq % hkv || d > 1024) return 1;
+    const int nb = n / B, G = hq / hkv;
+    const double scale = 1.0 / sqrt((double)d);
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int r = 0; r < nsel; ++r) {
+        const int h = qsel[2 * r], g = h / G;
+        const int64_t qpos = qsel[2 * r + 1];
+        const int qb = (int)(qpos / B);
+        const uint16_t *kg = k + (int64_t)g * n * d, *vg = v + (int64_t)g * n * d;
+        float qrow[1024];
+        const uint16_t *qsrc = q + ((int64_t)h * n + qpos) * d;
+        for (int c = 0; c < d; ++c) qrow[c] = bf16_to_f32(qsrc[c]);
+        const int32_t *list = col_idx + row_ptr[h * (nb + 1) + qb];
+        const int len = row_ptr[h * (nb + 1) + qb + 1] - row_ptr[h * (nb + 1) + qb];
+        double m = -INFINITY;
+        for (int e = 0; e < len; ++e)
+            for (int c = 0; c < B; ++c) {
+                const int64_t key = (int64_t)list[e] * B + c;
+                if (key > qpos) continue;
+                double s = 0.0;
+                for (int x = 0; x < d; ++x) s += (double)qrow[x] * (double)bf16_to_f32(kg[key * d + x]);
+                s *= scale;
+                if (s > m) m = s;
+            }
+        double l = 0.0;
+        double *o = out + (int64_t)r * d;
+        for (int x = 0; x < d; ++x) o[x] = 0.0;
+        for (int e = 0; e < len; ++e)
+            for (int c = 0; c < B; ++c) {
+                const int64_t key = (int64_t)list[e] * B + c;
+                if (key > qpos) continue;
+                double s = 0.0;
+                for (int x = 0; x < d; ++x) s += (double)qrow[x] * (double)bf16_to_f32(kg[key * d + x]);
+                const double w = exp(scale * s - m);
+                l += w;
+                for (int x = 0; x < d; ++x) o[x] += w * (double)bf16_to_f32(vg[key * d + x]);
+            }
+        for (int x = 0; x < d; ++x) o[x] /= l;
+    }
+    return 0;
+}

@@ -60,6 +60,7 @@ def lib():
         L.orc_expand.restype = i64
         L.orc_attend.argtypes = [P, P, P, i, i, i, i, i, P, P, P, i, P]
         L.orc_threads.restype = i
+        L.orc_attend_queries.argtypes = [P, P, P, i, i, i, i, i, P, P, P, i, P]
         _lib = L
     return _lib
 
@@ -213,6 +214,18 @@ def attend(q, k, v, n, hq, hkv, d, row_ptr, col_idx, rows, B=128) -> np.ndarray:
     return out
 
 
+def attend_queries(q, k, v, n, hq, hkv, d, row_ptr, col_idx, qsel, B=128) -> np.ndarray:
+    """Eq. 1 for individual queries; qsel is [m, 2] (head, position); returns [m, d]."""
+    qsel = np.ascontiguousarray(qsel, dtype=np.int32).reshape(-1, 2)
+    out = np.zeros((len(qsel), d), dtype=np.float64)
+    rc = lib().orc_attend_queries(_p(_u16(q)), _p(_u16(k)), _p(_u16(v)), n, hq, hkv, d, B,
+                                  _p(np.ascontiguousarray(row_ptr, dtype=np.int32)),
+                                  _p(np.ascontiguousarray(col_idx, dtype=np.int32)), _p(qsel),
+                                  len(qsel), _p(out))
+    assert rc == 0, rc
+    return out
+
+
 # --------------------------------------------------------------------------
 # Whole-path composition (Alg. 1): route -> select -> expand, every head.
 # --------------------------------------------------------------------------
@@ -244,12 +257,13 @@ def full_causal_lists(hq: int, nb: int):
 
 
 def plan(q, k, n, hq, hkv, d=128, B=128, alpha=1.0, tau=TAU_PROXY, gamma=GAMMA,
-         kmin_tokens=K_MIN_TOKENS, heads=None) -> Plan:
+         kmin_tokens=K_MIN_TOKENS, heads=None, routed: Route | None = None) -> Plan:
     """Alg. 1 up to the index set: routing, per-head selection and expansion.
 
-    Head h's lists start at offset h*Nb*(Nb+1)/2 of col_idx (its worst case)."""
+    Head h's lists start at offset h*Nb*(Nb+1)/2 of col_idx (its worst case).
+    `routed` reuses an earlier route() result for the same inputs."""
     nb = n // B
-    r = route(q, k, n, hq, hkv, d, B, tau, B, B)
+    r = routed if routed is not None else route(q, k, n, hq, hkv, d, B, tau, B, B)
     per = nb * (nb + 1) // 2
     row_ptr = np.zeros((hq, nb + 1), dtype=np.int32)
     col_idx = np.zeros(hq * per, dtype=np.int32)

@@ -90,23 +90,41 @@ def vs_exempt(p: np.ndarray, s: O.VSSel) -> set:
     return set(np.nonzero(np.abs(pf - ref) <= BAND * ref)[0].tolist())
 
 
-def pe_exempt(abar: np.ndarray, s: O.PESel, gamma=O.GAMMA) -> set:
-    """(qb, kb) entries near the gamma cut-off."""
+def pe_exempt(abar: np.ndarray, s: O.PESel, gamma=O.GAMMA) -> np.ndarray:
+    """Bool [Nb, Nb]: causal entries whose value is within BAND of the gamma
+    cut-off value (plus the next entry in order when K* itself is ambiguous)."""
     nb = abar.shape[0]
     v32 = abar.astype(np.float32).astype(np.float64)
-    near = np.abs(v32 - s.vstar) <= BAND * s.vstar
-    ex = set(zip(*np.nonzero(np.tril(near))))
+    ex = np.tril(np.abs(v32 - s.vstar) <= BAND * s.vstar)
     g = float(np.float32(gamma))
     if abs(s.cum_before + s.vstar - g) <= BAND * g:
-        # K* is ambiguous by +1: the next entry in order is exempt too
         idx = np.tril_indices(nb)
         vals = v32[idx]
         flat = idx[0] * nb + idx[1]
         order = np.lexsort((flat, -vals))
         if s.kstar < len(order):
             e = order[s.kstar]
-            ex.add((int(idx[0][e]), int(idx[1][e])))
-    return {(int(a), int(b)) for a, b in ex}
+            ex[idx[0][e], idx[1][e]] = True
+    return ex
+
+
+def rows_matrix(row_ptr_h: np.ndarray, col_idx: np.ndarray, nb: int):
+    """Dense [Nb, Nb] membership of one head's CSR rows, after checking that
+    every row is ascending, unique, <= qb and contains 0 and qb."""
+    lens = np.diff(row_ptr_h)
+    assert np.all(lens >= 1)
+    cols = col_idx[row_ptr_h[0]:row_ptr_h[-1]]
+    rows = np.repeat(np.arange(nb), lens)
+    assert np.all(cols <= rows) and np.all(cols >= 0)
+    starts = row_ptr_h[:-1] - row_ptr_h[0]
+    ends = row_ptr_h[1:] - row_ptr_h[0] - 1
+    assert np.all(cols[starts] == 0) and np.all(cols[ends] == np.arange(nb))
+    inner = np.ones(len(cols), bool)
+    inner[starts] = False
+    assert np.all(np.diff(cols)[inner[1:]] > 0)
+    M = np.zeros((nb, nb), bool)
+    M[rows, cols] = True
+    return M
 
 
 class Report:
@@ -136,10 +154,15 @@ def check_select(inp, gr, gs, alpha, orc_route: O.Route, heads=None, rep=None, g
     nb = n // B
     rep = rep or Report(sp.name)
     heads = range(hq) if heads is None else heads
+    tri = nb * (nb + 1) // 2
+    diag_or_sink = np.eye(nb, dtype=bool)
+    diag_or_sink[:, 0] = True
+    diag_or_sink = np.tril(diag_or_sink)
     for h in heads:
         rp = gs["row_ptr"][h]
-        base = h * nb * (nb + 1) // 2
+        base = h * tri
         assert rp[0] == base, (h, rp[0], base)
+        M = rows_matrix(rp, gs["col_idx"], nb)
         if orc_route.pattern[h]:
             kv, ks, kp = gs["counts"][h]
             got_v = set(gs["sel_v"][h, :kv].tolist())
@@ -151,25 +174,23 @@ def check_select(inp, gr, gs, alpha, orc_route: O.Route, heads=None, rep=None, g
                 bad = rep.add(got, set(s.sel.tolist()), nb, vs_exempt(p, s))
                 assert not bad, (h, dname, sorted(bad))
             # expansion of the GPU's sets is exact
-            erp, eci, cnt = O.expand(nb, True, np.array(sorted(got_v)), np.array(sorted(got_s)), base=base,
-                                     col_idx=np.zeros(base + nb * (nb + 1) // 2, np.int32))
-            assert np.array_equal(rp, erp), h
-            assert np.array_equal(gs["col_idx"][base:base + cnt], eci[base:base + cnt]), h
+            erp, eci, cnt = O.expand(nb, True, np.array(sorted(got_v)), np.array(sorted(got_s)))
+            assert np.array_equal(rp - base, erp), h
+            assert np.array_equal(gs["col_idx"][base:base + cnt], eci[:cnt]), h
         else:
             ab = O.pe_map(inp.q, inp.k, n, hq, hkv, 128, h)
             s = O.pe_select(ab, gamma)
             ex = pe_exempt(ab, s, gamma)
             kv, ks, kp = gs["counts"][h]
             assert kv == 0 and ks == 0
-            assert abs(int(kp) - s.kstar) <= len(ex), (h, kp, s.kstar)
-            for qb in range(nb):
-                got = set(gs["col_idx"][rp[qb]:rp[qb + 1]].tolist())
-                row = gs["col_idx"][rp[qb]:rp[qb + 1]]
-                assert np.all(np.diff(row) > 0) and row[0] == 0 and row[-1] == qb
-                want = set(np.nonzero(s.mask[qb, :qb + 1])[0].tolist()) | {0, qb}
-                exq = {kb for (a, kb) in ex if a == qb and kb not in (0, qb)}
-                bad = rep.add(got, want, qb + 1, exq)
-                assert not bad, (h, qb, sorted(bad))
+            assert abs(int(kp) - s.kstar) <= int(ex.sum()), (h, kp, s.kstar)
+            want = (s.mask.astype(bool) | diag_or_sink)
+            diff = M ^ want
+            bad = diff & ~ex & ~diag_or_sink
+            rep.compared += tri
+            rep.mismatch += int(diff.sum())
+            rep.exempt += int((diff & ex).sum())
+            assert not bad.any(), (h, np.argwhere(bad)[:10].tolist())
     return rep
 
 

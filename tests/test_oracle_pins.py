@@ -421,3 +421,16 @@ def test_attend_sparse_matches_explicit_mask():
     for t, r in enumerate(rows):
         h, qb = divmod(int(r), nb)
         np.testing.assert_allclose(sub[t], out[h, qb * B:(qb + 1) * B], rtol=1e-12)
+
+
+def test_attend_queries_is_textbook():
+    n, d, B = 384, 16, 32
+    hq, hkv = 2, 1
+    nb = n // B
+    q, k, v = rand_qkv(n, hq, hkv, d, seed=51, scale=1.3)
+    rp, ci = O.full_causal_lists(hq, nb)
+    sel = np.array([[0, 0], [1, n - 1], [0, 77], [1, 200]], dtype=np.int32)
+    got = O.attend_queries(q, k, v, n, hq, hkv, d, rp, ci, sel, B)
+    ref = sdpa64(q, k, v, 2, torch.ones(n, n, dtype=torch.bool).tril()).numpy()
+    for i, (h, t) in enumerate(sel):
+        np.testing.assert_allclose(got[i], ref[h, t], rtol=1e-10, atol=1e-12)
