@@ -4,8 +4,9 @@
 // query head (256 queries, 32 per wavefront).  It walks the merged union of
 // the two blocks' key-block lists, so every K/V tile is fetched once for both
 // blocks; the listed blocks are streamed as 64-key sub-tiles through
-// double-buffered LDS (K row-major, V transposed), and each wavefront whose
-// block lists the tile runs
+// double-buffered LDS (K row-major; V transposed, keys permuted so that each
+// operand fragment is one 16-byte read), and each wavefront whose block
+// lists the tile runs
 //     S^T = K Q^T          (32x32x16 bf16 MFMA, fp32 accumulate)
 //     online softmax       (exp2 domain, fp32 running max / sum)
 //     O^T += V^T P^T       (P rounded to bf16, fp32 accumulate)
@@ -13,7 +14,9 @@
 // in exactly the register order the P^T operand of the second product
 // needs, so P never leaves registers.  The causal mask is applied only on
 // the diagonal key block; sub-tiles that lie entirely in a wavefront's
-// future are skipped.
+// future are skipped.  Fragment reads are issued several products ahead
+// of the matrix cores (scheduling-group hints), and the exponentials of
+// key group u+1 are interleaved with the PV products of group u.
 #include "crisp_common.h"
 #include "crisp_kernels.h"
 
@@ -23,7 +26,7 @@ namespace {
 
 constexpr int kKT = 64;                   // keys per sub-tile
 constexpr int kKPitch = kD + 8;           // K tile row pitch (bf16), 272 bytes
-constexpr int kVPitch = kKT + 4;          // V^T tile row pitch (bf16), 136 bytes
+constexpr int kVPitch = kKT + 8;          // V^T tile row pitch (bf16), 144 bytes
 constexpr int kKStage = kKT * kKPitch;    // bf16 elements
 constexpr int kVStage = kD * kVPitch;
 constexpr int kStage = kKStage + kVStage;
@@ -69,8 +72,9 @@ __device__ __forceinline__ void cursor_advance(ListCursor& c, const int32_t* __r
     if (!c.dense && (c.pos >> 6) != c.chunk) {
         c.chunk = c.pos >> 6;
         c.cur = c.nxt;
+        // lanes past the end keep stale values, which are never read
         const int e = 64 * (c.chunk + 1) + lane;
-        c.nxt = (e < c.len) ? col_idx[c.lbase + e] : -1;
+        if (e < c.len) c.nxt = col_idx[c.lbase + e];
     }
 }
 
@@ -170,8 +174,7 @@ attend_pair(int b, uint16_t* lds, const uint16_t* __restrict__ q, const uint16_t
         for (int i = 0; i < 2; ++i) {
             const int e = tid + kThreads * i;
             *reinterpret_cast<u32x4*>(ks + (e >> 4) * kKPitch + 8 * (e & 15)) = pk[i];
-            *reinterpret_cast<u32x2*>(vs + (e >> 3) * kVPitch + 8 * (e & 7)) = u32x2{pv[i][0], pv[i][1]};
-            *reinterpret_cast<u32x2*>(vs + (e >> 3) * kVPitch + 8 * (e & 7) + 4) = u32x2{pv[i][2], pv[i][3]};
+            *reinterpret_cast<u32x4*>(vs + (e >> 3) * kVPitch + 8 * (e & 7)) = pv[i];
         }
     };
 
@@ -203,36 +206,48 @@ attend_pair(int b, uint16_t* lds, const uint16_t* __restrict__ q, const uint16_t
         return true;
     };
 
+    // Instruction-group masks for __builtin_amdgcn_sched_group_barrier.
+    constexpr int kSchedValu = 0x002, kSchedMfma = 0x008, kSchedDsRead = 0x100;
+
     f32x16 s[2];
-    bf16x8 pf[4];
-    // S^T = K Q^T for the tile in `stage`
+    // S^T = K Q^T for the tile in `stage`.  The 16 K fragments are read in
+    // the order the matrix cores consume them, six reads ahead.
     auto qk = [&](int stage) {
-        const uint16_t* ks = lds + stage * kStage;
+        const uint16_t* kbase = lds + stage * kStage + l32 * kKPitch + 8 * hi;
+        bf16x8 kf[16];
+        for (int i = 0; i < 16; ++i) {      // i = 2 st + a
+            const int st = i >> 1, a = i & 1;
+            kf[i] = *reinterpret_cast<const bf16x8*>(kbase + 32 * a * kKPitch + 16 * st);
+        }
         s[0] = f32x16{};
         s[1] = f32x16{};
-        for (int st = 0; st < 8; ++st)
-            for (int a = 0; a < 2; ++a) {
-                const bf16x8 kf = *reinterpret_cast<const bf16x8*>(ks + (32 * a + l32) * kKPitch + 16 * st + 8 * hi);
-                s[a] = mfma32(kf, qf[st], s[a]);
+        for (int i = 0; i < 16; ++i) s[i & 1] = mfma32(kf[i], qf[i >> 1], s[i & 1]);
+        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 6, 0);
+        for (int i = 0; i < 10; ++i) {
+            __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 6, 0);
+    };
+    // causal mask on the diagonal block (wave-uniform branch around it)
+    auto mask = [&](int sub) {
+        for (int a = 0; a < 2; ++a)
+            for (int r = 0; r < 16; ++r) {
+                const int kc = kKT * sub + 32 * a + 8 * (r >> 2) + 4 * hi + (r & 3);
+                if (kc > qc) s[a][r] = -INFINITY;
             }
     };
-    // online softmax of s into bf16 probabilities pf
-    auto softmax = [&](bool diag, int sub) {
-        if (diag) {
-            // causal mask on the diagonal block only (wave-uniform branch)
-            asm volatile("; diagonal mask");
-            for (int a = 0; a < 2; ++a)
-                for (int r = 0; r < 16; ++r) {
-                    const int kc = kKT * sub + 32 * a + 8 * (r >> 2) + 4 * hi + (r & 3);
-                    if (kc > qc) s[a][r] = -INFINITY;
-                }
-        }
-        // running max in raw-score units; the accumulator is rescaled only
-        // when the max grows by more than 2^8 in probability (exact: the
-        // final normalisation uses the same reference max)
-        float tmax = -INFINITY;
-        for (int a = 0; a < 2; ++a)
-            for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, s[a][r]);
+    // Running max in raw-score units (tree reduction); the accumulator is
+    // rescaled only when the max grows by more than 2^8 in probability
+    // (exact: the final normalisation uses the same reference max).
+    auto update_max = [&]() {
+        float t[11];
+        for (int i = 0; i < 5; ++i) t[i] = fmaxf(fmaxf(s[0][3 * i], s[0][3 * i + 1]), s[0][3 * i + 2]);
+        for (int i = 0; i < 5; ++i) t[5 + i] = fmaxf(fmaxf(s[1][3 * i], s[1][3 * i + 1]), s[1][3 * i + 2]);
+        t[10] = fmaxf(s[0][15], s[1][15]);
+        const float u0 = fmaxf(fmaxf(t[0], t[1]), t[2]), u1 = fmaxf(fmaxf(t[3], t[4]), t[5]);
+        const float u2 = fmaxf(fmaxf(t[6], t[7]), t[8]), u3 = fmaxf(t[9], t[10]);
+        float tmax = fmaxf(fmaxf(u0, u1), fmaxf(u2, u3));
         tmax = fmaxf(tmax, swap_half(tmax));
         const bool grow = tmax > m_run + rescale_gap;
         if (__ballot(grow)) {
@@ -245,29 +260,43 @@ attend_pair(int b, uint16_t* lds, const uint16_t* __restrict__ q, const uint16_t
             for (int dt = 0; dt < 4; ++dt)
                 for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
         }
-        // p = 2^(c (s - m)) as one FMA and one v_exp; a lane whose keys are
-        // all masked so far keeps m = -inf and uses 0 as its reference
-        const float neg_mc = (m_run == -INFINITY) ? 0.f : -m_run * scale_log2;
-        for (int a = 0; a < 2; ++a)
-            for (int r = 0; r < 16; ++r) {
-                const float p = __builtin_amdgcn_exp2f(fmaf(s[a][r], scale_log2, neg_mc));
-                l_run += p;
-                pf[2 * a + (r >> 3)][r & 7] = (__bf16)p;
-            }
     };
-    // O^T += V^T P^T for the tile in `stage`
-    auto pv_mfma = [&](int stage) {
-        const uint16_t* vs = lds + stage * kStage + kKStage;
-        for (int dt = 0; dt < 4; ++dt) {
-            const uint16_t* vrow = vs + (32 * dt + l32) * kVPitch;
-            for (int u = 0; u < 4; ++u) {
-                const int kk = 32 * (u >> 1) + 16 * (u & 1) + 4 * hi;
-                const u32x2 lo = *reinterpret_cast<const u32x2*>(vrow + kk);
-                const u32x2 hi2 = *reinterpret_cast<const u32x2*>(vrow + kk + 8);
-                const u32x4 vv = {lo[0], lo[1], hi2[0], hi2[1]};
-                o[dt] = mfma32(__builtin_bit_cast(bf16x8, vv), pf[u], o[dt]);
+    // p = 2^(c s - c m) (one FMA and one v_exp), rounded to bf16 into the
+    // P^T operand, then O^T += V^T P^T.  Probabilities of key group u + 1
+    // are computed while the matrix cores run group u; a lane whose keys
+    // are all masked so far keeps m = -inf and uses 0 as its reference.
+    auto exp_pv = [&](int stage) {
+        const uint16_t* vbase = lds + stage * kStage + kKStage + l32 * kVPitch + 8 * hi;
+        const float neg_mc = (m_run == -INFINITY) ? 0.f : -m_run * scale_log2;
+        bf16x8 vf[16];                       // vf[4 u + dt]
+        for (int u = 0; u < 4; ++u)
+            for (int dt = 0; dt < 4; ++dt) {
+                vf[4 * u + dt] = *reinterpret_cast<const bf16x8*>(vbase + 32 * dt * kVPitch + 16 * u);
+            }
+        bf16x8 pf[4];
+        float acc[4] = {0.f, 0.f, 0.f, 0.f};
+        for (int u = 0; u < 4; ++u) {        // key group u: s[u >> 1][8 (u & 1) .. +7]
+            for (int j = 0; j < 8; ++j) {
+                const float p = __builtin_amdgcn_exp2f(fmaf(s[u >> 1][8 * (u & 1) + j], scale_log2, neg_mc));
+                acc[j & 3] += p;
+                pf[u][j] = (__bf16)p;
             }
         }
+        for (int u = 0; u < 4; ++u)
+            for (int dt = 0; dt < 4; ++dt) o[dt] = mfma32(vf[4 * u + dt], pf[u], o[dt]);
+        l_run += (acc[0] + acc[1]) + (acc[2] + acc[3]);
+        // schedule: V reads for groups 0, 1 and the probabilities of group
+        // 0 first; then each group's 4 products interleaved with the next
+        // group's probabilities and V reads
+        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 8, 0);
+        __builtin_amdgcn_sched_group_barrier(kSchedValu, 30, 0);
+        for (int u = 0; u < 3; ++u)
+            for (int dt = 0; dt < 4; ++dt) {
+                __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(kSchedValu, 7, 0);
+                if (u < 2) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+            }
+        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 4, 0);
     };
 
     // Sequential schedule: tile t+1 is fetched into registers while tile t
@@ -283,8 +312,9 @@ attend_pair(int b, uint16_t* lds, const uint16_t* __restrict__ q, const uint16_t
             __syncthreads();
             if (cur.act) {
                 qk(stage);
-                softmax(cur.diag, cur.sub);
-                pv_mfma(stage);
+                if (cur.diag) mask(cur.sub);
+                update_max();
+                exp_pv(stage);
             }
             if (!has_next) break;
             store_tile(stage ^ 1);
@@ -343,7 +373,11 @@ __global__ void zero_counters_kernel(int* __restrict__ ctr)
     if (threadIdx.x < 8) ctr[threadIdx.x] = 0;
 }
 
-// vt[g][d][key] = v[g][key][d]; grid (n/64, hkv), 256 threads.
+// V^T with keys permuted inside every group of 16 (bits 2 and 3 of the key
+// index swapped): vt[g][d][16 j + pi(c)] = v[g][16 j + c][d].  A lane's 8 keys
+// of a PV operand fragment, {4h .. 4h+3, 8+4h .. 8+4h+3} for lane half h (the
+// order the S^T accumulator holds them in), are then 16 contiguous bytes.
+// grid (n/64, hkv), 256 threads.
 __global__ void __launch_bounds__(256)
 v_transpose_kernel(const uint16_t* __restrict__ v, int n, uint16_t* __restrict__ vt)
 {
@@ -362,8 +396,11 @@ v_transpose_kernel(const uint16_t* __restrict__ v, int n, uint16_t* __restrict__
         const int e = tid + 256 * i;
         const int d = e >> 3, c8 = e & 7;
         u32x4 val;
-        for (int x = 0; x < 4; ++x)
-            val[x] = (uint32_t)tile[8 * c8 + 2 * x][d] | ((uint32_t)tile[8 * c8 + 2 * x + 1][d] << 16);
+        for (int x = 0; x < 4; ++x) {
+            const int p0 = 8 * c8 + 2 * x;              // positions p0, p0 + 1
+            const int k0 = (p0 & ~12) | ((p0 & 4) << 1) | ((p0 & 8) >> 1);
+            val[x] = (uint32_t)tile[k0][d] | ((uint32_t)tile[k0 + 1][d] << 16);
+        }
         *reinterpret_cast<u32x4*>(dst + (size_t)d * n + 8 * c8) = val;
     }
 }
