@@ -251,9 +251,9 @@ def generate(spec: Spec, threads: int = 8) -> Inputs:
     import torch
 
     n, hq, hkv, g = spec.n, spec.hq, spec.hkv, spec.group
-    if n % BLOCK:
-        raise ValueError("n must be a multiple of 128")
-    nb = n // BLOCK
+    if n < 1:
+        raise ValueError("n must be positive")
+    nb = -(-n // BLOCK)                 # the last block may be partial
     ss = np.random.SeedSequence(SEED_BASE + 100 * spec.config_id + spec.n_index)
     kids = ss.spawn(2 + 3 * hkv + hq)
     plan = np.random.Generator(np.random.PCG64(kids[1]))
@@ -270,7 +270,7 @@ def generate(spec: Spec, threads: int = 8) -> Inputs:
         else:
             blocks = lo_b + plan.integers(0, span, size=ncand)
         offs = plan.integers(0, BLOCK, size=ncand)
-        stripe_pos[gi] = blocks * BLOCK + offs
+        stripe_pos[gi] = np.minimum(blocks * BLOCK + offs, n - 1)
         c = plan.normal(0.0, 0.5, size=nb)
         c[0] = 0.0
         c[nb - 1] = 0.0
@@ -299,7 +299,7 @@ def generate(spec: Spec, threads: int = 8) -> Inputs:
         kk[:, NOISE_CH] = rk.standard_normal((n, N_NOISE), dtype=np.float32) * k_noise_scale
         kk[np.ix_(~noisy[gi], NOISE_CH)] = 0.0
         kk[:, BAND_CH] = band_k
-        kk[:, CLUSTER_CH] = np.repeat(cluster[gi], BLOCK).astype(np.float32)
+        kk[:, CLUSTER_CH] = np.repeat(cluster[gi], BLOCK)[:n].astype(np.float32)
         for t in range(min(16, n)):
             kk[t, SINK_CH[t]] = 1.0
         kk[:min(64, n), DSINK_CH] = 1.0

@@ -56,17 +56,17 @@ static double dot(const float *a, const float *b, int d)
 
 /*
  * Proxy attention of one query head (Alg. 2, lines 3-5): the representative
- * query block Q^ is the last b = B query rows; A^ = Softmax(Q^ K^T / sqrt(d)).
- * Causal reading: row i sits at position q_i = n - B + i and sees keys
- * k <= q_i; entries with k > q_i are exactly 0.
- * Output ahat is [B][n], doubles.
+ * query block Q^ is the last R = min(b, n) query rows (b = B); A^ =
+ * Softmax(Q^ K^T / sqrt(d)).  Causal reading: row i sits at position
+ * q_i = n - R + i and sees keys k <= q_i; entries with k > q_i are exactly 0.
+ * Output ahat is [R][n], doubles.
  */
-static void proxy_rows(const float *qh, const float *kg, int n, int d, int B, double *ahat)
+static void proxy_rows(const float *qh, const float *kg, int n, int d, int R, double *ahat)
 {
     const double scale = 1.0 / sqrt((double)d);
 #pragma omp parallel for schedule(dynamic, 1)
-    for (int i = 0; i < B; ++i) {
-        const int64_t qi = (int64_t)n - B + i;
+    for (int i = 0; i < R; ++i) {
+        const int64_t qi = (int64_t)n - R + i;
         const float *qrow = qh + qi * d;
         double *row = ahat + (int64_t)i * n;
         double m = -INFINITY;
@@ -87,65 +87,69 @@ static void proxy_rows(const float *qh, const float *kg, int n, int d, int B, do
 
 /*
  * Directional block scores (Alg. 3, lines 3 and 5) and C_struct (Eq. 2).
- *   a_v = colmean(A^): a_v[k] = (1/B) sum_i A^[i,k]
- *   a_s = diagmean(A^): the diagonal through (i,k) is indexed by the key it
- *         meets in the last query row, sigma = k + (B-1-i), so that slash
- *         position n-1 is offset 0 (recency) and position 0 the farthest
- *         diagonal (sink region); a_s[sigma] = (1/B) sum over valid (i,k).
- *   p_d = blockpool(a_d): sum over the B positions of each block.
- *   C_struct = (1/B) sum_i sum_{k in anchor} A^[i,k], anchor = first w_sink
- *              keys and last w_local keys (a set: overlaps counted once).
+ * Blocks partition the n tokens into N_b = ceil(n / B) blocks (Section 4.3);
+ * the last one holds n - (N_b - 1) B tokens.
+ *   a_v = colmean(A^): a_v[k] = (1/R) sum_i A^[i,k]
+ *   a_s = diagmean(A^): entry (i,k) lies on the diagonal of offset
+ *         o = q_i - k >= 0; diagonals are grouped into offset blocks
+ *         floor(o / B), and slash block j is offset block N_b - 1 - j, so
+ *         slash block N_b - 1 is the recency band (offsets 0 .. B-1) and
+ *         slash block 0 the farthest diagonals (the sink region).
+ *   p_d = blockpool(a_d): sum over the positions of each block.
+ *   C_struct = (1/R) sum_i sum_{k in anchor} A^[i,k], anchor = the first
+ *              and the last block (the w_sink = w_local = B windows of
+ *              Section 4.3), one block when N_b = 1.
  */
-static void block_scores(const double *ahat, int n, int B, int w_sink, int w_local,
-                         double *pv, double *ps, double *cstruct)
+static void block_scores(const double *ahat, int n, int B, int R, double *pv, double *ps,
+                         double *cstruct)
 {
-    const int nb = n / B;
+    const int nb = (n + B - 1) / B;
 #pragma omp parallel for schedule(static)
     for (int j = 0; j < nb; ++j) {
         double sv = 0.0, ss = 0.0;
-        for (int i = 0; i < B; ++i) {
-            const int64_t qi = (int64_t)n - B + i;
+        for (int i = 0; i < R; ++i) {
+            const int64_t qi = (int64_t)n - R + i;
             const double *row = ahat + (int64_t)i * n;
-            for (int c = 0; c < B; ++c) {
-                int64_t k = (int64_t)j * B + c;
-                sv += row[k]; /* zero where k > q_i */
-                int64_t sigma = (int64_t)j * B + c;
-                int64_t kk = sigma - (B - 1 - i);
-                if (kk >= 0 && kk <= qi) ss += row[kk];
-            }
+            /* key block j: keys jB .. min(jB + B, n) - 1 (zero past q_i) */
+            for (int64_t k = (int64_t)j * B; k < (int64_t)(j + 1) * B && k < n; ++k) sv += row[k];
+            /* slash block j: offsets (Nb-1-j)B .. (Nb-j)B - 1, keys q_i - o >= 0 */
+            for (int64_t o = (int64_t)(nb - 1 - j) * B; o < (int64_t)(nb - j) * B && o <= qi; ++o)
+                ss += row[qi - o];
         }
-        pv[j] = sv / B;
-        ps[j] = ss / B;
+        pv[j] = sv / R;
+        ps[j] = ss / R;
     }
     double cs = 0.0;
-    for (int i = 0; i < B; ++i) {
+    const int64_t last0 = (int64_t)(nb - 1) * B;
+    for (int i = 0; i < R; ++i) {
         const double *row = ahat + (int64_t)i * n;
         for (int64_t k = 0; k < n; ++k)
-            if (k < w_sink || k >= (int64_t)n - w_local) cs += row[k];
+            if (k < B || k >= last0) cs += row[k];
     }
-    *cstruct = cs / B;
+    *cstruct = cs / R;
 }
 
-/* Single-head proxy map, exported for the brute-force pins. */
+/* Single-head proxy map, exported for the brute-force pins; ahat is [R][n]. */
 int orc_proxy_map(const uint16_t *q, const uint16_t *k, int n, int hq, int hkv, int d, int B,
                   int h, double *ahat)
 {
-    if (n < B || n % B || hq % hkv || h < 0 || h >= hq) return 1;
-    const int g = h / (hq / hkv);
+    if (n < 1 || B < 1 || hq % hkv || h < 0 || h >= hq) return 1;
+    const int g = h / (hq / hkv), R = n < B ? n : B;
     float *qh = widen(q + (int64_t)h * n * d, (int64_t)n * d);
     float *kg = widen(k + (int64_t)g * n * d, (int64_t)n * d);
     if (!qh || !kg) { free(qh); free(kg); return 2; }
-    proxy_rows(qh, kg, n, d, B, ahat);
+    proxy_rows(qh, kg, n, d, R, ahat);
     free(qh);
     free(kg);
     return 0;
 }
 
+/* ahat is [R][n] with R = min(B, n); the anchor windows must equal B. */
 int orc_block_scores(const double *ahat, int n, int B, int w_sink, int w_local,
                      double *pv, double *ps, double *cstruct)
 {
-    if (n < B || n % B) return 1;
-    block_scores(ahat, n, B, w_sink, w_local, pv, ps, cstruct);
+    if (n < 1 || B < 1 || w_sink != B || w_local != B) return 1;
+    block_scores(ahat, n, B, n < B ? n : B, pv, ps, cstruct);
     return 0;
 }
 
@@ -153,28 +157,27 @@ int orc_block_scores(const double *ahat, int n, int B, int w_sink, int w_local,
  * PatSearch (Alg. 2) for every query head: proxy map, block scores,
  * C_struct (Eq. 2) and the routing rule "VS iff C_struct >= tau_proxy"
  * (Alg. 2, lines 9-13), the comparison taken in float.
- * pattern: 1 = VS, 0 = PE.
+ * pattern: 1 = VS, 0 = PE.  p_v and p_s are [hq][N_b].
  */
 int orc_route(const uint16_t *q, const uint16_t *k, int n, int hq, int hkv, int d, int B,
               float tau, int w_sink, int w_local,
               double *pv, double *ps, double *cstruct, uint8_t *pattern)
 {
-    if (n < B || n % B || hq % hkv) return 1;
-    const int nb = n / B, G = hq / hkv;
-    double *ahat = (double *)malloc((size_t)B * n * sizeof(double));
+    if (n < 1 || B < 1 || hq % hkv || w_sink != B || w_local != B) return 1;
+    const int nb = (n + B - 1) / B, G = hq / hkv, R = n < B ? n : B;
+    double *ahat = (double *)malloc((size_t)R * n * sizeof(double));
     float *qlast = (float *)malloc((size_t)n * d * sizeof(float));
     if (!ahat || !qlast) { free(ahat); free(qlast); return 2; }
     for (int g = 0; g < hkv; ++g) {
         float *kg = widen(k + (int64_t)g * n * d, (int64_t)n * d);
         if (!kg) { free(ahat); free(qlast); return 2; }
         for (int h = g * G; h < (g + 1) * G; ++h) {
-            /* only the last B query rows are read; widen those */
+            /* only the last R query rows are read; widen those */
             const uint16_t *qh = q + (int64_t)h * n * d;
-            for (int64_t e = (int64_t)(n - B) * d; e < (int64_t)n * d; ++e)
+            for (int64_t e = (int64_t)(n - R) * d; e < (int64_t)n * d; ++e)
                 qlast[e] = bf16_to_f32(qh[e]);
-            proxy_rows(qlast, kg, n, d, B, ahat);
-            block_scores(ahat, n, B, w_sink, w_local, pv + (int64_t)h * nb, ps + (int64_t)h * nb,
-                         cstruct + h);
+            proxy_rows(qlast, kg, n, d, R, ahat);
+            block_scores(ahat, n, B, R, pv + (int64_t)h * nb, ps + (int64_t)h * nb, cstruct + h);
             pattern[h] = ((float)cstruct[h] >= tau) ? 1 : 0;
         }
         free(kg);
@@ -272,7 +275,8 @@ int orc_gamma_select(const double *p, int nb, float gamma, int kmin, int32_t *se
 
 /*
  * Pooled map of one query head for the PE path (Alg. 4, lines 3-6):
- *   Qbar[qb] = mean of Q over the B tokens of query block qb (all queries),
+ *   Qbar[qb] = mean of Q over the tokens of query block qb (all queries; the
+ *              last block may hold fewer than B),
  *   Kbar[kb] = mean of K over key block kb,
  *   Abar = row softmax of Qbar Kbar^T / sqrt(d) over the causal key blocks
  *          kb <= qb (entries kb > qb are 0),
@@ -282,8 +286,8 @@ int orc_gamma_select(const double *p, int nb, float gamma, int kmin, int32_t *se
 int orc_pe_map(const uint16_t *q, const uint16_t *k, int n, int hq, int hkv, int d, int B,
                int h, double *abar)
 {
-    if (n < B || n % B || hq % hkv || h < 0 || h >= hq) return 1;
-    const int nb = n / B, g = h / (hq / hkv);
+    if (n < 1 || B < 1 || hq % hkv || h < 0 || h >= hq) return 1;
+    const int nb = (n + B - 1) / B, g = h / (hq / hkv);
     const double scale = 1.0 / sqrt((double)d);
     double *qbar = (double *)calloc((size_t)nb * d, sizeof(double));
     double *kbar = (double *)calloc((size_t)nb * d, sizeof(double));
@@ -291,7 +295,8 @@ int orc_pe_map(const uint16_t *q, const uint16_t *k, int n, int hq, int hkv, int
     const uint16_t *qh = q + (int64_t)h * n * d, *kg = k + (int64_t)g * n * d;
 #pragma omp parallel for schedule(static)
     for (int b = 0; b < nb; ++b) {
-        for (int t = 0; t < B; ++t) {
+        const int len = (b == nb - 1) ? n - b * B : B;   /* tokens in block b */
+        for (int t = 0; t < len; ++t) {
             int64_t pos = (int64_t)b * B + t;
             for (int c = 0; c < d; ++c) {
                 qbar[(int64_t)b * d + c] += (double)bf16_to_f32(qh[pos * d + c]);
@@ -299,8 +304,8 @@ int orc_pe_map(const uint16_t *q, const uint16_t *k, int n, int hq, int hkv, int
             }
         }
         for (int c = 0; c < d; ++c) {
-            qbar[(int64_t)b * d + c] /= B;
-            kbar[(int64_t)b * d + c] /= B;
+            qbar[(int64_t)b * d + c] /= len;
+            kbar[(int64_t)b * d + c] /= len;
         }
     }
 #pragma omp parallel for schedule(dynamic, 4)
@@ -407,14 +412,16 @@ int64_t orc_expand(int nb, int vs, const int32_t *sv, int nv, const int32_t *ss,
  * query at position t in block qb the allowed keys are the tokens of the
  * listed key blocks that are not in its future (k <= t).
  * row_ptr is [hq][Nb+1] (absolute offsets into col_idx); rows lists the
- * (h*Nb + qb) query blocks to compute; out is [nrows][B][d] doubles.
+ * (h*Nb + qb) query blocks to compute; out is [nrows][B][d] doubles (rows of
+ * positions >= n in a partial last block are left 0).  Keys k >= n do not
+ * exist: k <= t < n excludes them.
  */
 int orc_attend(const uint16_t *q, const uint16_t *k, const uint16_t *v, int n, int hq, int hkv,
                int d, int B, const int32_t *row_ptr, const int32_t *col_idx,
                const int32_t *rows, int nrows, double *out)
 {
-    if (n < B || n % B || hq % hkv) return 1;
-    const int nb = n / B, G = hq / hkv;
+    if (n < 1 || B < 1 || hq % hkv) return 1;
+    const int nb = (n + B - 1) / B, G = hq / hkv;
     const double scale = 1.0 / sqrt((double)d);
     for (int g = 0; g < hkv; ++g) {
         int any = 0;
@@ -429,6 +436,11 @@ int orc_attend(const uint16_t *q, const uint16_t *k, const uint16_t *v, int n, i
                 const int h = rows[r] / nb, qb = rows[r] % nb;
                 if (h / G != g) continue;
                 const int64_t qpos = (int64_t)qb * B + t;
+                double *o = out + ((int64_t)r * B + t) * d;
+                if (qpos >= n) {                 /* past the end: rows are 0 */
+                    for (int c = 0; c < d; ++c) o[c] = 0.0;
+                    continue;
+                }
                 float qrow[1024];
                 const uint16_t *qsrc = q + ((int64_t)h * n + qpos) * d;
                 for (int c = 0; c < d; ++c) qrow[c] = bf16_to_f32(qsrc[c]);
@@ -443,7 +455,6 @@ int orc_attend(const uint16_t *q, const uint16_t *k, const uint16_t *v, int n, i
                         if (s > m) m = s;
                     }
                 double l = 0.0;
-                double *o = out + ((int64_t)r * B + t) * d;
                 for (int c = 0; c < d; ++c) o[c] = 0.0;
                 for (int e = 0; e < len; ++e)
                     for (int c = 0; c < B; ++c) {
@@ -472,8 +483,8 @@ int orc_attend_queries(const uint16_t *q, const uint16_t *k, const uint16_t *v, 
                        int hkv, int d, int B, const int32_t *row_ptr, const int32_t *col_idx,
                        const int32_t *qsel, int nsel, double *out)
 {
-    if (n < B || n % B || hq % hkv || d > 1024) return 1;
-    const int nb = n / B, G = hq / hkv;
+    if (n < 1 || B < 1 || hq % hkv || d > 1024) return 1;
+    const int nb = (n + B - 1) / B, G = hq / hkv;
     const double scale = 1.0 / sqrt((double)d);
 #pragma omp parallel for schedule(dynamic, 1)
     for (int r = 0; r < nsel; ++r) {

@@ -84,9 +84,14 @@ def _u16(x) -> np.ndarray:
     return x.contiguous().view(torch.int16).numpy().view(np.uint16)
 
 
+def nblocks(n: int, B: int = 128) -> int:
+    """N_b = ceil(n / B): the last block may be partial (Section 4.3)."""
+    return (n + B - 1) // B
+
+
 def proxy_map(q, k, n, hq, hkv, d, h, B=128) -> np.ndarray:
-    """A^ of one query head, [B, n] float64 (Alg. 2, lines 3-5)."""
-    out = np.zeros((B, n), dtype=np.float64)
+    """A^ of one query head, [min(B, n), n] float64 (Alg. 2, lines 3-5)."""
+    out = np.zeros((min(B, n), n), dtype=np.float64)
     rc = lib().orc_proxy_map(_p(_u16(q)), _p(_u16(k)), n, hq, hkv, d, B, h, _p(out))
     assert rc == 0, rc
     return out
@@ -96,7 +101,8 @@ def block_scores(ahat: np.ndarray, B=128, w_sink=W_SINK, w_local=W_LOCAL):
     """(p_v, p_s, C_struct) of one head from its A^ (Alg. 3 lines 3-5, Eq. 2)."""
     ahat = np.ascontiguousarray(ahat, dtype=np.float64)
     n = ahat.shape[1]
-    nb = n // B
+    assert ahat.shape[0] == min(B, n)
+    nb = nblocks(n, B)
     pv = np.zeros(nb)
     ps = np.zeros(nb)
     cs = np.zeros(1)
@@ -115,7 +121,7 @@ class Route:
 
 def route(q, k, n, hq, hkv, d=128, B=128, tau=TAU_PROXY, w_sink=W_SINK, w_local=W_LOCAL) -> Route:
     """PatSearch (Alg. 2) for every query head."""
-    nb = n // B
+    nb = nblocks(n, B)
     pv = np.zeros((hq, nb))
     ps = np.zeros((hq, nb))
     cs = np.zeros(hq)
@@ -157,7 +163,7 @@ def gamma_select(p: np.ndarray, gamma: float = GAMMA, kmin_blocks: int = 0) -> n
 
 def pe_map(q, k, n, hq, hkv, d, h, B=128) -> np.ndarray:
     """Normalised pooled map A-bar of one query head, [Nb, Nb] (Alg. 4, lines 3-6)."""
-    nb = n // B
+    nb = nblocks(n, B)
     out = np.zeros((nb, nb), dtype=np.float64)
     rc = lib().orc_pe_map(_p(_u16(q)), _p(_u16(k)), n, hq, hkv, d, B, h, _p(out))
     assert rc == 0, rc
@@ -262,7 +268,7 @@ def plan(q, k, n, hq, hkv, d=128, B=128, alpha=1.0, tau=TAU_PROXY, gamma=GAMMA,
 
     Head h's lists start at offset h*Nb*(Nb+1)/2 of col_idx (its worst case).
     `routed` reuses an earlier route() result for the same inputs."""
-    nb = n // B
+    nb = nblocks(n, B)
     r = routed if routed is not None else route(q, k, n, hq, hkv, d, B, tau, B, B)
     per = nb * (nb + 1) // 2
     row_ptr = np.zeros((hq, nb + 1), dtype=np.int32)

@@ -434,3 +434,139 @@ def test_attend_queries_is_textbook():
     ref = sdpa64(q, k, v, 2, torch.ones(n, n, dtype=torch.bool).tril()).numpy()
     for i, (h, t) in enumerate(sel):
         np.testing.assert_allclose(got[i], ref[h, t], rtol=1e-10, atol=1e-12)
+
+
+# ------------------------------------------------- ragged n (N_b = ceil(n/B))
+def brute_proxy_any(q, k, h, G, B):
+    """A^ for any n: the last R = min(B, n) query rows, causal."""
+    n, d = q.shape[1], q.shape[2]
+    R = min(B, n)
+    qh = q[h, n - R:].double().numpy()
+    kg = k[h // G].double().numpy()
+    s = qh @ kg.T / math.sqrt(d)
+    qi = n - R + np.arange(R)
+    s[np.arange(n)[None, :] > qi[:, None]] = -np.inf
+    s -= s.max(axis=1, keepdims=True)
+    e = np.exp(s)
+    return e / e.sum(axis=1, keepdims=True)
+
+
+def brute_scores_any(a, B):
+    """p_v by block column sums (partial last block); p_s by the offset of
+    every entry from its query's diagonal: slash block Nb-1-floor(o/B)."""
+    R, n = a.shape
+    nb = -(-n // B)
+    starts = np.arange(0, n, B)
+    pv = np.add.reduceat(a.sum(0), starts) / R
+    qi = (n - R + np.arange(R))[:, None]
+    kk = np.arange(n)[None, :]
+    valid = kk <= qi
+    j = nb - 1 - (qi - kk) // B
+    ps = np.zeros(nb)
+    np.add.at(ps, j[valid], a[valid])
+    return pv, ps / R
+
+
+@pytest.mark.parametrize("n,B", [(1, 128), (100, 128), (129, 128), (300, 128), (200, 64),
+                                 (1000, 128), (1111, 32)])
+def test_ragged_proxy_and_scores_bruteforce(n, B):
+    d, hq, hkv = 32, 2, 1
+    q, k, _ = rand_qkv(n, hq, hkv, d, seed=n + B, scale=1.5)
+    nb = -(-n // B)
+    r = O.route(q, k, n, hq, hkv, d, B, 0.2, B, B)
+    for h in range(hq):
+        a = O.proxy_map(q, k, n, hq, hkv, d, h, B)
+        a_bf = brute_proxy_any(q, k, h, hq // hkv, B)
+        assert a.shape == (min(B, n), n)
+        np.testing.assert_allclose(a, a_bf, rtol=1e-12, atol=1e-15)
+        pv_bf, ps_bf = brute_scores_any(a_bf, B)
+        np.testing.assert_allclose(r.p_v[h], pv_bf, rtol=1e-11, atol=1e-15)
+        np.testing.assert_allclose(r.p_s[h], ps_bf, rtol=1e-11, atol=1e-15)
+        assert r.p_v[h].sum() == pytest.approx(1.0, abs=1e-12)
+        assert r.p_s[h].sum() == pytest.approx(1.0, abs=1e-12)
+        # C_struct: mass of the first and the last block (one block if Nb = 1)
+        anchor = np.zeros(n, bool)
+        anchor[:B] = True
+        anchor[(nb - 1) * B:] = True
+        assert r.c_struct[h] == pytest.approx(a_bf[:, anchor].sum(1).mean(), rel=1e-12)
+        want = pv_bf[0] + (pv_bf[-1] if nb > 1 else 0.0)
+        assert r.c_struct[h] == pytest.approx(want, rel=1e-12)
+
+
+def test_ragged_offset_reading_equals_trace_reading_when_aligned():
+    """For n a multiple of B the offset-indexed slash blocks equal the
+    diagonal-trace definition (sigma = k + B-1-i) used for aligned n."""
+    n, B, d = 512, 64, 16
+    q, k, _ = rand_qkv(n, 1, 1, d, seed=77)
+    a = brute_proxy_any(q, k, 0, 1, B)
+    pv1, ps1 = brute_scores_any(a, B)
+    pv2, ps2 = brute_scores(a, B)
+    np.testing.assert_allclose(pv1, pv2, rtol=1e-12)
+    np.testing.assert_allclose(ps1, ps2, rtol=1e-12)
+
+
+def test_ragged_uniform_closed_form():
+    """Q = 0, n = 1000: row i is uniform over q_i + 1 keys; the last block
+    holds 1000 - 7*128 = 104 keys."""
+    n, B = 1000, 128
+    q = torch.zeros(1, n, 128, dtype=torch.bfloat16)
+    _, k, _ = rand_qkv(n, 1, 1, 128, seed=6)
+    r = O.route(q, k, n, 1, 1)
+    qi = n - B + np.arange(B)
+    pv0 = np.mean(B / (qi + 1.0))
+    last0 = 7 * B
+    pvl = np.mean(np.maximum(qi - last0 + 1, 0) / (qi + 1.0))
+    assert r.p_v[0][0] == pytest.approx(pv0, rel=1e-12)
+    assert r.p_v[0][-1] == pytest.approx(pvl, rel=1e-12)
+    # slash recency block: offsets 0..127 of every row
+    assert r.p_s[0][-1] == pytest.approx(np.mean(B / (qi + 1.0)), rel=1e-12)
+
+
+def brute_pe_map_any(q, k, h, G, B):
+    n, d = q.shape[1], q.shape[2]
+    nb = -(-n // B)
+    qd, kd = q[h].double().numpy(), k[h // G].double().numpy()
+    qb = np.stack([qd[b * B:(b + 1) * B].mean(0) for b in range(nb)])
+    kb = np.stack([kd[b * B:(b + 1) * B].mean(0) for b in range(nb)])
+    s = qb @ kb.T / math.sqrt(d)
+    s[np.triu(np.ones((nb, nb), bool), 1)] = -np.inf
+    s -= s.max(1, keepdims=True)
+    e = np.exp(s)
+    a = e / e.sum(1, keepdims=True)
+    return a / a.sum()
+
+
+@pytest.mark.parametrize("n,B", [(300, 128), (1000, 128), (77, 32), (5, 128)])
+def test_ragged_pe_map_bruteforce(n, B):
+    d = 32
+    q, k, _ = rand_qkv(n, 2, 1, d, seed=500 + n, scale=3.0)
+    for h in range(2):
+        np.testing.assert_allclose(O.pe_map(q, k, n, 2, 1, d, h, B), brute_pe_map_any(q, k, h, 2, B),
+                                   rtol=1e-11, atol=1e-16)
+
+
+@pytest.mark.parametrize("n,B", [(1, 32), (37, 32), (300, 128), (1000, 128)])
+def test_ragged_attend_is_textbook(n, B):
+    d, hq, hkv = 16, 4, 2
+    nb = -(-n // B)
+    q, k, v = rand_qkv(n, hq, hkv, d, seed=700 + n, scale=1.2)
+    rp, ci = O.full_causal_lists(hq, nb)
+    out = O.attend(q, k, v, n, hq, hkv, d, rp, ci, np.arange(hq * nb), B).reshape(hq, nb * B, d)
+    causal = torch.ones(n, n, dtype=torch.bool).tril()
+    ref = sdpa64(q, k, v, hq // hkv, causal).numpy()
+    np.testing.assert_allclose(out[:, :n], ref, rtol=1e-10, atol=1e-12)
+    assert np.all(out[:, n:] == 0)
+    sel = np.array([[h, p] for h in range(hq) for p in (0, n - 1, n // 2)], dtype=np.int32)
+    one = O.attend_queries(q, k, v, n, hq, hkv, d, rp, ci, sel, B)
+    np.testing.assert_allclose(one, ref[sel[:, 0], sel[:, 1]], rtol=1e-10, atol=1e-12)
+
+
+def test_ragged_plan_small_nb_is_dense():
+    """N_b <= 2 (mu = r / (N_b - 2) undefined) selects every causal block."""
+    for n in (50, 200, 256):
+        q, k, _ = rand_qkv(n, 2, 1, 128, seed=n)
+        p = O.plan(q, k, n, 2, 1)
+        rp, ci = O.full_causal_lists(2, -(-n // 128))
+        for h in range(2):
+            lens = np.diff(p.row_ptr[h])
+            assert lens.tolist() == np.diff(rp[h]).tolist()
