@@ -105,7 +105,7 @@ def main():
     crisp.lib()
     spec = synth.config_spec(WORKLOAD)
     n, hq, hkv = spec.n, spec.hq, spec.hkv
-    nb = n // B
+    nb = -(-n // B)
     log(f"generating {WORKLOAD}: n={n} hq={hq} hkv={hkv}")
     t0 = time.perf_counter()
     inp = synth.generate(spec, threads=16)

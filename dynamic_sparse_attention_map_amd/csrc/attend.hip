@@ -143,7 +143,11 @@ attend_pair(int b, uint16_t* lds, const uint16_t* __restrict__ q, const uint16_t
     }
 
     const int qc = 32 * wq + l32;                         // query within its block
-    const size_t qrow = (size_t)h * n + (size_t)(active ? myqb : 0) * kB + qc;
+    // a partial last block has rows past the end: they load the last row
+    // (their results are never stored)
+    const int qpos = (active ? myqb : 0) * kB + qc;
+    const bool q_valid = active && qpos < n;
+    const size_t qrow = (size_t)h * n + min(qpos, n - 1);
     bf16x8 qf[8];
     for (int s = 0; s < 8; ++s)
         qf[s] = *reinterpret_cast<const bf16x8*>(q + qrow * kD + 16 * s + 8 * hi);
@@ -154,7 +158,8 @@ attend_pair(int b, uint16_t* lds, const uint16_t* __restrict__ q, const uint16_t
     const float rescale_gap = 8.0f / scale_log2;   // 2^8 in probability
 
     const uint16_t* kg = k + (size_t)g * n * kD;
-    const uint16_t* vg = vt + (size_t)g * kD * n;
+    const size_t n_pad = (size_t)nb * kB;                 // V^T row length
+    const uint16_t* vg = vt + (size_t)g * kD * n_pad;
 
     // staging: 2 x 16 bytes of K and 2 x 16 bytes of V^T per thread
     u32x4 pk[2], pv[2];
@@ -163,9 +168,13 @@ attend_pair(int b, uint16_t* lds, const uint16_t* __restrict__ q, const uint16_t
         for (int i = 0; i < 2; ++i) {
             const int e = tid + kThreads * i;
             const int row = e >> 4, ch = e & 15;              // 64 keys x 16 chunks
-            pk[i] = *reinterpret_cast<const u32x4*>(kg + (key0 + row) * kD + 8 * ch);
+            // keys past the end of a partial last block read as zero (every
+            // query that exists masks them: they lie in its future)
+            pk[i] = u32x4{0u, 0u, 0u, 0u};
+            if (key0 + row < (size_t)n)
+                pk[i] = *reinterpret_cast<const u32x4*>(kg + (key0 + row) * kD + 8 * ch);
             const int dr = e >> 3, vc = e & 7;                // 128 d-rows x 8 chunks
-            pv[i] = *reinterpret_cast<const u32x4*>(vg + (size_t)dr * n + key0 + 8 * vc);
+            pv[i] = *reinterpret_cast<const u32x4*>(vg + (size_t)dr * n_pad + key0 + 8 * vc);
         }
     };
     auto store_tile = [&](int stage) {
@@ -325,6 +334,7 @@ attend_pair(int b, uint16_t* lds, const uint16_t* __restrict__ q, const uint16_t
 
     if (!active) return;
     const float l = l_run + swap_half(l_run);
+    if (!q_valid) return;             // after the wave-wide exchange above
     const float inv = (l > 0.f) ? 1.0f / l : 0.f;
     uint16_t* orow = out + qrow * kD;
     for (int dt = 0; dt < 4; ++dt)
@@ -377,9 +387,10 @@ __global__ void zero_counters_kernel(int* __restrict__ ctr)
 // index swapped): vt[g][d][16 j + pi(c)] = v[g][16 j + c][d].  A lane's 8 keys
 // of a PV operand fragment, {4h .. 4h+3, 8+4h .. 8+4h+3} for lane half h (the
 // order the S^T accumulator holds them in), are then 16 contiguous bytes.
-// grid (n/64, hkv), 256 threads.
+// Rows have n_pad = N_b * B keys; keys past n are zero.
+// grid (n_pad/64, hkv), 256 threads.
 __global__ void __launch_bounds__(256)
-v_transpose_kernel(const uint16_t* __restrict__ v, int n, uint16_t* __restrict__ vt)
+v_transpose_kernel(const uint16_t* __restrict__ v, int n, int n_pad, uint16_t* __restrict__ vt)
 {
     __shared__ uint16_t tile[64][kD + 8];
     const int g = blockIdx.y, key0 = blockIdx.x * 64, tid = threadIdx.x;
@@ -387,11 +398,12 @@ v_transpose_kernel(const uint16_t* __restrict__ v, int n, uint16_t* __restrict__
     for (int i = 0; i < 4; ++i) {
         const int e = tid + 256 * i;
         const int row = e >> 4, ch = e & 15;
-        *reinterpret_cast<u32x4*>(&tile[row][8 * ch]) =
-            *reinterpret_cast<const u32x4*>(src + (size_t)row * kD + 8 * ch);
+        u32x4 val = {0u, 0u, 0u, 0u};
+        if (key0 + row < n) val = *reinterpret_cast<const u32x4*>(src + (size_t)row * kD + 8 * ch);
+        *reinterpret_cast<u32x4*>(&tile[row][8 * ch]) = val;
     }
     __syncthreads();
-    uint16_t* dst = vt + (size_t)g * kD * n + key0;
+    uint16_t* dst = vt + (size_t)g * kD * n_pad + key0;
     for (int i = 0; i < 4; ++i) {
         const int e = tid + 256 * i;
         const int d = e >> 3, c8 = e & 7;
@@ -401,7 +413,7 @@ v_transpose_kernel(const uint16_t* __restrict__ v, int n, uint16_t* __restrict__
             const int k0 = (p0 & ~12) | ((p0 & 4) << 1) | ((p0 & 8) >> 1);
             val[x] = (uint32_t)tile[k0][d] | ((uint32_t)tile[k0 + 1][d] << 16);
         }
-        *reinterpret_cast<u32x4*>(dst + (size_t)d * n + 8 * c8) = val;
+        *reinterpret_cast<u32x4*>(dst + (size_t)d * n_pad + 8 * c8) = val;
     }
 }
 
@@ -409,7 +421,9 @@ v_transpose_kernel(const uint16_t* __restrict__ v, int n, uint16_t* __restrict__
 
 hipError_t launch_v_transpose(const uint16_t* v, int n, int hkv, uint16_t* vt, hipStream_t stream)
 {
-    hipLaunchKernelGGL(v_transpose_kernel, dim3(n / 64, hkv), dim3(256), 0, stream, v, n, vt);
+    const int n_pad = (n + kB - 1) / kB * kB;
+    hipLaunchKernelGGL(v_transpose_kernel, dim3(n_pad / 64, hkv), dim3(256), 0, stream, v, n, n_pad,
+                       vt);
     return hipGetLastError();
 }
 
@@ -417,7 +431,7 @@ hipError_t launch_attend(const uint16_t* q, const uint16_t* k, const uint16_t* v
                          const int32_t* row_ptr, const int32_t* col_idx, int n, int hq, int hkv,
                          int* counters, uint16_t* out, hipStream_t stream)
 {
-    const int nb = n / kB, G = hq / hkv;
+    const int nb = (n + kB - 1) / kB, G = hq / hkv;
     const long long chunks = (long long)((nb + 1) / 2) * hkv;
     const long long items = ((chunks + 7) / 8) * 8 * G;
     const int per_xcd = (int)(items / 8);

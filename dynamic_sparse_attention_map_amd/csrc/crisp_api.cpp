@@ -37,7 +37,7 @@ struct Layout {
 Layout make_layout(const Shape& s)
 {
     Layout L{};
-    const size_t hq = s.hq, hkv = s.hkv, nb = s.nb, n = s.n;
+    const size_t hq = s.hq, hkv = s.hkv, nb = s.nb;
     const size_t tri = nb * (nb + 1) / 2;
     size_t o = 0;
     auto take = [&](size_t bytes) {
@@ -60,7 +60,7 @@ Layout make_layout(const Shape& s)
     L.bitmap = take(hq * 2 * nb);
     L.select_end = o;
     o = 0;
-    L.vt = take(hkv * kD * n * sizeof(uint16_t));
+    L.vt = take(hkv * kD * (nb * kB) * sizeof(uint16_t));     // V^T padded to N_b blocks
     L.queue = take(8 * sizeof(int));
     L.attend_end = o;
     o = L.route_end;
@@ -83,9 +83,10 @@ Layout make_layout(const Shape& s)
 int check_shape(int seq_len, int n_heads, int n_kv_heads, int head_dim, int block_size, Shape* s)
 {
     if (head_dim != kD || block_size != kB) return CRISP_ERR_UNSUPPORTED;
-    if (seq_len <= 0 || n_heads <= 0 || n_kv_heads <= 0) return CRISP_ERR_SHAPE;
-    if (seq_len % block_size != 0 || n_heads % n_kv_heads != 0) return CRISP_ERR_SHAPE;
-    const int nb = seq_len / block_size;
+    if (seq_len < 0 || n_heads <= 0 || n_kv_heads <= 0) return CRISP_ERR_SHAPE;
+    if (n_heads % n_kv_heads != 0) return CRISP_ERR_SHAPE;
+    // N_b = ceil(n / B): the last block may be partial; n = 0 is an empty call
+    const int nb = (int)(((long long)seq_len + block_size - 1) / block_size);
     if (nb > kMaxBlocks) return CRISP_ERR_UNSUPPORTED;
     const long long tri = (long long)nb * (nb + 1) / 2;
     if ((long long)n_heads * tri >= (1LL << 31)) return CRISP_ERR_UNSUPPORTED;
@@ -189,7 +190,7 @@ const char* crisp_status_string(int code)
     switch (code) {
     case CRISP_OK: return "ok";
     case CRISP_ERR_INVALID_ARG: return "invalid argument (null or misaligned pointer, or bad option)";
-    case CRISP_ERR_SHAPE: return "bad shape (seq_len % block_size, n_heads % n_kv_heads, or non-positive size)";
+    case CRISP_ERR_SHAPE: return "bad shape (negative seq_len, n_heads % n_kv_heads != 0, or non-positive head count)";
     case CRISP_ERR_UNSUPPORTED: return "unsupported (head_dim, block_size and anchor windows must be 128; N_b <= 4096)";
     case CRISP_ERR_WORKSPACE: return "workspace or CSR capacity too small";
     case CRISP_ERR_HIP: return "HIP launch error";
@@ -234,6 +235,7 @@ int crisp_route(const void* q, const void* k, int seq_len, int n_heads, int n_kv
     if (rc) return rc;
     Opts op;
     if ((rc = check_opts(opts, &op))) return rc;
+    if (s.n == 0) return CRISP_OK;
     if (bad_ptr(q) || bad_ptr(k) || bad_ptr(ws, kAlign) || !pattern || bad_ptr(c_struct, 4) ||
         bad_ptr(p_v, 4) || bad_ptr(p_s, 4))
         return CRISP_ERR_INVALID_ARG;
@@ -258,6 +260,7 @@ int crisp_select(const void* q, const void* k, const uint8_t* pattern, const flo
     Opts op;
     if ((rc = check_opts(opts, &op))) return rc;
     if (!std::isfinite(alpha) || alpha < 0.0f) return CRISP_ERR_INVALID_ARG;
+    if (s.n == 0) return CRISP_OK;
     if (bad_ptr(q) || bad_ptr(k) || bad_ptr(ws, kAlign) || !pattern || bad_ptr(p_v, 4) ||
         bad_ptr(p_s, 4) || bad_ptr(sel_v, 4) || bad_ptr(sel_s, 4) || bad_ptr(sel_counts, 4) ||
         bad_ptr(row_ptr, 4) || bad_ptr(col_idx, 4))
@@ -279,6 +282,7 @@ int crisp_attend(const void* q, const void* k, const void* v, const int32_t* row
     Shape s;
     const int rc = check_shape(seq_len, n_heads, n_kv_heads, head_dim, block_size, &s);
     if (rc) return rc;
+    if (s.n == 0) return CRISP_OK;
     if (bad_ptr(q) || bad_ptr(k) || bad_ptr(v) || bad_ptr(out) || bad_ptr(ws, kAlign) ||
         bad_ptr(row_ptr, 4) || bad_ptr(col_idx, 4))
         return CRISP_ERR_INVALID_ARG;
@@ -294,6 +298,7 @@ int crisp_attend_dense(const void* q, const void* k, const void* v, int seq_len,
     Shape s;
     const int rc = check_shape(seq_len, n_heads, n_kv_heads, head_dim, block_size, &s);
     if (rc) return rc;
+    if (s.n == 0) return CRISP_OK;
     if (bad_ptr(q) || bad_ptr(k) || bad_ptr(v) || bad_ptr(out) || bad_ptr(ws, kAlign))
         return CRISP_ERR_INVALID_ARG;
     const Layout L = make_layout(s);
@@ -311,6 +316,7 @@ int crisp_prefill(const void* q, const void* k, const void* v, int seq_len, int 
     Opts op;
     if ((rc = check_opts(opts, &op))) return rc;
     if (!std::isfinite(alpha) || alpha < 0.0f) return CRISP_ERR_INVALID_ARG;
+    if (s.n == 0) return CRISP_OK;
     if (bad_ptr(q) || bad_ptr(k) || bad_ptr(v) || bad_ptr(out) || bad_ptr(ws, kAlign))
         return CRISP_ERR_INVALID_ARG;
     const Layout L = make_layout(s);

@@ -159,7 +159,8 @@ __device__ __forceinline__ bool group_has_pe(const uint8_t* pattern, int g, int 
     return false;
 }
 
-// grid (Nb, hq + hkv): block means of Q (PE heads) and K (groups with a PE head).
+// grid (Nb, hq + hkv): block means of Q (PE heads) and K (groups with a PE
+// head), over the tokens each block holds (the last block may be partial).
 __global__ void __launch_bounds__(256)
 pe_pool_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                const uint8_t* __restrict__ pattern, int n, int hq, int G,
@@ -167,7 +168,8 @@ pe_pool_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
 {
     __shared__ float red[16][kD];
     const int qb = blockIdx.x, y = blockIdx.y, tid = threadIdx.x;
-    const int nb = n / kB;
+    const int nb = (n + kB - 1) / kB;
+    const int len = min(kB, n - qb * kB);           // tokens in block qb
     const uint16_t* src;
     float* dst;
     if (y < hq) {
@@ -182,7 +184,7 @@ pe_pool_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     }
     const int dc = tid & 15, tg = tid >> 4;
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    for (int t = tg * 8; t < tg * 8 + 8; ++t) {
+    for (int t = tg * 8; t < min(tg * 8 + 8, len); ++t) {
         const u32x4 raw = *reinterpret_cast<const u32x4*>(src + (size_t)t * kD + 8 * dc);
         for (int e = 0; e < 4; ++e) {
             acc[2 * e] += __uint_as_float(raw[e] << 16);
@@ -194,7 +196,7 @@ pe_pool_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     if (tid < kD) {
         float s = 0.f;
         for (int x = 0; x < 16; ++x) s += red[x][tid];
-        dst[tid] = s * (1.0f / kB);
+        dst[tid] = s / (float)len;
     }
 }
 
@@ -473,7 +475,7 @@ hipError_t launch_select(const uint16_t* q, const uint16_t* k, const uint8_t* pa
                          int32_t* sel_s, int32_t* sel_counts, int32_t* row_ptr, int32_t* col_idx,
                          hipStream_t stream)
 {
-    const int nb = n / kB, G = hq / hkv;
+    const int nb = (n + kB - 1) / kB, G = hq / hkv;
     hipError_t e;
 #define CRISP_CHECK_LAUNCH() \
     if ((e = hipGetLastError()) != hipSuccess) return e

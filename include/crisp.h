@@ -16,9 +16,12 @@
  *   h / (n_heads / n_kv_heads) (grouped-query attention).  out has q's shape.
  * Device pointers: every array argument is device memory, 16-byte aligned
  *   (the workspace 256-byte aligned).  opts is a host pointer (may be NULL).
- * Sizes: head_dim == 128 and block_size == 128 (B in the paper); seq_len a
- *   positive multiple of block_size; n_heads a multiple of n_kv_heads;
- *   N_b = seq_len / block_size.
+ * Sizes: head_dim == 128 and block_size == 128 (B in the paper); any
+ *   seq_len >= 0; n_heads a multiple of n_kv_heads.  Blocks partition the
+ *   sequence as in Section 4.3 of the paper: N_b = ceil(seq_len /
+ *   block_size), the last block holding seq_len - (N_b - 1) * block_size
+ *   tokens.  seq_len == 0 is an empty call: after the size and option checks
+ *   it returns CRISP_OK without reading any pointer or launching anything.
  * Ownership: the caller allocates and owns all memory, including the
  *   workspace (size from crisp_workspace_size).  The library keeps no
  *   pointer after a call returns and never allocates device memory.
@@ -44,7 +47,7 @@ extern "C" {
 enum crisp_status {
     CRISP_OK = 0,
     CRISP_ERR_INVALID_ARG = 1, /* NULL or misaligned pointer, bad option value   */
-    CRISP_ERR_SHAPE = 2,       /* seq_len % block_size, n_heads % n_kv_heads, ... */
+    CRISP_ERR_SHAPE = 2,       /* seq_len < 0, n_heads % n_kv_heads, heads <= 0   */
     CRISP_ERR_UNSUPPORTED = 3, /* head_dim / block_size / anchor windows != 128   */
     CRISP_ERR_WORKSPACE = 4,   /* workspace or CSR capacity too small             */
     CRISP_ERR_HIP = 5          /* a kernel launch failed                          */
@@ -84,14 +87,16 @@ int crisp_workspace_size(int seq_len, int n_heads, int n_kv_heads, int head_dim,
 
 /*
  * PatSearch (Alg. 2) for every query head.  The representative queries are
- * the last block_size rows; A^ = Softmax(Q^ K^T / sqrt(d)) with the causal
- * mask.  Outputs (device):
+ * the last R = min(block_size, seq_len) rows; A^ = Softmax(Q^ K^T / sqrt(d))
+ * with the causal mask.  Outputs (device):
  *   p_v, p_s   float [n_heads][N_b]  block-pooled column / diagonal means of
- *              A^ (Alg. 3 lines 3-5); each row sums to 1.  Diagonal (slash)
- *              block j collects the diagonals that meet the last query row
- *              at keys j*B .. j*B+B-1, so block N_b-1 is the recency band and
- *              block 0 the farthest diagonals.
- *   c_struct   float [n_heads]  anchor mass, Eq. 2 (= p_v[0] + p_v[N_b-1])
+ *              A^ over its R rows (Alg. 3 lines 3-5); each row sums to 1.
+ *              Entry (i, k) lies on the diagonal at offset o = q_i - k from
+ *              its query q_i; diagonal (slash) block j collects the offsets
+ *              (N_b-1-j)*B .. (N_b-j)*B - 1, so block N_b-1 is the recency
+ *              band and block 0 the farthest diagonals.
+ *   c_struct   float [n_heads]  anchor mass, Eq. 2: the first and the last
+ *              block (= p_v[0] + p_v[N_b-1]; p_v[0] when N_b = 1)
  *   pattern    uint8 [n_heads]  1 = vertical-slash, 0 = pooled estimation
  * A^ itself is never materialised.
  */
@@ -128,7 +133,8 @@ int crisp_select(const void *q, const void *k, const uint8_t *pattern, const flo
  * blocks of (h, qb), times V.  row_ptr / col_idx as written by crisp_select
  * (any absolute layout with unique lists; row_ptr must stay inside col_idx).
  * Listed blocks outside [0, qb] are ignored; a row with no valid block yields
- * zeros.  Accumulates in fp32, writes bf16 out.
+ * zeros.  Accumulates in fp32, writes bf16 out (rows < seq_len only).
+ * Uses the workspace for V re-laid out as V^T padded to N_b * B keys.
  */
 int crisp_attend(const void *q, const void *k, const void *v, const int32_t *row_ptr,
                  const int32_t *col_idx, int seq_len, int n_heads, int n_kv_heads, int head_dim,

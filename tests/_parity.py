@@ -34,7 +34,7 @@ def to_dev(inp):
 
 def gpu_route(q, k, ws, opts=None):
     hq, n, _ = q.shape
-    nb = n // B
+    nb = -(-n // B)
     dev = q.device
     pattern = torch.zeros(hq, dtype=torch.uint8, device=dev)
     cs = torch.zeros(hq, dtype=torch.float32, device=dev)
@@ -46,7 +46,7 @@ def gpu_route(q, k, ws, opts=None):
 
 def gpu_select(q, k, r, alpha, ws, opts=None):
     hq, n, _ = q.shape
-    nb = n // B
+    nb = -(-n // B)
     dev = q.device
     _, cap = crisp.crisp_workspace_size(n, hq, k.shape[0])
     sel_v = torch.full((hq, nb), -1, dtype=torch.int32, device=dev)
@@ -151,7 +151,7 @@ def check_select(inp, gr, gs, alpha, orc_route: O.Route, heads=None, rep=None, g
     """Sets (exempt-aware), counts, and exact expansion of the GPU's own sets."""
     sp = inp.spec
     n, hq, hkv = sp.n, sp.hq, sp.hkv
-    nb = n // B
+    nb = -(-n // B)
     rep = rep or Report(sp.name)
     heads = range(hq) if heads is None else heads
     tri = nb * (nb + 1) // 2

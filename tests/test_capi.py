@@ -1,0 +1,125 @@
+"""The C-ABI library on the host (no GPU needed): every function declared in
+include/crisp.h is exported, sizes are what the header states, and argument
+validation answers before anything is launched."""
+import ctypes as C
+
+import pytest
+
+from dynamic_sparse_attention_map_amd import crisp
+
+OK, INVALID, SHAPE, UNSUPPORTED, WORKSPACE, HIP = range(6)
+
+
+@pytest.fixture(scope="module")
+def L():
+    return crisp.lib()
+
+
+def test_every_header_symbol_is_exported(L):
+    names = crisp.header_symbols()
+    assert {"crisp_route", "crisp_select", "crisp_prefill", "crisp_attend", "crisp_attend_dense",
+            "crisp_workspace_size", "crisp_status_string", "crisp_set_stage_events"} <= set(names)
+    for name in names:
+        assert hasattr(L, name), name
+
+
+def test_status_strings(L):
+    seen = set()
+    for code in range(6):
+        s = crisp.status_string(code)
+        assert s and s != "unknown status"
+        seen.add(s)
+    assert len(seen) == 6
+    assert crisp.status_string(99) == "unknown status"
+
+
+def ws_size(n, hq=32, hkv=8, d=128, b=128):
+    ws, cap = C.c_size_t(0), C.c_int64(0)
+    rc = crisp.lib().crisp_workspace_size(n, hq, hkv, d, b, C.byref(ws), C.byref(cap))
+    return rc, ws.value, cap.value
+
+
+@pytest.mark.parametrize("n", [1, 127, 128, 129, 300, 4096, 131072, 524288])
+def test_workspace_size_ragged(n):
+    rc, ws, cap = ws_size(n)
+    assert rc == OK
+    nb = -(-n // 128)
+    assert cap == 32 * nb * (nb + 1) // 2
+    # at least the CSR lists, both score arrays and the padded V^T
+    assert ws >= cap * 4 + 2 * 32 * nb * 4 + 8 * 128 * nb * 128 * 2
+    assert ws % 256 == 0
+
+
+def test_workspace_size_monotone_and_empty():
+    sizes = [ws_size(n)[1] for n in (1, 128, 129, 1000, 10000)]
+    assert sizes == sorted(sizes)
+    rc, ws, cap = ws_size(0)
+    assert rc == OK and cap == 0
+
+
+@pytest.mark.parametrize("args,code", [
+    ((-1, 32, 8, 128, 128), SHAPE),
+    ((128, 30, 8, 128, 128), SHAPE),
+    ((128, 0, 8, 128, 128), SHAPE),
+    ((128, 32, 0, 128, 128), SHAPE),
+    ((128, 32, 8, 64, 128), UNSUPPORTED),
+    ((128, 32, 8, 128, 64), UNSUPPORTED),
+    ((4096 * 128 + 1, 32, 8, 128, 128), UNSUPPORTED),
+])
+def test_workspace_size_errors(args, code):
+    ws, cap = C.c_size_t(0), C.c_int64(0)
+    assert crisp.lib().crisp_workspace_size(*args, C.byref(ws), C.byref(cap)) == code
+
+
+def test_workspace_size_null_outputs(L):
+    assert L.crisp_workspace_size(128, 4, 1, 128, 128, None, None) == INVALID
+
+
+def _opts(**kw):
+    o = crisp.crisp_opts(0.2, 0.95, 1024, 128, 128)
+    for k, v in kw.items():
+        setattr(o, k, v)
+    return C.byref(o)
+
+
+FAKE = C.c_void_p(1 << 20)      # aligned, never dereferenced: validation fails first
+
+
+def test_validation_before_launch(L):
+    # null / misaligned pointers
+    assert L.crisp_route(None, FAKE, 256, 4, 1, 128, 128, None, FAKE, 1 << 30, FAKE, FAKE, FAKE,
+                         FAKE, None) == INVALID
+    assert L.crisp_attend(FAKE, FAKE, C.c_void_p((1 << 20) + 2), FAKE, FAKE, 256, 4, 1, 128, 128,
+                          FAKE, 1 << 30, FAKE, None) == INVALID
+    # shapes and options
+    assert L.crisp_prefill(FAKE, FAKE, FAKE, 256, 4, 3, 128, 128, 1.0, None, FAKE, 1 << 30, FAKE,
+                           None) == SHAPE
+    assert L.crisp_prefill(FAKE, FAKE, FAKE, 256, 4, 1, 128, 128, -1.0, None, FAKE, 1 << 30, FAKE,
+                           None) == INVALID
+    assert L.crisp_prefill(FAKE, FAKE, FAKE, 256, 4, 1, 128, 128, float("nan"), None, FAKE, 1 << 30,
+                           FAKE, None) == INVALID
+    assert L.crisp_prefill(FAKE, FAKE, FAKE, 256, 4, 1, 128, 128, 1.0, _opts(gamma=0.0), FAKE,
+                           1 << 30, FAKE, None) == INVALID
+    assert L.crisp_prefill(FAKE, FAKE, FAKE, 256, 4, 1, 128, 128, 1.0, _opts(k_min_tokens=100),
+                           FAKE, 1 << 30, FAKE, None) == INVALID
+    assert L.crisp_prefill(FAKE, FAKE, FAKE, 256, 4, 1, 128, 128, 1.0, _opts(w_sink=64), FAKE,
+                           1 << 30, FAKE, None) == UNSUPPORTED
+    # workspace too small
+    _, need, cap = ws_size(300, 4, 1)
+    assert L.crisp_prefill(FAKE, FAKE, FAKE, 300, 4, 1, 128, 128, 1.0, None, FAKE, need - 256, FAKE,
+                           None) == WORKSPACE
+    assert L.crisp_select(FAKE, FAKE, FAKE, FAKE, FAKE, 300, 4, 1, 128, 128, 1.0, None, FAKE, need,
+                          FAKE, FAKE, FAKE, FAKE, FAKE, cap - 1, None) == WORKSPACE
+
+
+def test_empty_sequence_is_a_no_op(L):
+    """seq_len == 0: OK without reading any pointer (all NULL here)."""
+    assert L.crisp_route(None, None, 0, 4, 1, 128, 128, None, None, 0, None, None, None, None,
+                         None) == OK
+    assert L.crisp_select(None, None, None, None, None, 0, 4, 1, 128, 128, 1.0, None, None, 0, None,
+                          None, None, None, None, 0, None) == OK
+    assert L.crisp_attend(None, None, None, None, None, 0, 4, 1, 128, 128, None, 0, None, None) == OK
+    assert L.crisp_attend_dense(None, None, None, 0, 4, 1, 128, 128, None, 0, None, None) == OK
+    assert L.crisp_prefill(None, None, None, 0, 4, 1, 128, 128, 1.0, None, None, 0, None, None) == OK
+    # the size and option checks still run
+    assert L.crisp_prefill(None, None, None, 0, 4, 3, 128, 128, 1.0, None, None, 0, None, None) == SHAPE

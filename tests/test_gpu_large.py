@@ -48,7 +48,7 @@ def sample_queries(nb, hq, blocks_per_head, queries_per_block, seed):
 def full_case(name, n=None, blocks_per_head=64, queries_per_block=2, prefill_check=True):
     spec = synth.config_spec(name, n)
     n, hq, hkv = spec.n, spec.hq, spec.hkv
-    nb = n // B
+    nb = -(-n // B)
     P.log(f"case {name}: n={n} hq={hq} hkv={hkv}; generating")
     inp = synth.generate(spec, threads=16)
     q, k, v = P.to_dev(inp)
@@ -109,7 +109,7 @@ def test_c5_mass_cliff_sweep(n):
     block counts of CRISP against the cumulative gamma = 0.95 selector."""
     spec = synth.config_spec("c5", n)
     hq, hkv = spec.hq, spec.hkv
-    nb = n // B
+    nb = -(-n // B)
     P.log(f"case c5: n={n}; generating")
     inp = synth.generate(spec, threads=16)
     q, k, _ = P.to_dev(inp)

@@ -25,7 +25,7 @@ def case(inp, alpha=1.0, rows=None, tag=""):
     """Route, select and attend on the GPU; check all three against the oracle."""
     sp = inp.spec
     n, hq, hkv = sp.n, sp.hq, sp.hkv
-    nb = n // B
+    nb = -(-n // B)
     P.log(f"case {sp.name}{tag}: n={n} hq={hq} hkv={hkv} alpha={alpha}")
     q, k, v = P.to_dev(inp)
     ws = crisp.alloc_workspace(n, hq, hkv)
@@ -41,7 +41,9 @@ def case(inp, alpha=1.0, rows=None, tag=""):
     if rows is None:
         rows = np.arange(hq * nb, dtype=np.int32)
     want = O.attend(inp.q, inp.k, inp.v, n, hq, hkv, 128, plan.row_ptr, plan.col_idx, rows)
-    got = out.float().cpu().numpy().reshape(hq * nb, B, 128)[rows]
+    full = torch.zeros(hq, nb * B, 128)          # rows past n (a partial last block) are 0
+    full[:, :n] = out.float().cpu()
+    got = full.numpy().reshape(hq * nb, B, 128)[rows]
     P.check_outputs(got, want, f"{sp.name}{tag} attend")
     for h in range(hq):
         sel = rows // nb == h
@@ -57,7 +59,7 @@ def test_c1_full_parity():
 def test_c1_dense_matches_oracle():
     inp = synth.generate(synth.config_spec("c1"))
     n, hq, hkv = 4096, 4, 1
-    nb = n // B
+    nb = -(-n // B)
     q, k, v = P.to_dev(inp)
     ws = crisp.alloc_workspace(n, hq, hkv)
     out = torch.empty_like(q)
@@ -89,6 +91,45 @@ def test_tiny_sequences(n):
     """N_b = 1, 2 (every block kept), 3 and 5 (ragged proxy tiles)."""
     sp = synth.custom_spec(n, 2, 1, [synth.VS, synth.DIFFUSE], seed_id=60 + n // 128)
     case(synth.generate(sp), tag=f"-n{n}")
+
+
+@pytest.mark.parametrize("n", [1, 77, 129, 300, 1000, 3000 + 57])
+def test_ragged_sequences(n):
+    """n not a multiple of B: N_b = ceil(n/B), a partial last block in the
+    proxy rows, the slash split, the PE means and the attention tiles."""
+    kinds = [synth.VS, synth.DIFFUSE, synth.VS, synth.VS]
+    sp = synth.custom_spec(n, 4, 2, kinds, seed_id=100 + n % 97)
+    r = case(synth.generate(sp), tag=f"-n{n}")
+    # the end-to-end call on the GPU's own lists equals the staged calls
+    q, k, v = r["q"], r["k"], r["v"]
+    out = torch.empty_like(q)
+    crisp.crisp_prefill(q, k, v, 1.0, crisp.alloc_workspace(n, 4, 2), out)
+    gs = r["gs"]
+    staged = P.gpu_attend(q, k, v, gs["row_ptr"], gs["col_idx"], crisp.alloc_workspace(n, 4, 2))
+    assert torch.equal(out.view(torch.int16), staged.view(torch.int16))
+
+
+def test_ragged_dense_matches_oracle():
+    n, hq, hkv = 2048 + 100, 4, 1
+    sp = synth.custom_spec(n, hq, hkv, [synth.VS, synth.DIFFUSE, synth.VS, synth.VS], seed_id=111)
+    inp = synth.generate(sp)
+    nb = -(-n // B)
+    q, k, v = P.to_dev(inp)
+    out = torch.empty_like(q)
+    crisp.crisp_attend_dense(q, k, v, crisp.alloc_workspace(n, hq, hkv), out)
+    rp, ci = O.full_causal_lists(hq, nb)
+    want = O.attend(inp.q, inp.k, inp.v, n, hq, hkv, 128, rp, ci, np.arange(hq * nb, dtype=np.int32))
+    got = torch.zeros(hq, nb * B, 128)
+    got[:, :n] = out.float().cpu()
+    P.check_outputs(got.numpy().reshape(hq * nb, B, 128), want, "ragged dense")
+
+
+def test_empty_sequence():
+    q = torch.empty(4, 0, 128, dtype=torch.bfloat16, device="cuda")
+    k = torch.empty(1, 0, 128, dtype=torch.bfloat16, device="cuda")
+    out = torch.empty_like(q)
+    crisp.crisp_prefill(q, k, k, 1.0, crisp.alloc_workspace(0, 4, 1), out)
+    torch.cuda.synchronize()
 
 
 @pytest.mark.parametrize("hq,hkv", [(2, 2), (7, 1), (8, 2)])
