@@ -187,6 +187,59 @@ int orc_route(const uint16_t *q, const uint16_t *k, int n, int hq, int hkv, int 
     return 0;
 }
 
+/*
+ * FlexPrefill's pattern search (Alg. 5), the routing CRISP replaces:
+ *   abar = Softmax(pool(Q^) pool(K)^T / sqrt(d)) over the N_b key blocks,
+ *          pool(Q^) the mean of the R = min(B, n) representative rows and
+ *          pool(K) the per-block key means (over the tokens each block holds);
+ *   ahat = sumpool(Softmax(Q^ K^T / sqrt(d))) = p_v (per-query mean, pooled);
+ *   D_JS = sqrt(KL(ahat||m) / 2 + KL(abar||m) / 2), m = (ahat + abar) / 2,
+ *          natural logarithms, 0 log 0 = 0.
+ * pv holds the head's p_v (from orc_route); returns D_JS in *djs.  The
+ * routing bit "VS iff D_JS >= tau" is taken in float by the caller.
+ */
+int orc_jsd(const uint16_t *q, const uint16_t *k, int n, int hq, int hkv, int d, int B, int h,
+            const double *pv, double *djs)
+{
+    if (n < 1 || B < 1 || hq % hkv || h < 0 || h >= hq) return 1;
+    const int nb = (n + B - 1) / B, g = h / (hq / hkv), R = n < B ? n : B;
+    const double scale = 1.0 / sqrt((double)d);
+    double *qbar = (double *)calloc((size_t)d, sizeof(double));
+    double *abar = (double *)malloc((size_t)nb * sizeof(double));
+    if (!qbar || !abar) { free(qbar); free(abar); return 2; }
+    const uint16_t *qh = q + (int64_t)h * n * d, *kg = k + (int64_t)g * n * d;
+    for (int i = 0; i < R; ++i)
+        for (int c = 0; c < d; ++c) qbar[c] += (double)bf16_to_f32(qh[((int64_t)n - R + i) * d + c]);
+    for (int c = 0; c < d; ++c) qbar[c] /= R;
+    double m = -INFINITY;
+#pragma omp parallel for schedule(static)
+    for (int b = 0; b < nb; ++b) {
+        const int len = (b == nb - 1) ? n - b * B : B;
+        double s = 0.0;
+        for (int c = 0; c < d; ++c) {
+            double kb = 0.0;
+            for (int t = 0; t < len; ++t) kb += (double)bf16_to_f32(kg[((int64_t)b * B + t) * d + c]);
+            s += qbar[c] * (kb / len);
+        }
+        abar[b] = scale * s;
+    }
+    for (int b = 0; b < nb; ++b) if (abar[b] > m) m = abar[b];
+    double l = 0.0;
+    for (int b = 0; b < nb; ++b) { abar[b] = exp(abar[b] - m); l += abar[b]; }
+    double kl_hat = 0.0, kl_bar = 0.0;
+    for (int b = 0; b < nb; ++b) {
+        abar[b] /= l;
+        const double mb = 0.5 * (pv[b] + abar[b]);
+        if (pv[b] > 0.0) kl_hat += pv[b] * log(pv[b] / mb);
+        if (abar[b] > 0.0) kl_bar += abar[b] * log(abar[b] / mb);
+    }
+    double js = 0.5 * kl_hat + 0.5 * kl_bar;
+    *djs = sqrt(js > 0.0 ? js : 0.0);
+    free(qbar);
+    free(abar);
+    return 0;
+}
+
 /* ---- ordering helpers: (value desc, index asc) on float-rounded values ---- */
 typedef struct { float v; int64_t i; } vi_t;
 
@@ -205,14 +258,35 @@ static int cmp_int(const void *a, const void *b)
 }
 
 /*
- * Sink-aware selection in one direction (Alg. 3, lines 7-12; Eq. 3 and 4):
- *   r = max(1 - p[0] - p[Nb-1], 0);  mu = r / (Nb - 2);  theta = alpha * mu
+ * Budget and top-k shared by both noise floors (Alg. 3, lines 10-12; Eq. 4):
  *   k = #{j : p[j] > theta}, counted over all Nb blocks
  *   k = clip(k, k_min, Nb);  S = top-k(p), ties to the lower block index.
- * All in float, in that order.  Writes the selected blocks in ascending
- * order to sel and returns their number; theta_out receives theta and
- * kth_out the k-th largest value (the decisive value when the clip binds).
- * Nb <= 2 (mu undefined): every block is selected.
+ * pf holds p rounded to float.  Writes S ascending to sel, returns |S|.
+ */
+static int floor_topk(const float *pf, int nb, float theta, int kmin, int32_t *sel,
+                      float *kth_out, int *clipped_out)
+{
+    vi_t *ord = (vi_t *)malloc((size_t)nb * sizeof(vi_t));
+    int count = 0;
+    for (int j = 0; j < nb; ++j) count += (pf[j] > theta);
+    int kk = count < kmin ? kmin : count;
+    if (kk > nb) kk = nb;
+    for (int j = 0; j < nb; ++j) { ord[j].v = pf[j]; ord[j].i = j; }
+    qsort(ord, nb, sizeof(vi_t), cmp_desc);
+    for (int t = 0; t < kk; ++t) sel[t] = (int32_t)ord[t].i;
+    qsort(sel, kk, sizeof(int32_t), cmp_int);
+    *kth_out = ord[kk - 1].v;
+    *clipped_out = (count < kk);
+    free(ord);
+    return kk;
+}
+
+/*
+ * Sink-aware selection in one direction (Alg. 3, lines 7-12; Eq. 3 and 4):
+ *   r = max(1 - p[0] - p[Nb-1], 0);  mu = r / (Nb - 2);  theta = alpha * mu
+ *   then floor_topk.  All in float, in that order.  theta_out receives
+ *   theta and kth_out the k-th largest value (the decisive value when the
+ *   clip binds).  Nb <= 2 (mu undefined): every block is selected.
  */
 int orc_vs_select(const double *p, int nb, float alpha, int kmin, int32_t *sel,
                   float *theta_out, float *kth_out, int *clipped_out)
@@ -225,26 +299,46 @@ int orc_vs_select(const double *p, int nb, float alpha, int kmin, int32_t *sel,
         return nb;
     }
     float *pf = (float *)malloc((size_t)nb * sizeof(float));
-    vi_t *ord = (vi_t *)malloc((size_t)nb * sizeof(vi_t));
     for (int j = 0; j < nb; ++j) pf[j] = (float)p[j];
     float r = 1.0f - pf[0];
     r = r - pf[nb - 1];
     if (r < 0.0f) r = 0.0f;
     float mu = r / (float)(nb - 2);
     float theta = alpha * mu;
-    int count = 0;
-    for (int j = 0; j < nb; ++j) count += (pf[j] > theta);
-    int kk = count < kmin ? kmin : count;
-    if (kk > nb) kk = nb;
-    for (int j = 0; j < nb; ++j) { ord[j].v = pf[j]; ord[j].i = j; }
-    qsort(ord, nb, sizeof(vi_t), cmp_desc);
-    for (int t = 0; t < kk; ++t) sel[t] = (int32_t)ord[t].i;
-    qsort(sel, kk, sizeof(int32_t), cmp_int);
     *theta_out = theta;
-    *kth_out = ord[kk - 1].v;
-    *clipped_out = (count < kk);
+    int kk = floor_topk(pf, nb, theta, kmin, sel, kth_out, clipped_out);
     free(pf);
-    free(ord);
+    return kk;
+}
+
+static int cmp_float(const void *a, const void *b)
+{
+    float x = *(const float *)a, y = *(const float *)b;
+    return (x > y) - (x < y);
+}
+
+/*
+ * The median noise floor of Appendix H ("Median instead of mean as the noise
+ * floor"): the floor is the median of the non-retained blocks 1 .. Nb-2
+ * instead of their mean r / (Nb - 2); for an even count the mean of the two
+ * middle values.  theta = alpha * median, then floor_topk.  In float.
+ */
+int orc_vs_select_median(const double *p, int nb, float alpha, int kmin, int32_t *sel,
+                         float *theta_out, float *kth_out, int *clipped_out)
+{
+    if (nb <= 2) return orc_vs_select(p, nb, alpha, kmin, sel, theta_out, kth_out, clipped_out);
+    const int m = nb - 2;
+    float *pf = (float *)malloc((size_t)nb * sizeof(float));
+    float *mid = (float *)malloc((size_t)m * sizeof(float));
+    for (int j = 0; j < nb; ++j) pf[j] = (float)p[j];
+    for (int j = 0; j < m; ++j) mid[j] = pf[j + 1];
+    qsort(mid, m, sizeof(float), cmp_float);
+    const float med = (m & 1) ? mid[m / 2] : (mid[m / 2 - 1] + mid[m / 2]) * 0.5f;
+    const float theta = alpha * med;
+    *theta_out = theta;
+    int kk = floor_topk(pf, nb, theta, kmin, sel, kth_out, clipped_out);
+    free(pf);
+    free(mid);
     return kk;
 }
 

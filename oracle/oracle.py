@@ -21,6 +21,9 @@ LIB = os.path.join(HERE, "liboracle.so")
 
 # Paper defaults (Section 5, "Setup"; Section 3.2 for the anchor windows).
 TAU_PROXY = 0.2
+# FlexPrefill's JSD threshold (Alg. 5) is not given by the CRISP paper; 0.1
+# is this implementation's default for the baseline router.
+TAU_JSD = 0.1
 GAMMA = 0.95
 K_MIN_TOKENS = 1024
 W_SINK = 128
@@ -52,6 +55,8 @@ def lib():
         L.orc_block_scores.argtypes = [P, i, i, i, i, P, P, P]
         L.orc_route.argtypes = [P, P, i, i, i, i, i, f, i, i, P, P, P, P]
         L.orc_vs_select.argtypes = [P, i, f, i, P, P, P, P]
+        L.orc_vs_select_median.argtypes = [P, i, f, i, P, P, P, P]
+        L.orc_jsd.argtypes = [P, P, i, i, i, i, i, i, P, P]
         L.orc_gamma_select.argtypes = [P, i, f, i, P]
         L.orc_pe_map.argtypes = [P, P, i, i, i, i, i, i, P]
         L.orc_pe_select.argtypes = [P, i, f, P, P, P]
@@ -132,6 +137,24 @@ def route(q, k, n, hq, hkv, d=128, B=128, tau=TAU_PROXY, w_sink=W_SINK, w_local=
     return Route(pv, ps, cs, pat)
 
 
+def jsd(q, k, n, hq, hkv, d, h, p_v, B=128) -> float:
+    """FlexPrefill's D_JS of one head (Alg. 5) against its p_v."""
+    pv = np.ascontiguousarray(p_v, dtype=np.float64)
+    out = np.zeros(1)
+    rc = lib().orc_jsd(_p(_u16(q)), _p(_u16(k)), n, hq, hkv, d, B, h, _p(pv), _p(out))
+    assert rc == 0, rc
+    return float(out[0])
+
+
+def route_jsd(q, k, n, hq, hkv, d=128, B=128, tau_jsd=TAU_JSD, routed: Route | None = None) -> Route:
+    """Alg. 5 for every head: p_v / p_s as route(); c_struct holds D_JS and
+    the pattern is "VS iff D_JS >= tau_jsd" (in float)."""
+    r = routed if routed is not None else route(q, k, n, hq, hkv, d, B)
+    djs = np.array([jsd(q, k, n, hq, hkv, d, h, r.p_v[h], B) for h in range(hq)])
+    pat = (djs.astype(np.float32) >= np.float32(tau_jsd)).astype(np.uint8)
+    return Route(r.p_v, r.p_s, djs, pat)
+
+
 @dataclass
 class VSSel:
     sel: np.ndarray        # ascending int32 block indices
@@ -140,15 +163,18 @@ class VSSel:
     clipped: bool          # k_min clip was active
 
 
-def vs_select(p: np.ndarray, alpha: float, kmin_blocks: int = K_MIN_TOKENS // 128) -> VSSel:
-    """Sink-aware noise-floor selection in one direction (Alg. 3, Eq. 3-4)."""
+def vs_select(p: np.ndarray, alpha: float, kmin_blocks: int = K_MIN_TOKENS // 128,
+              floor: str = "mean") -> VSSel:
+    """Noise-floor selection in one direction: the sink-aware mean floor of
+    Alg. 3 / Eq. 3-4, or the median floor of Appendix H (floor="median")."""
     p = np.ascontiguousarray(p, dtype=np.float64)
     nb = p.shape[0]
     sel = np.zeros(nb, dtype=np.int32)
     th = np.zeros(1, dtype=np.float32)
     kth = np.zeros(1, dtype=np.float32)
     cl = np.zeros(1, dtype=np.int32)
-    cnt = lib().orc_vs_select(_p(p), nb, float(alpha), kmin_blocks, _p(sel), _p(th), _p(kth), _p(cl))
+    fn = {"mean": lib().orc_vs_select, "median": lib().orc_vs_select_median}[floor]
+    cnt = fn(_p(p), nb, float(alpha), kmin_blocks, _p(sel), _p(th), _p(kth), _p(cl))
     return VSSel(sel[:cnt].copy(), float(th[0]), float(kth[0]), bool(cl[0]))
 
 
@@ -263,11 +289,14 @@ def full_causal_lists(hq: int, nb: int):
 
 
 def plan(q, k, n, hq, hkv, d=128, B=128, alpha=1.0, tau=TAU_PROXY, gamma=GAMMA,
-         kmin_tokens=K_MIN_TOKENS, heads=None, routed: Route | None = None) -> Plan:
+         kmin_tokens=K_MIN_TOKENS, heads=None, routed: Route | None = None,
+         vs_rule: str = "mean", gamma_vs: float = GAMMA) -> Plan:
     """Alg. 1 up to the index set: routing, per-head selection and expansion.
 
+    vs_rule picks the VS budget: "mean" (Alg. 3), "median" (Appendix H) or
+    "gamma" (FlexPrefill's cumulative rule, Alg. 6, with the k_min clip).
     Head h's lists start at offset h*Nb*(Nb+1)/2 of col_idx (its worst case).
-    `routed` reuses an earlier route() result for the same inputs."""
+    `routed` reuses an earlier route() / route_jsd() result for the same inputs."""
     nb = nblocks(n, B)
     r = routed if routed is not None else route(q, k, n, hq, hkv, d, B, tau, B, B)
     per = nb * (nb + 1) // 2
@@ -277,8 +306,12 @@ def plan(q, k, n, hq, hkv, d=128, B=128, alpha=1.0, tau=TAU_PROXY, gamma=GAMMA,
     kmin = kmin_tokens // B
     for h in (range(hq) if heads is None else heads):
         if r.pattern[h]:
-            sv = vs_select(r.p_v[h], alpha, kmin)
-            sls = vs_select(r.p_s[h], alpha, kmin)
+            if vs_rule == "gamma":
+                sv = VSSel(gamma_select(r.p_v[h], gamma_vs, kmin), 0.0, 0.0, False)
+                sls = VSSel(gamma_select(r.p_s[h], gamma_vs, kmin), 0.0, 0.0, False)
+            else:
+                sv = vs_select(r.p_v[h], alpha, kmin, vs_rule)
+                sls = vs_select(r.p_s[h], alpha, kmin, vs_rule)
             vs_v[h], vs_s[h] = sv, sls
             rp, _, _ = expand(nb, True, sv.sel, sls.sel, base=h * per, col_idx=col_idx)
         else:

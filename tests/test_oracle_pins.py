@@ -570,3 +570,112 @@ def test_ragged_plan_small_nb_is_dense():
         for h in range(2):
             lens = np.diff(p.row_ptr[h])
             assert lens.tolist() == np.diff(rp[h]).tolist()
+
+
+# ------------------------------------------- FlexPrefill baseline (App. A)
+def brute_abar(q, k, h, G, B):
+    """Alg. 5 line 3 by numpy: softmax over blocks of the pooled query and
+    the per-block key means."""
+    n, d = q.shape[1], q.shape[2]
+    R = min(B, n)
+    nb = -(-n // B)
+    qbar = q[h, n - R:].double().numpy().mean(0)
+    kd = k[h // G].double().numpy()
+    kbar = np.stack([kd[b * B:(b + 1) * B].mean(0) for b in range(nb)])
+    z = kbar @ qbar / math.sqrt(d)
+    e = np.exp(z - z.max())
+    return e / e.sum()
+
+
+@pytest.mark.parametrize("n,B", [(1024, 128), (1000, 128), (640, 64)])
+def test_jsd_matches_scipy(n, B):
+    from scipy.spatial.distance import jensenshannon
+    d, hq, hkv = 32, 4, 2
+    q, k, _ = rand_qkv(n, hq, hkv, d, seed=900 + n, scale=2.0)
+    r = O.route(q, k, n, hq, hkv, d, B, 0.2, B, B)
+    rj = O.route_jsd(q, k, n, hq, hkv, d, B, 0.1, routed=r)
+    for h in range(hq):
+        pv_bf, _ = brute_scores_any(brute_proxy_any(q, k, h, hq // hkv, B), B)
+        want = jensenshannon(pv_bf, brute_abar(q, k, h, hq // hkv, B))   # natural log
+        assert rj.c_struct[h] == pytest.approx(want, rel=1e-9, abs=1e-12)
+        assert rj.pattern[h] == (np.float32(want) >= np.float32(0.1))
+    np.testing.assert_array_equal(rj.p_v, r.p_v)
+
+
+def test_jsd_closed_forms():
+    """Identical distributions give 0; disjoint supports give sqrt(ln 2)."""
+    n, d, B = 512, 16, 128
+    # Q = 0: A^ rows uniform over their visible keys; abar uniform over blocks
+    q = torch.zeros(1, n, d, dtype=torch.bfloat16)
+    _, k, _ = rand_qkv(n, 1, 1, d, seed=12)
+    r = O.route(q, k, n, 1, 1, d, B)
+    uni = np.full(n // B, 1.0 / (n // B))
+    from scipy.spatial.distance import jensenshannon
+    assert O.jsd(q, k, n, 1, 1, d, 0, r.p_v[0], B) == pytest.approx(jensenshannon(r.p_v[0], uni), rel=1e-12)
+    # p_v all on block 0 while abar is (numerically) all on the last block
+    pv = np.zeros(n // B)
+    pv[0] = 1.0
+    q2 = torch.zeros(1, n, d)
+    q2[0, :, 0] = 30.0
+    k2 = torch.zeros(1, n, d)
+    k2[0, n - B:, 0] = 30.0
+    got = O.jsd(q2.to(torch.bfloat16), k2.to(torch.bfloat16), n, 1, 1, d, 0, pv, B)
+    assert got == pytest.approx(math.sqrt(math.log(2.0)), rel=1e-9)
+
+
+def brute_vs_median(p, alpha, kmin):
+    pf = p.astype(np.float32)
+    nb = len(pf)
+    mid = np.sort(pf[1:nb - 1])
+    m = len(mid)
+    med = mid[m // 2] if m % 2 else np.float32((mid[m // 2 - 1] + mid[m // 2]) * np.float32(0.5))
+    assert med == np.float32(np.median(pf[1:nb - 1]))      # numpy's median, in float
+    th = np.float32(alpha) * np.float32(med)
+    cnt = int((pf > th).sum())
+    kk = min(max(cnt, kmin), nb)
+    order = sorted(range(nb), key=lambda j: (-pf[j], j))
+    return sorted(order[:kk]), th
+
+
+@pytest.mark.parametrize("seed", range(10))
+def test_vs_select_median_floor(seed):
+    rng = np.random.default_rng(1000 + seed)
+    nb = int(rng.integers(4, 40))
+    p = rng.random(nb) ** 3
+    p[0] += 2.0
+    p /= p.sum()
+    for alpha in (0.5, 1.0, 2.0):
+        for kmin in (1, 3, 8):
+            s = O.vs_select(p, alpha, kmin, floor="median")
+            want, th = brute_vs_median(p, alpha, kmin)
+            assert s.sel.tolist() == want
+            assert s.theta == th
+
+
+def test_median_floor_resists_one_dominant_block():
+    """Appendix H's clumpy-noise case: one large interior block lifts the
+    mean floor above weaker signal blocks but not the median floor."""
+    nb = 40
+    p = np.full(nb, 0.005)
+    p[0], p[-1] = 0.3, 0.1
+    p[5] = 0.8                     # dominant interior block
+    p[10:13] = 0.02                # weaker genuine signal
+    p /= p.sum()
+    mean_sel = set(O.vs_select(p, 1.0, 1).sel.tolist())
+    med_sel = set(O.vs_select(p, 1.0, 1, floor="median").sel.tolist())
+    assert mean_sel == {0, 5, 39}              # mu = 0.72 / 38 > 0.014
+    assert med_sel == {0, 5, 10, 11, 12, 39}   # median = 0.0035
+
+
+def test_gamma_rule_with_kmin_clip():
+    rng = np.random.default_rng(5)
+    p = rng.random(30) ** 4
+    p[0] = 200.0                   # the sink alone reaches gamma: the cliff's collapse
+    p /= p.sum()
+    pure = O.gamma_select(p, 0.95)
+    assert pure.tolist() == [0]
+    clipped = O.gamma_select(p, 0.95, kmin_blocks=8)
+    assert len(pure) < 8 and len(clipped) == 8
+    order = sorted(range(30), key=lambda j: (-np.float32(p[j]), j))
+    assert clipped.tolist() == sorted(order[:8])
+    assert set(pure.tolist()) <= set(clipped.tolist())
