@@ -5,7 +5,9 @@ on the headline workload: one attention layer of Llama-3.1-8B head shape
 (32 query / 8 KV heads, head_dim 128) at 131072 tokens, alpha = 1.0, with
 24 vertical-slash and 8 diffuse heads (seeded synthetic inputs resident in
 HBM before timing starts).  Dense causal attention with the same kernel is
-timed on the same inputs for the speedup.  Prints one JSON line.
+timed on the same inputs for the speedup, and so is the FlexPrefill baseline
+(JSD routing + cumulative gamma VS selection) that the paper compares with.
+Prints one JSON line.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu]
 """
@@ -90,6 +92,8 @@ def main():
     ap.add_argument("--alpha", type=float, default=1.0)
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--no-dense", action="store_true", help="skip the dense timing")
+    ap.add_argument("--no-flexprefill", action="store_true",
+                    help="skip the FlexPrefill-baseline timing")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="end with a 1 GiB device-to-device copy (reference for counter runs)")
     args = ap.parse_args()
@@ -165,6 +169,48 @@ def main():
     log(f"prefill {ms_step:.3f} ms/step (wall {wall / args.steps * 1e3:.3f}); stages "
         f"route {route_ms:.3f} select {select_ms:.3f} v-relayout {vt_ms:.3f} attend {attend_ms:.3f}")
 
+    # ---- FlexPrefill baseline (JSD routing + cumulative gamma VS rule, the
+    # paper's comparison system) on the same inputs and kernels ----
+    fp = None
+    if not args.no_flexprefill:
+        fopts = crisp.flexprefill_opts()
+        out_f = torch.empty_like(q)
+        ws_f = crisp.alloc_workspace(n, hq, hkv)
+        pat_f = torch.zeros(hq, dtype=torch.uint8, device="cuda")
+        crisp.crisp_route(q, k, ws_f, pat_f, cs, pv, ps, opts=fopts)
+        rp_f = torch.zeros(hq, nb + 1, dtype=torch.int32, device="cuda")
+        ci_f = torch.zeros(cap, dtype=torch.int32, device="cuda")
+        crisp.crisp_select(q, k, pat_f, pv, ps, args.alpha, ws_f, sel_v, sel_s, counts, rp_f, ci_f,
+                           opts=fopts)
+        torch.cuda.synchronize()
+        rpf = rp_f.cpu().numpy()
+        fp_pairs = int((rpf[:, nb] - rpf[:, 0]).sum())
+        fp_vs = int(pat_f.sum().item())
+        del ci_f
+        for _ in range(min(args.warmup, 2)):
+            crisp.crisp_prefill(q, k, v, args.alpha, ws_f, out_f, opts=fopts)
+        fsteps = max(3, args.steps // 2)
+        f_ev = [events(5) for _ in range(fsteps)]
+        f0, f1 = events(2)
+        torch.cuda.synchronize()
+        f0.record(stream)
+        for s in range(fsteps):
+            crisp.crisp_set_stage_events(f_ev[s])
+            crisp.crisp_prefill(q, k, v, args.alpha, ws_f, out_f, opts=fopts)
+        crisp.crisp_set_stage_events(None)
+        f1.record(stream)
+        torch.cuda.synchronize()
+        fp_ms = f0.elapsed_time(f1) / fsteps
+        fst = np.array([[e[i].elapsed_time(e[i + 1]) for i in range(4)] for e in f_ev]).mean(axis=0)
+        fp = {"ms": round(fp_ms, 3), "computed_pairs": fp_pairs, "vs_heads": fp_vs,
+              "stages_ms": {"route": round(float(fst[0]), 3), "select": round(float(fst[1]), 3),
+                            "attend": round(float(fst[2] + fst[3]), 3)},
+              "crisp_speedup": round(fp_ms / ms_step, 3),
+              "rule": "JSD routing (tau 0.1) + cumulative gamma = 0.95 VS rule with k_min 8 blocks; "
+                      "PE path as CRISP"}
+        log(f"flexprefill {fp_ms:.3f} ms/step, {fp_pairs} pairs, {fp_vs} VS heads")
+        del out_f, ws_f
+
     # ---- dense baseline: same kernel, every causal block ----
     dense_ms = dense_attend_ms = None
     if not args.no_dense:
@@ -217,6 +263,7 @@ def main():
         "density": round(pairs / dense_pairs, 4),
         "vs_heads": int(pattern_h.sum()), "pe_heads": int(hq - pattern_h.sum()),
         "roofline": roofline,
+        "flexprefill_baseline": fp,
     }
     if args.calibrate_copy:
         src = torch.ones(1 << 29, dtype=torch.int16, device="cuda")

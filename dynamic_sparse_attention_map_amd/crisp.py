@@ -31,12 +31,27 @@ class CrispError(RuntimeError):
 
 class crisp_opts(C.Structure):
     _fields_ = [("tau_proxy", C.c_float), ("gamma", C.c_float), ("k_min_tokens", C.c_int),
-                ("w_sink", C.c_int), ("w_local", C.c_int)]
+                ("w_sink", C.c_int), ("w_local", C.c_int), ("router", C.c_int),
+                ("tau_jsd", C.c_float), ("vs_rule", C.c_int), ("gamma_vs", C.c_float)]
 
 
-def default_opts() -> crisp_opts:
-    """The paper's defaults (Section 5, "Setup"; Section 3.2)."""
-    return crisp_opts(0.2, 0.95, 1024, 128, 128)
+ROUTER_CSTRUCT, ROUTER_JSD = 0, 1
+VS_NOISE_MEAN, VS_NOISE_MEDIAN, VS_GAMMA = 0, 1, 2
+
+
+def default_opts(**overrides) -> crisp_opts:
+    """The library's defaults (crisp_default_opts), with fields overridden."""
+    o = crisp_opts()
+    lib().crisp_default_opts(C.byref(o))
+    for k, v in overrides.items():
+        setattr(o, k, v)
+    return o
+
+
+def flexprefill_opts(**overrides) -> crisp_opts:
+    """The FlexPrefill baseline of Appendix A: JSD routing (Alg. 5) and the
+    cumulative gamma rule for VS heads (Alg. 6), k_min as configured."""
+    return default_opts(router=ROUTER_JSD, vs_rule=VS_GAMMA, **overrides)
 
 
 _lib = None
@@ -59,6 +74,8 @@ def lib():
         L.crisp_attend_dense.argtypes = [P, P, P, i, i, i, i, i, P, sz, P, P]
         L.crisp_prefill.argtypes = [P, P, P, i, i, i, i, i, f, P, P, sz, P, P]
         L.crisp_set_stage_events.argtypes = [P, i]
+        L.crisp_default_opts.argtypes = [P]
+        L.crisp_default_opts.restype = None
         for name in ("crisp_workspace_size", "crisp_route", "crisp_select", "crisp_attend",
                      "crisp_attend_dense", "crisp_prefill", "crisp_set_stage_events"):
             getattr(L, name).restype = i

@@ -25,7 +25,7 @@ struct Shape {
 // the select scratch and the transposed V (stages run in that order on one
 // stream); region P after it holds crisp_prefill's intermediates.
 struct Layout {
-    size_t part_m, part_lo, part_up;                       // route (in S)
+    size_t part_m, part_lo, part_up, jsd_kbar, jsd_qbar;   // route (in S)
     size_t qbar, kbar, abar, hist_mass, hist_count, state, bitmap;   // select (in S)
     size_t vt, queue;                                      // attend (in S)
     size_t route_end, select_end, attend_end;              // bytes of S each stage needs
@@ -49,6 +49,8 @@ Layout make_layout(const Shape& s)
     L.part_m = take(part);
     L.part_lo = take(part);
     L.part_up = take(part);
+    L.jsd_kbar = take(hkv * nb * kD * sizeof(float));      // JSD router only
+    L.jsd_qbar = take(hq * kD * sizeof(float));
     L.route_end = o;
     o = 0;
     L.qbar = take(hq * nb * kD * sizeof(float));
@@ -104,21 +106,30 @@ bool bad_ptr(const void* p, size_t align = 16)
 }
 
 struct Opts {
-    float tau, gamma;
-    int kmin_blocks;
+    float tau, gamma, tau_jsd, gamma_vs;
+    int kmin_blocks, router, vs_rule;
 };
+
+constexpr crisp_opts kDefaults = {0.2f, 0.95f, 1024, kB, kB, CRISP_ROUTER_CSTRUCT, 0.1f,
+                                  CRISP_VS_NOISE_MEAN, 0.95f};
 
 int check_opts(const crisp_opts* o, Opts* out)
 {
-    crisp_opts d = {0.2f, 0.95f, 1024, kB, kB};
-    if (o) d = *o;
-    if (!std::isfinite(d.tau_proxy)) return CRISP_ERR_INVALID_ARG;
+    const crisp_opts d = o ? *o : kDefaults;
+    if (!std::isfinite(d.tau_proxy) || !std::isfinite(d.tau_jsd)) return CRISP_ERR_INVALID_ARG;
     if (!(d.gamma > 0.0f && d.gamma <= 1.0f)) return CRISP_ERR_INVALID_ARG;
+    if (!(d.gamma_vs > 0.0f && d.gamma_vs <= 1.0f)) return CRISP_ERR_INVALID_ARG;
     if (d.k_min_tokens < 0 || d.k_min_tokens % kB != 0) return CRISP_ERR_INVALID_ARG;
+    if (d.router != CRISP_ROUTER_CSTRUCT && d.router != CRISP_ROUTER_JSD) return CRISP_ERR_INVALID_ARG;
+    if (d.vs_rule < CRISP_VS_NOISE_MEAN || d.vs_rule > CRISP_VS_GAMMA) return CRISP_ERR_INVALID_ARG;
     if (d.w_sink != kB || d.w_local != kB) return CRISP_ERR_UNSUPPORTED;
     out->tau = d.tau_proxy;
     out->gamma = d.gamma;
+    out->tau_jsd = d.tau_jsd;
+    out->gamma_vs = d.gamma_vs;
     out->kmin_blocks = d.k_min_tokens / kB;
+    out->router = d.router;
+    out->vs_rule = d.vs_rule;
     return CRISP_OK;
 }
 
@@ -142,10 +153,16 @@ int do_route(const Shape& s, const Opts& op, const void* q, const void* k, void*
              const Layout& L, uint8_t* pattern, float* c_struct, float* p_v, float* p_s,
              hipStream_t stream)
 {
+    RouteArgs ra;
+    ra.router = op.router;
+    ra.tau = op.router == CRISP_ROUTER_JSD ? op.tau_jsd : op.tau;
+    ra.part_m = at<float>(ws, L.part_m);
+    ra.part_lo = at<float>(ws, L.part_lo);
+    ra.part_up = at<float>(ws, L.part_up);
+    ra.jsd_kbar = at<float>(ws, L.jsd_kbar);
+    ra.jsd_qbar = at<float>(ws, L.jsd_qbar);
     return hip_status(launch_route(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
-                                   s.n, s.hq, s.hkv, op.tau, at<float>(ws, L.part_m),
-                                   at<float>(ws, L.part_lo), at<float>(ws, L.part_up), p_v, p_s,
-                                   c_struct, pattern, stream));
+                                   s.n, s.hq, s.hkv, ra, p_v, p_s, c_struct, pattern, stream));
 }
 
 int do_select(const Shape& s, const Opts& op, float alpha, const void* q, const void* k,
@@ -161,9 +178,14 @@ int do_select(const Shape& s, const Opts& op, float alpha, const void* q, const 
     sc.hist_count = at<uint32_t>(ws, L.hist_count);
     sc.state = at<PeState>(ws, L.state);
     sc.bitmap = at<uint8_t>(ws, L.bitmap);
+    VsRule vr;
+    vr.rule = op.vs_rule;
+    vr.alpha = alpha;
+    vr.gamma_vs = op.gamma_vs;
+    vr.kmin_blocks = op.kmin_blocks;
     return hip_status(launch_select(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
-                                    pattern, p_v, p_s, s.n, s.hq, s.hkv, alpha, op.kmin_blocks,
-                                    op.gamma, sc, sel_v, sel_s, counts, row_ptr, col_idx, stream));
+                                    pattern, p_v, p_s, s.n, s.hq, s.hkv, vr, op.gamma, sc, sel_v,
+                                    sel_s, counts, row_ptr, col_idx, stream));
 }
 
 int do_attend(const Shape& s, const void* q, const void* k, const void* v, const int32_t* row_ptr,
@@ -184,6 +206,11 @@ int do_attend(const Shape& s, const void* q, const void* k, const void* v, const
 }  // namespace
 
 extern "C" {
+
+void crisp_default_opts(crisp_opts* opts)
+{
+    if (opts) *opts = kDefaults;
+}
 
 const char* crisp_status_string(int code)
 {

@@ -28,9 +28,26 @@ struct PeState {
 // Fixed point used for masses: value * 2^62 truncated (values are <= 1).
 constexpr double kFix = 4611686018427387904.0;
 
-hipError_t launch_route(const uint16_t* q, const uint16_t* k, int n, int hq, int hkv, float tau,
-                        float* part_m, float* part_lo, float* part_up, float* p_v, float* p_s,
-                        float* c_struct, uint8_t* pattern, hipStream_t stream);
+struct RouteArgs {
+    int router;                     // 0: C_struct >= tau (Alg. 2); 1: D_JS >= tau (Alg. 5)
+    float tau;
+    float* part_m;                  // [hq][Nb][128] per (tile, row) partials
+    float* part_lo;
+    float* part_up;
+    float* jsd_kbar;                // [hkv][Nb][128] block key means (router 1)
+    float* jsd_qbar;                // [hq][128] mean representative query (router 1)
+};
+
+hipError_t launch_route(const uint16_t* q, const uint16_t* k, int n, int hq, int hkv,
+                        const RouteArgs& a, float* p_v, float* p_s, float* c_struct,
+                        uint8_t* pattern, hipStream_t stream);
+
+struct VsRule {
+    int rule;                       // 0: mean floor, 1: median floor, 2: cumulative gamma
+    float alpha;                    // floor multiplier (rules 0, 1)
+    float gamma_vs;                 // coverage target (rule 2)
+    int kmin_blocks;                // every rule clips to at least this many blocks
+};
 
 struct SelectScratch {
     float* qbar;                    // [hq][Nb][128]
@@ -43,8 +60,8 @@ struct SelectScratch {
 };
 
 hipError_t launch_select(const uint16_t* q, const uint16_t* k, const uint8_t* pattern,
-                         const float* p_v, const float* p_s, int n, int hq, int hkv, float alpha,
-                         int kmin_blocks, float gamma, const SelectScratch& s, int32_t* sel_v,
+                         const float* p_v, const float* p_s, int n, int hq, int hkv,
+                         const VsRule& vs, float gamma, const SelectScratch& s, int32_t* sel_v,
                          int32_t* sel_s, int32_t* sel_counts, int32_t* row_ptr, int32_t* col_idx,
                          hipStream_t stream);
 

@@ -14,7 +14,10 @@
 // e_i = N_b - 1 - floor(q_i / B) (0 or 1; always 0 when B divides n).  So
 // lower + upper pools the tile's column mass (vertical score) and lower /
 // upper split it between two slash blocks.  mass_reduce_kernel rescales the
-// partials with the global row maxima and normalisers.
+// partials with the global row maxima and normalisers.  Under the JSD router
+// (FlexPrefill's Alg. 5, kept as the baseline) two more kernels pool the
+// keys and the representative queries and compare the pooled estimate with
+// p_v.
 #include "crisp_common.h"
 #include "crisp_kernels.h"
 
@@ -28,6 +31,9 @@ constexpr int kKRow = kD + 8;   // LDS row pitch of a K tile (bf16): 272 bytes
 // grid: (ceil(Nb / tiles_per_wg), n_kv_heads * ceil(G / 4)); block: 4
 // wavefronts sharing one staged K tile.  Wave w handles query head
 // kv*G + 4*sub + w (idle when that is >= G; it still helps stage K).
+// Aligned (B divides n): row i sits at column i of the last tile, so the
+// split column and the causal cut are compile-time per (chunk, key group).
+template <bool Aligned>
 __global__ void __launch_bounds__(256)
 proxy_map_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, int n, int nb,
                  int G, int tiles_per_wg, float scale_log2,
@@ -69,12 +75,20 @@ proxy_map_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
         // stage K tile t: 128 rows x 256 bytes as 16-byte chunks; rows past
         // the end of the sequence are zero (and masked below)
         __syncthreads();
-        for (int e = threadIdx.x; e < kTileKeys * (kD / 8); e += 256) {
-            const int row = e >> 4, ch = e & 15;
-            const size_t key = (size_t)t * kTileKeys + row;
-            u32x4 val = {0u, 0u, 0u, 0u};
-            if (key < (size_t)n) val = *reinterpret_cast<const u32x4*>(kg + key * kD + 8 * ch);
-            *reinterpret_cast<u32x4*>(&ks[row * kKRow + 8 * ch]) = val;
+        if ((t + 1) * kTileKeys <= n) {
+            for (int e = threadIdx.x; e < kTileKeys * (kD / 8); e += 256) {
+                const int row = e >> 4, ch = e & 15;
+                *reinterpret_cast<u32x4*>(&ks[row * kKRow + 8 * ch]) =
+                    *reinterpret_cast<const u32x4*>(kg + ((size_t)t * kTileKeys + row) * kD + 8 * ch);
+            }
+        } else {
+            for (int e = threadIdx.x; e < kTileKeys * (kD / 8); e += 256) {
+                const int row = e >> 4, ch = e & 15;
+                const size_t key = (size_t)t * kTileKeys + row;
+                u32x4 val = {0u, 0u, 0u, 0u};
+                if (key < (size_t)n) val = *reinterpret_cast<const u32x4*>(kg + key * kD + 8 * ch);
+                *reinterpret_cast<u32x4*>(&ks[row * kKRow + 8 * ch]) = val;
+            }
         }
         __syncthreads();
         if (!active) continue;
@@ -95,27 +109,28 @@ proxy_map_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
             // this lane: query row i at position qi, 64 of the tile's 128 keys
             const int i = 32 * c + l32;
             const int qi = q0 + i;
-            const int bi = qi & (kB - 1);
-            const int rel = qi - t * kTileKeys;     // last visible column
+            const int bi = Aligned ? i : (qi & (kB - 1));
+            const int rel = Aligned ? i : qi - t * kTileKeys;     // last visible column
+            const bool cut = Aligned ? (t == nb - 1) : maybe_future;
             float m = -INFINITY;
             for (int a = 0; a < 4; ++a)
                 for (int r = 0; r < 16; ++r) {
                     const int col = 32 * a + 8 * (r >> 2) + 4 * hi + (r & 3);
                     float x = acc[a][r] * scale_log2;
-                    if (maybe_future && col > rel) x = -INFINITY;   // causal
+                    if (cut && col > rel) x = -INFINITY;   // causal
                     acc[a][r] = x;
                     m = fmaxf(m, x);
                 }
             m = fmaxf(m, swap_half(m));
+            // a tile wholly in the row's future keeps m = -inf and sums 0
+            const float mref = (m == -INFINITY) ? 0.f : m;
             float lo = 0.f, up = 0.f;
-            if (m > -INFINITY) {                    // else: the whole tile is in the row's future
-                for (int a = 0; a < 4; ++a)
-                    for (int r = 0; r < 16; ++r) {
-                        const int col = 32 * a + 8 * (r >> 2) + 4 * hi + (r & 3);
-                        const float e = exp2f(acc[a][r] - m);
-                        if (col <= bi) lo += e; else up += e;
-                    }
-            }
+            for (int a = 0; a < 4; ++a)
+                for (int r = 0; r < 16; ++r) {
+                    const int col = 32 * a + 8 * (r >> 2) + 4 * hi + (r & 3);
+                    const float e = exp2f(acc[a][r] - mref);
+                    if (col <= bi) lo += e; else up += e;
+                }
             lo += swap_half(lo);
             up += swap_half(up);
             if (hi == 0 && i < R) {
@@ -134,14 +149,16 @@ proxy_map_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
 //   p_v[t] = (1/R) sum_i w_ti (LO + UP)[t][i]
 //   p_s[t] = (1/R) sum_i (w_(t-e_i)i LO[t-e_i][i] + w_(t-e_i-1)i UP[t-e_i-1][i])
 // Tiles wholly in a row's future carry M = -inf and are skipped.
-__global__ void __launch_bounds__(256)
+// 1024 threads: eight per row in phase 1, sixteen wavefronts over the tiles
+// in phase 2.
+__global__ void __launch_bounds__(1024)
 mass_reduce_kernel(const float* __restrict__ part_m, const float* __restrict__ part_lo,
-                   const float* __restrict__ part_up, int n, int nb, float tau,
+                   const float* __restrict__ part_up, int n, int nb, float tau, int route_here,
                    float* __restrict__ p_v, float* __restrict__ p_s,
                    float* __restrict__ c_struct, uint8_t* __restrict__ pattern)
 {
-    __shared__ float row_m[2][kB];
-    __shared__ double row_l[2][kB];
+    __shared__ float row_m[8][kB];
+    __shared__ double row_l[8][kB];
     __shared__ float row_inv[kB];
     __shared__ float row_mx[kB];
     // lower / upper slash sums of each tile, for rows with e_i = 0 and 1
@@ -154,13 +171,13 @@ mass_reduce_kernel(const float* __restrict__ part_m, const float* __restrict__ p
     const size_t base = (size_t)h * nb * kB;
     const int R = min(kB, n), q0 = n - R;
 
-    // phase 1: per-row online max / normaliser, two threads per row
+    // phase 1: per-row online max / normaliser, eight threads per row
     {
         const int i = tid & (kB - 1), part = tid >> 7;
         float m = -INFINITY;
         double l = 0.0;
         if (i < R) {
-            for (int t = part; t < nb; t += 2) {
+            for (int t = part; t < nb; t += 8) {
                 const size_t o = base + (size_t)t * kB + i;
                 const float mt = part_m[o];
                 if (mt == -INFINITY) continue;
@@ -178,11 +195,11 @@ mass_reduce_kernel(const float* __restrict__ part_m, const float* __restrict__ p
     }
     __syncthreads();
     if (tid < R) {
-        const float m0 = row_m[0][tid], m1 = row_m[1][tid];
-        const float m = fmaxf(m0, m1);
+        float m = -INFINITY;
+        for (int x = 0; x < 8; ++x) m = fmaxf(m, row_m[x][tid]);
         double l = 0.0;
-        if (m0 > -INFINITY) l += row_l[0][tid] * (double)exp2f(m0 - m);
-        if (m1 > -INFINITY) l += row_l[1][tid] * (double)exp2f(m1 - m);
+        for (int x = 0; x < 8; ++x)
+            if (row_m[x][tid] > -INFINITY) l += row_l[x][tid] * (double)exp2f(row_m[x][tid] - m);
         row_mx[tid] = m;
         row_inv[tid] = (float)(1.0 / l);
     }
@@ -190,7 +207,7 @@ mass_reduce_kernel(const float* __restrict__ part_m, const float* __restrict__ p
 
     // phase 2: one wavefront per tile, lanes over the R rows
     const int lane = tid & 63, w = tid >> 6;
-    for (int t = w; t < nb; t += 4) {
+    for (int t = w; t < nb; t += 16) {
         double sv = 0.0, slo0 = 0.0, sup0 = 0.0, slo1 = 0.0, sup1 = 0.0;
         for (int i = lane; i < R; i += 64) {
             const size_t o = base + (size_t)t * kB + i;
@@ -222,13 +239,13 @@ mass_reduce_kernel(const float* __restrict__ part_m, const float* __restrict__ p
     __syncthreads();
     // slash block t: lower parts of tile t (e = 0) and t-1 (e = 1), upper
     // parts of tile t-1 (e = 0) and t-2 (e = 1)
-    for (int t = tid; t < nb; t += 256) {
+    for (int t = tid; t < nb; t += 1024) {
         float ps = lo_sum[0][t];
         if (t >= 1) ps += up_sum[0][t - 1] + lo_sum[1][t - 1];
         if (t >= 2) ps += up_sum[1][t - 2];
         p_s[(size_t)h * nb + t] = ps;
     }
-    if (tid == 0) {
+    if (tid == 0 && route_here) {
         // Eq. 2 with w_sink = w_local = B: the first and the last key block
         const float cs = (nb > 1) ? pv_ends[0] + pv_ends[1] : pv_ends[0];
         c_struct[h] = cs;
@@ -236,12 +253,116 @@ mass_reduce_kernel(const float* __restrict__ part_m, const float* __restrict__ p
     }
 }
 
+// FlexPrefill's router (Alg. 5), the baseline CRISP replaces.
+// grid (Nb, hkv + hq), 256 threads: y < hkv: mean of key block x of KV head
+// y over the tokens it holds; y >= hkv (x == 0 only): mean of the R
+// representative query rows of head y - hkv.
+__global__ void __launch_bounds__(256)
+jsd_pool_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, int n, int nb,
+                int hkv, float* __restrict__ kbar, float* __restrict__ qbar)
+{
+    __shared__ float red[16][kD];
+    const int x = blockIdx.x, y = blockIdx.y, tid = threadIdx.x;
+    const uint16_t* src;
+    float* dst;
+    int len;
+    if (y < hkv) {
+        len = min(kB, n - x * kB);
+        src = k + ((size_t)y * n + (size_t)x * kB) * kD;
+        dst = kbar + ((size_t)y * nb + x) * kD;
+    } else {
+        if (x != 0) return;
+        len = min(kB, n);
+        src = q + ((size_t)(y - hkv) * n + (n - len)) * kD;
+        dst = qbar + (size_t)(y - hkv) * kD;
+    }
+    const int dc = tid & 15, tg = tid >> 4;
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    for (int t = tg * 8; t < min(tg * 8 + 8, len); ++t) {
+        const u32x4 raw = *reinterpret_cast<const u32x4*>(src + (size_t)t * kD + 8 * dc);
+        for (int e = 0; e < 4; ++e) {
+            acc[2 * e] += __uint_as_float(raw[e] << 16);
+            acc[2 * e + 1] += __uint_as_float(raw[e] & 0xffff0000u);
+        }
+    }
+    for (int e = 0; e < 8; ++e) red[tg][8 * dc + e] = acc[e];
+    __syncthreads();
+    if (tid < kD) {
+        float sum = 0.f;
+        for (int r = 0; r < 16; ++r) sum += red[r][tid];
+        dst[tid] = sum / (float)len;
+    }
+}
+
+// One work-group per query head:
+//   abar_j = softmax_j(qbar . kbar_j / sqrt(d)) over the N_b blocks,
+//   D_JS = sqrt(KL(p_v||m) / 2 + KL(abar||m) / 2), m = (p_v + abar) / 2,
+// natural logarithms, sums in double; VS iff D_JS >= tau (in float).
+__global__ void __launch_bounds__(256)
+jsd_route_kernel(const float* __restrict__ kbar, const float* __restrict__ qbar,
+                 const float* __restrict__ p_v, int nb, int G, float tau,
+                 float* __restrict__ c_struct, uint8_t* __restrict__ pattern)
+{
+    __shared__ float qs[kD];
+    __shared__ float z[kMaxBlocks];
+    __shared__ float red_f[4];
+    __shared__ double red_d[3][4];
+    const int h = blockIdx.x, g = h / G, tid = threadIdx.x;
+    const int lane = tid & 63, w = tid >> 6;
+    if (tid < kD) qs[tid] = qbar[(size_t)h * kD + tid];
+    __syncthreads();
+    const float scale = 1.0f / sqrtf((float)kD);
+    float mx = -INFINITY;
+    for (int j = tid; j < nb; j += 256) {
+        const float* kr = kbar + ((size_t)g * nb + j) * kD;
+        float dot = 0.f;
+        for (int c = 0; c < kD; ++c) dot = fmaf(qs[c], kr[c], dot);
+        z[j] = dot * scale;
+        mx = fmaxf(mx, z[j]);
+    }
+    mx = wave_max(mx);
+    if (lane == 0) red_f[w] = mx;
+    __syncthreads();
+    mx = fmaxf(fmaxf(red_f[0], red_f[1]), fmaxf(red_f[2], red_f[3]));
+    double l = 0.0;
+    for (int j = tid; j < nb; j += 256) {
+        const float e = expf(z[j] - mx);
+        z[j] = e;
+        l += (double)e;
+    }
+    l = wave_sum(l);
+    if (lane == 0) red_d[0][w] = l;
+    __syncthreads();
+    l = red_d[0][0] + red_d[0][1] + red_d[0][2] + red_d[0][3];
+    const double inv = 1.0 / l;
+    double kl_hat = 0.0, kl_bar = 0.0;
+    for (int j = tid; j < nb; j += 256) {
+        const double a = (double)p_v[(size_t)h * nb + j], b = (double)z[j] * inv;
+        const double m = 0.5 * (a + b);
+        if (a > 0.0) kl_hat += a * log(a / m);
+        if (b > 0.0) kl_bar += b * log(b / m);
+    }
+    kl_hat = wave_sum(kl_hat);
+    kl_bar = wave_sum(kl_bar);
+    if (lane == 0) {
+        red_d[1][w] = kl_hat;
+        red_d[2][w] = kl_bar;
+    }
+    __syncthreads();
+    if (tid == 0) {
+        const double js = 0.5 * (red_d[1][0] + red_d[1][1] + red_d[1][2] + red_d[1][3]) +
+                          0.5 * (red_d[2][0] + red_d[2][1] + red_d[2][2] + red_d[2][3]);
+        const float d = (float)sqrt(js > 0.0 ? js : 0.0);
+        c_struct[h] = d;
+        pattern[h] = (d >= tau) ? 1 : 0;
+    }
+}
+
 }  // namespace
 
 hipError_t launch_route(const uint16_t* q, const uint16_t* k, int n, int hq, int hkv,
-                        float tau, float* part_m, float* part_lo, float* part_up,
-                        float* p_v, float* p_s, float* c_struct, uint8_t* pattern,
-                        hipStream_t stream)
+                        const RouteArgs& a, float* p_v, float* p_s, float* c_struct,
+                        uint8_t* pattern, hipStream_t stream)
 {
     const int nb = (n + kB - 1) / kB;
     const int G = hq / hkv;
@@ -251,12 +372,23 @@ hipError_t launch_route(const uint16_t* q, const uint16_t* k, int n, int hq, int
     while (tiles_per_wg < 8 && (size_t)((nb + 2 * tiles_per_wg - 1) / (2 * tiles_per_wg)) * hkv >= 1024)
         tiles_per_wg *= 2;
     dim3 grid((nb + tiles_per_wg - 1) / tiles_per_wg, hkv * ((G + 3) / 4));
-    hipLaunchKernelGGL(proxy_map_kernel, grid, dim3(256), 0, stream, q, k, n, nb, G,
-                       tiles_per_wg, scale_log2, part_m, part_lo, part_up);
+    if (n % kB == 0)
+        hipLaunchKernelGGL(proxy_map_kernel<true>, grid, dim3(256), 0, stream, q, k, n, nb, G,
+                           tiles_per_wg, scale_log2, a.part_m, a.part_lo, a.part_up);
+    else
+        hipLaunchKernelGGL(proxy_map_kernel<false>, grid, dim3(256), 0, stream, q, k, n, nb, G,
+                           tiles_per_wg, scale_log2, a.part_m, a.part_lo, a.part_up);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(mass_reduce_kernel, dim3(hq), dim3(256), 0, stream, part_m, part_lo, part_up,
-                       n, nb, tau, p_v, p_s, c_struct, pattern);
+    const int route_here = a.router == 0;
+    hipLaunchKernelGGL(mass_reduce_kernel, dim3(hq), dim3(1024), 0, stream, a.part_m, a.part_lo,
+                       a.part_up, n, nb, a.tau, route_here, p_v, p_s, c_struct, pattern);
+    if ((e = hipGetLastError()) != hipSuccess || route_here) return e;
+    hipLaunchKernelGGL(jsd_pool_kernel, dim3(nb, hkv + hq), dim3(256), 0, stream, q, k, n, nb, hkv,
+                       a.jsd_kbar, a.jsd_qbar);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL(jsd_route_kernel, dim3(hq), dim3(256), 0, stream, a.jsd_kbar, a.jsd_qbar, p_v,
+                       nb, G, a.tau, c_struct, pattern);
     return hipGetLastError();
 }
 

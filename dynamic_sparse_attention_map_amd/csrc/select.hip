@@ -1,14 +1,17 @@
 // Index selection and block-list expansion kernels.
 //
-//   vs_select_kernel   sink-aware noise floor per VS direction (Alg. 3,
-//                      lines 7-12; Eq. 3-4) with stream compaction
+//   vs_select_kernel   VS budget per direction: the sink-aware noise floor
+//                      (Alg. 3, lines 7-12; Eq. 3-4), the median floor
+//                      (Appendix H) or FlexPrefill's cumulative rule (Alg. 6),
+//                      with stream compaction
 //   pe_*_kernel        pooled estimation for PE heads (Alg. 4): block-mean
 //                      pooling of Q and K, the causal pooled softmax map,
 //                      normalisation, and the gamma-cumsum cut-off found by a
 //                      mass-weighted radix select on the float bits instead
 //                      of a full sort
-//   expand_kernel      per-(head, query block) key-block lists (the block
-//                      mask M_S of Eq. 1), CSR with per-head worst-case bases
+//   expand_*_kernel    per-(head, query block) key-block lists (the block
+//                      mask M_S of Eq. 1), CSR with per-head worst-case bases:
+//                      row lengths, per-head scan, fill
 //
 // Decisions are taken in float in the order the paper writes them; the
 // pooled masses are summed in 2^-62 fixed point, which is exact and
@@ -53,17 +56,73 @@ __device__ int block_scan_1024(int v, int* wsum, int* total)
     return excl;
 }
 
-// grid (hq, 2): direction 0 = vertical (p_v), 1 = slash (p_s).
+// Exclusive prefix sum of doubles over a 1024-thread block; also the total.
+__device__ double block_scan_1024(double v, double* wsum, double* total)
+{
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    double x = v;
+    for (int o = 1; o < 64; o <<= 1) {
+        const double y = __shfl_up(x, o);
+        if (lane >= o) x += y;
+    }
+    if (lane == 63) wsum[w] = x;
+    __syncthreads();
+    if (w == 0) {
+        double s = (lane < 16) ? wsum[lane] : 0.0;
+        for (int o = 1; o < 16; o <<= 1) {
+            const double y = __shfl_up(s, o);
+            if (lane >= o) s += y;
+        }
+        if (lane < 16) wsum[lane] = s;
+    }
+    __syncthreads();
+    const double excl = (w > 0 ? wsum[w - 1] : 0.0) + x - v;
+    *total = wsum[15];
+    __syncthreads();
+    return excl;
+}
+
+// Ascending bitonic sort of keys[0 .. np2) in LDS (np2 a power of two
+// <= kMaxBlocks), 1024 threads.
+__device__ void bitonic_sort(unsigned long long* keys, int np2)
+{
+    for (int k = 2; k <= np2; k <<= 1)
+        for (int j = k >> 1; j > 0; j >>= 1) {
+            for (int i = threadIdx.x; i < np2; i += 1024) {
+                const int ixj = i ^ j;
+                if (ixj > i) {
+                    const unsigned long long a = keys[i], b = keys[ixj];
+                    if ((a > b) == ((i & k) == 0)) {
+                        keys[i] = b;
+                        keys[ixj] = a;
+                    }
+                }
+            }
+            __syncthreads();
+        }
+}
+
+// grid (hq, 2): direction 0 = vertical (p_v), 1 = slash (p_s).  Budget rule:
+//   0  p_j > alpha * r / (N_b - 2), r = max(1 - p_0 - p_{N_b-1}, 0)   (Eq. 3-4)
+//   1  p_j > alpha * median(p_1 .. p_{N_b-2})                          (App. H)
+//   2  the shortest prefix of (p desc, j asc) whose running sum, in
+//      double, reaches gamma_vs                                        (Alg. 6)
+// then clip(k, k_min, N_b) with top-k by (p desc, j asc) for rules 0 and 1
+// (N_b <= 2 keeps every block under them) and, for rule 2, at least k_min
+// entries of the same order.  Values are compared in float.
 __global__ void __launch_bounds__(1024)
 vs_select_kernel(const uint8_t* __restrict__ pattern, const float* __restrict__ p_v,
-                 const float* __restrict__ p_s, int nb, float alpha, int kmin,
+                 const float* __restrict__ p_s, int nb, VsRule vr,
                  int32_t* __restrict__ sel_v, int32_t* __restrict__ sel_s,
                  int32_t* __restrict__ counts, uint8_t* __restrict__ bitmap)
 {
     __shared__ int wsum[16];
+    __shared__ double wsum_d[16];
     __shared__ float best_v[16];
     __shared__ int best_i[16];
+    __shared__ int s_kk;
     __shared__ uint8_t flag[kMaxBlocks];
+    __shared__ unsigned long long keys[kMaxBlocks];
 
     const int h = blockIdx.x, dir = blockIdx.y, tid = threadIdx.x;
     const int lane = tid & 63, w = tid >> 6;
@@ -74,57 +133,109 @@ vs_select_kernel(const uint8_t* __restrict__ pattern, const float* __restrict__ 
     const float* p = (dir ? p_s : p_v) + (size_t)h * nb;
     int32_t* sel = (dir ? sel_s : sel_v) + (size_t)h * nb;
     uint8_t* bm = bitmap + ((size_t)h * 2 + dir) * nb;
+    int np2 = 1;
+    while (np2 < nb) np2 <<= 1;
 
-    // Eq. 3: mu over the N_b - 2 non-retained blocks; Eq. 4: p_j > alpha * mu
-    float theta = -INFINITY;
-    if (nb > 2) {
-        float r = 1.0f - p[0];
-        r = r - p[nb - 1];
-        r = fmaxf(r, 0.0f);
-        const float mu = r / (float)(nb - 2);
-        theta = alpha * mu;
-    }
     float pv[4];
-    int cnt = 0;
     for (int e = 0; e < 4; ++e) {
         const int j = 4 * tid + e;
         pv[e] = (j < nb) ? p[j] : -INFINITY;
-        const bool f = (j < nb) && (pv[e] > theta);
-        flag[j] = f;
-        cnt += f;
     }
-    int total;
-    block_scan_1024(cnt, wsum, &total);
-    if (total < kmin && total < nb) {
-        // clip to k_min: top-k_min by (p desc, index asc)
-        const int kk = min(kmin, nb);
+    int cnt = 0;
+    if (vr.rule == 2) {
+        // order (p desc, j asc): the complemented float bits of p >= 0
+        // descend as p grows
+        for (int i = tid; i < np2; i += 1024)
+            keys[i] = (i < nb) ? ((unsigned long long)(~__float_as_uint(p[i])) << 32) | (unsigned)i
+                               : ~0ull;
+        __syncthreads();
+        bitonic_sort(keys, np2);
+        double part = 0.0, vals[4];
+        for (int e = 0; e < 4; ++e) {
+            const int t = 4 * tid + e;
+            vals[e] = (t < nb) ? (double)__uint_as_float(~(uint32_t)(keys[t] >> 32)) : 0.0;
+            part += vals[e];
+        }
+        if (tid == 0) s_kk = nb;
+        double total;
+        double run = block_scan_1024(part, wsum_d, &total);
+        for (int e = 0; e < 4; ++e) {
+            const int t = 4 * tid + e;
+            run += vals[e];
+            if (t < nb && run >= (double)vr.gamma_vs) {
+                atomicMin(&s_kk, t + 1);
+                break;
+            }
+        }
+        __syncthreads();
+        const int kk = min(max(s_kk, vr.kmin_blocks), nb);
         for (int e = 0; e < 4; ++e) flag[4 * tid + e] = 0;
         __syncthreads();
-        for (int round = 0; round < kk; ++round) {
-            float bv = -INFINITY;
-            int bi = 0x7fffffff;
-            for (int e = 0; e < 4; ++e) {
-                const int j = 4 * tid + e;
-                if (j < nb && !flag[j] && (pv[e] > bv || (pv[e] == bv && j < bi))) { bv = pv[e]; bi = j; }
-            }
-            for (int o = 32; o > 0; o >>= 1) {
-                const float ov = __shfl_xor(bv, o);
-                const int oi = __shfl_xor(bi, o);
-                if (ov > bv || (ov == bv && oi < bi)) { bv = ov; bi = oi; }
-            }
-            if (lane == 0) { best_v[w] = bv; best_i[w] = bi; }
-            __syncthreads();
-            if (tid == 0) {
-                float v = best_v[0];
-                int i = best_i[0];
-                for (int x = 1; x < 16; ++x)
-                    if (best_v[x] > v || (best_v[x] == v && best_i[x] < i)) { v = best_v[x]; i = best_i[x]; }
-                flag[i] = 1;
-            }
-            __syncthreads();
-        }
-        cnt = 0;
+        for (int t = tid; t < kk; t += 1024) flag[(uint32_t)keys[t]] = 1;
+        __syncthreads();
         for (int e = 0; e < 4; ++e) cnt += flag[4 * tid + e];
+    } else {
+        float theta = -INFINITY;
+        if (nb > 2 && vr.rule == 0) {
+            // Eq. 3: mu over the N_b - 2 non-retained blocks
+            float r = 1.0f - p[0];
+            r = r - p[nb - 1];
+            r = fmaxf(r, 0.0f);
+            const float mu = r / (float)(nb - 2);
+            theta = vr.alpha * mu;
+        } else if (nb > 2) {
+            // Appendix H: median of blocks 1 .. N_b-2 (ascending float bits)
+            for (int i = tid; i < np2; i += 1024)
+                keys[i] = (i >= 1 && i <= nb - 2)
+                              ? ((unsigned long long)__float_as_uint(p[i]) << 32) | (unsigned)i
+                              : ~0ull;
+            __syncthreads();
+            bitonic_sort(keys, np2);
+            const int m = nb - 2;
+            const float hi_v = __uint_as_float((uint32_t)(keys[m / 2] >> 32));
+            const float med = (m & 1) ? hi_v
+                                      : (__uint_as_float((uint32_t)(keys[m / 2 - 1] >> 32)) + hi_v) * 0.5f;
+            theta = vr.alpha * med;
+        }
+        for (int e = 0; e < 4; ++e) {
+            const int j = 4 * tid + e;
+            const bool f = (j < nb) && (pv[e] > theta);
+            flag[j] = f;
+            cnt += f;
+        }
+        int total;
+        block_scan_1024(cnt, wsum, &total);
+        if (total < vr.kmin_blocks && total < nb) {
+            // clip to k_min: top-k_min by (p desc, index asc)
+            const int kk = min(vr.kmin_blocks, nb);
+            for (int e = 0; e < 4; ++e) flag[4 * tid + e] = 0;
+            __syncthreads();
+            for (int round = 0; round < kk; ++round) {
+                float bv = -INFINITY;
+                int bi = 0x7fffffff;
+                for (int e = 0; e < 4; ++e) {
+                    const int j = 4 * tid + e;
+                    if (j < nb && !flag[j] && (pv[e] > bv || (pv[e] == bv && j < bi))) { bv = pv[e]; bi = j; }
+                }
+                for (int o = 32; o > 0; o >>= 1) {
+                    const float ov = __shfl_xor(bv, o);
+                    const int oi = __shfl_xor(bi, o);
+                    if (ov > bv || (ov == bv && oi < bi)) { bv = ov; bi = oi; }
+                }
+                if (lane == 0) { best_v[w] = bv; best_i[w] = bi; }
+                __syncthreads();
+                if (tid == 0) {
+                    float v = best_v[0];
+                    int i = best_i[0];
+                    for (int x = 1; x < 16; ++x)
+                        if (best_v[x] > v || (best_v[x] == v && best_i[x] < i)) { v = best_v[x]; i = best_i[x]; }
+                    flag[i] = 1;
+                }
+                __syncthreads();
+            }
+            cnt = 0;
+            for (int e = 0; e < 4; ++e) cnt += flag[4 * tid + e];
+        }
     }
     int kept;
     int pos = block_scan_1024(cnt, wsum, &kept);
@@ -391,75 +502,118 @@ pe_resolve_kernel(const uint8_t* __restrict__ pattern, int nb, int pass,
     }
 }
 
-// grid hq, 1024 threads: row lengths, per-head scan, fill.
-__global__ void __launch_bounds__(1024)
-expand_kernel(const uint8_t* __restrict__ pattern, int nb, const uint8_t* __restrict__ bitmap,
-              const float* __restrict__ abar, const PeState* __restrict__ state,
-              int32_t* __restrict__ row_ptr, int32_t* __restrict__ col_idx,
-              int32_t* __restrict__ counts)
-{
-    __shared__ int len[kMaxBlocks];
-    __shared__ uint8_t bmv[kMaxBlocks];
-    __shared__ uint8_t bms[kMaxBlocks];
-    __shared__ int wsum[16];
-    const int h = blockIdx.x, tid = threadIdx.x;
-    const int lane = tid & 63, w = tid >> 6;
-    const bool vs = pattern[h] != 0;
-    const size_t tri_total = tri(nb);
-    const size_t base = (size_t)h * tri_total;
-    const float* arow = abar + base;
-    uint32_t key_star = 0, flat_star = 0;
-    if (vs) {
-        for (int j = tid; j < nb; j += 1024) {
-            bmv[j] = bitmap[((size_t)h * 2) * nb + j];
-            bms[j] = bitmap[((size_t)h * 2 + 1) * nb + j];
-        }
-    } else {
-        key_star = state[h].key_star;
-        flat_star = state[h].flat_star;
-    }
-    __syncthreads();
+// Block-list membership of (qb, kb) for one head: VS rows from the two
+// direction bitmaps, PE rows from the gamma cut-off (key_star, flat_star).
+struct RowRule {
+    bool vs;
+    int nb;
+    const uint8_t* bmv;       // LDS copies of the head's bitmaps (VS)
+    const uint8_t* bms;
+    const float* arow;        // head's triangular pooled map (PE)
+    uint32_t key_star, flat_star;
 
-    auto member = [&](int qb, int kb) -> bool {
+    __device__ bool member(int qb, int kb) const
+    {
         if (kb > qb) return false;
         if (kb == 0 || kb == qb) return true;
         if (vs) return bmv[kb] || bms[nb - 1 - (qb - kb)];
         const uint32_t key = ~__float_as_uint(arow[tri(qb) + kb]);
         return key < key_star ||
                (key == key_star && (uint32_t)qb * (uint32_t)nb + (uint32_t)kb <= flat_star);
-    };
+    }
+};
 
-    for (int qb = w; qb < nb; qb += 16) {
-        int c = 0;
-        for (int kb0 = 0; kb0 <= qb; kb0 += 64) c += __popcll(__ballot(member(qb, kb0 + lane)));
-        if (lane == 0) len[qb] = c;
+constexpr int kRowsPerGroup = 64;   // query blocks per work-group of the expansion
+
+__device__ RowRule load_rule(const uint8_t* __restrict__ pattern, int nb, int h,
+                             const uint8_t* __restrict__ bitmap, const float* __restrict__ abar,
+                             const PeState* __restrict__ state, uint8_t* bmv, uint8_t* bms)
+{
+    RowRule r;
+    r.vs = pattern[h] != 0;
+    r.nb = nb;
+    r.bmv = bmv;
+    r.bms = bms;
+    r.arow = abar + (size_t)h * tri(nb);
+    r.key_star = r.flat_star = 0;
+    if (r.vs) {
+        for (int j = threadIdx.x; j < nb; j += blockDim.x) {
+            bmv[j] = bitmap[((size_t)h * 2) * nb + j];
+            bms[j] = bitmap[((size_t)h * 2 + 1) * nb + j];
+        }
+    } else {
+        r.key_star = state[h].key_star;
+        r.flat_star = state[h].flat_star;
     }
     __syncthreads();
-    int mine = 0;
+    return r;
+}
+
+// grid (ceil(Nb / 64), hq), 1024 threads: the length of each row, written
+// into row_ptr[h][qb] (scanned in place by expand_scan_kernel).
+__global__ void __launch_bounds__(1024)
+expand_count_kernel(const uint8_t* __restrict__ pattern, int nb, const uint8_t* __restrict__ bitmap,
+                    const float* __restrict__ abar, const PeState* __restrict__ state,
+                    int32_t* __restrict__ row_ptr)
+{
+    __shared__ uint8_t bmv[kMaxBlocks];
+    __shared__ uint8_t bms[kMaxBlocks];
+    const int h = blockIdx.y, lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const RowRule rule = load_rule(pattern, nb, h, bitmap, abar, state, bmv, bms);
+    const int q0 = blockIdx.x * kRowsPerGroup, q1 = min(nb, q0 + kRowsPerGroup);
+    for (int qb = q0 + w; qb < q1; qb += 16) {
+        int c = 0;
+        for (int kb0 = 0; kb0 <= qb; kb0 += 64) c += __popcll(__ballot(rule.member(qb, kb0 + lane)));
+        if (lane == 0) row_ptr[(size_t)h * (nb + 1) + qb] = c;
+    }
+}
+
+// grid hq, 1024 threads: exclusive scan of the row lengths into absolute
+// offsets (head h's lists start at h * Nb (Nb + 1) / 2), and K*.
+__global__ void __launch_bounds__(1024)
+expand_scan_kernel(const uint8_t* __restrict__ pattern, int nb, const PeState* __restrict__ state,
+                   int32_t* __restrict__ row_ptr, int32_t* __restrict__ counts)
+{
+    __shared__ int wsum[16];
+    const int h = blockIdx.x, tid = threadIdx.x;
+    const size_t base = (size_t)h * tri(nb);
+    int32_t* rp = row_ptr + (size_t)h * (nb + 1);
+    int len[4], mine = 0;
     for (int e = 0; e < 4; ++e) {
         const int j = 4 * tid + e;
-        mine += (j < nb) ? len[j] : 0;
+        len[e] = (j < nb) ? rp[j] : 0;
+        mine += len[e];
     }
     int total;
     int start = block_scan_1024(mine, wsum, &total);
     for (int e = 0; e < 4; ++e) {
         const int j = 4 * tid + e;
         if (j >= nb) break;
-        const int l = len[j];
-        len[j] = start;
-        row_ptr[(size_t)h * (nb + 1) + j] = (int32_t)(base + start);
-        start += l;
+        rp[j] = (int32_t)(base + start);
+        start += len[e];
     }
     if (tid == 0) {
-        row_ptr[(size_t)h * (nb + 1) + nb] = (int32_t)(base + total);
-        counts[h * 3 + 2] = vs ? 0 : (int32_t)state[h].kstar;
+        rp[nb] = (int32_t)(base + total);
+        counts[h * 3 + 2] = pattern[h] ? 0 : (int32_t)state[h].kstar;
     }
-    __syncthreads();
+}
+
+// grid (ceil(Nb / 64), hq), 1024 threads: ascending key blocks of each row.
+__global__ void __launch_bounds__(1024)
+expand_fill_kernel(const uint8_t* __restrict__ pattern, int nb, const uint8_t* __restrict__ bitmap,
+                   const float* __restrict__ abar, const PeState* __restrict__ state,
+                   const int32_t* __restrict__ row_ptr, int32_t* __restrict__ col_idx)
+{
+    __shared__ uint8_t bmv[kMaxBlocks];
+    __shared__ uint8_t bms[kMaxBlocks];
+    const int h = blockIdx.y, lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const RowRule rule = load_rule(pattern, nb, h, bitmap, abar, state, bmv, bms);
     const unsigned long long below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-    for (int qb = w; qb < nb; qb += 16) {
-        size_t pos = base + len[qb];
+    const int q0 = blockIdx.x * kRowsPerGroup, q1 = min(nb, q0 + kRowsPerGroup);
+    for (int qb = q0 + w; qb < q1; qb += 16) {
+        size_t pos = (size_t)row_ptr[(size_t)h * (nb + 1) + qb];
         for (int kb0 = 0; kb0 <= qb; kb0 += 64) {
-            const bool mbr = member(qb, kb0 + lane);
+            const bool mbr = rule.member(qb, kb0 + lane);
             const unsigned long long bal = __ballot(mbr);
             if (mbr) col_idx[pos + __popcll(bal & below)] = kb0 + lane;
             pos += __popcll(bal);
@@ -470,8 +624,8 @@ expand_kernel(const uint8_t* __restrict__ pattern, int nb, const uint8_t* __rest
 }  // namespace
 
 hipError_t launch_select(const uint16_t* q, const uint16_t* k, const uint8_t* pattern,
-                         const float* p_v, const float* p_s, int n, int hq, int hkv, float alpha,
-                         int kmin_blocks, float gamma, const SelectScratch& s, int32_t* sel_v,
+                         const float* p_v, const float* p_s, int n, int hq, int hkv,
+                         const VsRule& vs, float gamma, const SelectScratch& s, int32_t* sel_v,
                          int32_t* sel_s, int32_t* sel_counts, int32_t* row_ptr, int32_t* col_idx,
                          hipStream_t stream)
 {
@@ -480,7 +634,7 @@ hipError_t launch_select(const uint16_t* q, const uint16_t* k, const uint8_t* pa
 #define CRISP_CHECK_LAUNCH() \
     if ((e = hipGetLastError()) != hipSuccess) return e
     hipLaunchKernelGGL(vs_select_kernel, dim3(hq, 2), dim3(1024), 0, stream, pattern, p_v, p_s, nb,
-                       alpha, kmin_blocks, sel_v, sel_s, sel_counts, s.bitmap);
+                       vs, sel_v, sel_s, sel_counts, s.bitmap);
     CRISP_CHECK_LAUNCH();
     hipLaunchKernelGGL(pe_init_kernel, dim3(hq), dim3(256), 0, stream, pattern, gamma, s.hist_mass,
                        s.hist_count, s.state);
@@ -503,8 +657,15 @@ hipError_t launch_select(const uint16_t* q, const uint16_t* k, const uint8_t* pa
                            s.hist_mass, s.hist_count, s.state);
         CRISP_CHECK_LAUNCH();
     }
-    hipLaunchKernelGGL(expand_kernel, dim3(hq), dim3(1024), 0, stream, pattern, nb, s.bitmap, s.abar,
-                       s.state, row_ptr, col_idx, sel_counts);
+    const dim3 rows_grid((nb + kRowsPerGroup - 1) / kRowsPerGroup, hq);
+    hipLaunchKernelGGL(expand_count_kernel, rows_grid, dim3(1024), 0, stream, pattern, nb, s.bitmap,
+                       s.abar, s.state, row_ptr);
+    CRISP_CHECK_LAUNCH();
+    hipLaunchKernelGGL(expand_scan_kernel, dim3(hq), dim3(1024), 0, stream, pattern, nb, s.state,
+                       row_ptr, sel_counts);
+    CRISP_CHECK_LAUNCH();
+    hipLaunchKernelGGL(expand_fill_kernel, rows_grid, dim3(1024), 0, stream, pattern, nb, s.bitmap,
+                       s.abar, s.state, row_ptr, col_idx);
     CRISP_CHECK_LAUNCH();
 #undef CRISP_CHECK_LAUNCH
     return hipSuccess;

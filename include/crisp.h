@@ -53,15 +53,36 @@ enum crisp_status {
     CRISP_ERR_HIP = 5          /* a kernel launch failed                          */
 };
 
+/* Routers (crisp_opts.router). */
+enum crisp_router {
+    CRISP_ROUTER_CSTRUCT = 0,  /* structural proxy C_struct >= tau_proxy (Alg. 2, Eq. 2)  */
+    CRISP_ROUTER_JSD = 1       /* FlexPrefill's D_JS >= tau_jsd (Alg. 5), the baseline     */
+};
+
+/* VS budget rules (crisp_opts.vs_rule); every rule clips to k_min. */
+enum crisp_vs_rule {
+    CRISP_VS_NOISE_MEAN = 0,   /* p_j > alpha * r / (N_b - 2) (Alg. 3, Eq. 3-4)           */
+    CRISP_VS_NOISE_MEDIAN = 1, /* p_j > alpha * median(p_1 .. p_{N_b-2}) (Appendix H)      */
+    CRISP_VS_GAMMA = 2         /* shortest prefix of sorted p with sum >= gamma_vs (Alg. 6) */
+};
+
 /*
- * Hyper-parameters (Section 5, "Setup"; Section 3.2).  NULL selects the
- * paper's defaults {0.2, 0.95, 1024, 128, 128}.
+ * Hyper-parameters (Section 5, "Setup"; Section 3.2; Appendices A and H).
+ * NULL selects the defaults crisp_default_opts() writes:
+ * {0.2, 0.95, 1024, 128, 128, CRISP_ROUTER_CSTRUCT, 0.1, CRISP_VS_NOISE_MEAN,
+ * 0.95}.
  *   tau_proxy     routing threshold: VS iff C_struct >= tau_proxy (Alg. 2)
  *   gamma         PE coverage target (Alg. 4), in (0, 1]
  *   k_min_tokens  minimum budget per VS direction, in tokens (a multiple of
  *                 block_size; clip(k, k_min, N_b) of Alg. 3)
  *   w_sink        anchor windows of C_struct (Eq. 2); must equal block_size,
  *   w_local       which makes them exactly the first and last key block
+ *   router        enum crisp_router
+ *   tau_jsd       threshold of CRISP_ROUTER_JSD (not given by the paper; 0.1)
+ *   vs_rule       enum crisp_vs_rule
+ *   gamma_vs      coverage target of CRISP_VS_GAMMA, in (0, 1]
+ * CRISP itself is router 0 with rule 0; router 1 with rule 2 is the
+ * FlexPrefill baseline the paper compares against (Appendix A).
  */
 typedef struct crisp_opts {
     float tau_proxy;
@@ -69,7 +90,14 @@ typedef struct crisp_opts {
     int k_min_tokens;
     int w_sink;
     int w_local;
+    int router;
+    float tau_jsd;
+    int vs_rule;
+    float gamma_vs;
 } crisp_opts;
+
+/* Writes the defaults listed above into *opts (host pointer, not NULL). */
+void crisp_default_opts(crisp_opts *opts);
 
 /* Static text for a status code. */
 const char *crisp_status_string(int code);
@@ -95,9 +123,13 @@ int crisp_workspace_size(int seq_len, int n_heads, int n_kv_heads, int head_dim,
  *              its query q_i; diagonal (slash) block j collects the offsets
  *              (N_b-1-j)*B .. (N_b-j)*B - 1, so block N_b-1 is the recency
  *              band and block 0 the farthest diagonals.
- *   c_struct   float [n_heads]  anchor mass, Eq. 2: the first and the last
- *              block (= p_v[0] + p_v[N_b-1]; p_v[0] when N_b = 1)
+ *   c_struct   float [n_heads]  the routing statistic: the anchor mass of
+ *              Eq. 2, the first and the last block (= p_v[0] + p_v[N_b-1];
+ *              p_v[0] when N_b = 1), or D_JS (Alg. 5) under CRISP_ROUTER_JSD
  *   pattern    uint8 [n_heads]  1 = vertical-slash, 0 = pooled estimation
+ * CRISP_ROUTER_JSD: D_JS = sqrt(KL(p_v||m)/2 + KL(abar||m)/2), m the mean of
+ * the two, abar = Softmax over blocks of the mean representative query
+ * against the per-block key means (natural logarithms).
  * A^ itself is never materialised.
  */
 int crisp_route(const void *q, const void *k, int seq_len, int n_heads, int n_kv_heads,
@@ -119,7 +151,8 @@ int crisp_route(const void *q, const void *k, int seq_len, int n_heads, int n_kv
  *   col_idx       int32 [csr_capacity]
  * VS rows: {0, qb} u {v in S_v : v <= qb} u {qb - (N_b-1-j) : j in S_s, >= 0}.
  * PE rows: the kept (qb, kb) entries of the pooled map, plus {0, qb}.
- * alpha is the noise-floor multiplier of Eq. 4 (>= 0; 1.0 recommended).
+ * alpha is the noise-floor multiplier of Eq. 4 (>= 0; 1.0 recommended);
+ * opts->vs_rule picks the VS budget rule (alpha is unused by CRISP_VS_GAMMA).
  */
 int crisp_select(const void *q, const void *k, const uint8_t *pattern, const float *p_v,
                  const float *p_s, int seq_len, int n_heads, int n_kv_heads, int head_dim,

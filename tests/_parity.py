@@ -81,6 +81,36 @@ def check_route(gr, orc: O.Route, margin=None):
         assert np.all(np.abs(orc.c_struct - O.TAU_PROXY) >= margin), orc.c_struct
 
 
+def check_route_jsd(gr, orc: O.Route, tau=O.TAU_JSD):
+    """JSD router: D_JS close; routing bits exact outside a 1e-4 band of tau."""
+    np.testing.assert_allclose(gr["c_struct"], orc.c_struct, rtol=2e-4, atol=1e-6)
+    pat = gr["pattern"].astype(np.uint8)
+    near = np.abs(orc.c_struct - tau) <= BAND * tau
+    assert np.array_equal(pat[~near], orc.pattern[~near]), (pat, orc.pattern)
+    np.testing.assert_allclose(gr["p_v"], orc.p_v, rtol=2e-4, atol=1e-7)
+    np.testing.assert_allclose(gr["p_s"], orc.p_s, rtol=2e-4, atol=1e-7)
+
+
+def gamma_exempt(p: np.ndarray, gamma: float, kmin: int) -> set:
+    """Blocks whose membership under the cumulative rule could flip within
+    the 1e-4 band: near-ties with the cut-off value, and the entries on
+    either side of the cut when the running sum there is within the band."""
+    pf = p.astype(np.float32).astype(np.float64)
+    nb = len(pf)
+    order = sorted(range(nb), key=lambda j: (-pf[j], j))
+    cum = np.cumsum(pf[order])
+    g = float(np.float32(gamma))
+    hit = np.nonzero(cum >= g)[0]
+    kk = int(hit[0]) + 1 if len(hit) else nb
+    kk = min(max(kk, kmin), nb)
+    vstar = pf[order[kk - 1]]
+    ex = set(np.nonzero(np.abs(pf - vstar) <= BAND * max(vstar, 1e-30))[0].tolist())
+    for t in (kk - 2, kk - 1, kk):
+        if 0 <= t < nb and abs(cum[t] - g) <= BAND * g:
+            ex |= {order[t], order[min(t + 1, nb - 1)]}
+    return ex
+
+
 def vs_exempt(p: np.ndarray, s: O.VSSel) -> set:
     """Blocks whose deciding value is within BAND of the threshold."""
     pf = p.astype(np.float32).astype(np.float64)
@@ -147,8 +177,10 @@ class Report:
                 f"exempt={self.exempt} non_exempt={self.mismatch - self.exempt}")
 
 
-def check_select(inp, gr, gs, alpha, orc_route: O.Route, heads=None, rep=None, gamma=O.GAMMA):
-    """Sets (exempt-aware), counts, and exact expansion of the GPU's own sets."""
+def check_select(inp, gr, gs, alpha, orc_route: O.Route, heads=None, rep=None, gamma=O.GAMMA,
+                 vs_rule="mean", gamma_vs=O.GAMMA, kmin=O.K_MIN_TOKENS // 128):
+    """Sets (exempt-aware), counts, and exact expansion of the GPU's own sets.
+    vs_rule: "mean" (Alg. 3), "median" (Appendix H) or "gamma" (Alg. 6)."""
     sp = inp.spec
     n, hq, hkv = sp.n, sp.hq, sp.hkv
     nb = -(-n // B)
@@ -170,8 +202,13 @@ def check_select(inp, gr, gs, alpha, orc_route: O.Route, heads=None, rep=None, g
             assert np.all(np.diff(gs["sel_v"][h, :kv]) > 0) and np.all(np.diff(gs["sel_s"][h, :ks]) > 0)
             assert kp == 0
             for dname, got, p in (("v", got_v, orc_route.p_v[h]), ("s", got_s, orc_route.p_s[h])):
-                s = O.vs_select(p, alpha)
-                bad = rep.add(got, set(s.sel.tolist()), nb, vs_exempt(p, s))
+                if vs_rule == "gamma":
+                    want = set(O.gamma_select(p, gamma_vs, kmin).tolist())
+                    ex = gamma_exempt(p, gamma_vs, kmin)
+                else:
+                    s = O.vs_select(p, alpha, kmin, vs_rule)
+                    want, ex = set(s.sel.tolist()), vs_exempt(p, s)
+                bad = rep.add(got, want, nb, ex)
                 assert not bad, (h, dname, sorted(bad))
             # expansion of the GPU's sets is exact
             erp, eci, cnt = O.expand(nb, True, np.array(sorted(got_v)), np.array(sorted(got_s)))

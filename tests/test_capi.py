@@ -76,10 +76,7 @@ def test_workspace_size_null_outputs(L):
 
 
 def _opts(**kw):
-    o = crisp.crisp_opts(0.2, 0.95, 1024, 128, 128)
-    for k, v in kw.items():
-        setattr(o, k, v)
-    return C.byref(o)
+    return C.byref(crisp.default_opts(**kw))
 
 
 FAKE = C.c_void_p(1 << 20)      # aligned, never dereferenced: validation fails first
@@ -104,6 +101,10 @@ def test_validation_before_launch(L):
                            FAKE, 1 << 30, FAKE, None) == INVALID
     assert L.crisp_prefill(FAKE, FAKE, FAKE, 256, 4, 1, 128, 128, 1.0, _opts(w_sink=64), FAKE,
                            1 << 30, FAKE, None) == UNSUPPORTED
+    for bad in (dict(router=2), dict(vs_rule=3), dict(vs_rule=-1), dict(gamma_vs=0.0),
+                dict(gamma_vs=1.5), dict(tau_jsd=float("inf"))):
+        assert L.crisp_prefill(FAKE, FAKE, FAKE, 256, 4, 1, 128, 128, 1.0, _opts(**bad), FAKE,
+                               1 << 30, FAKE, None) == INVALID, bad
     # workspace too small
     _, need, cap = ws_size(300, 4, 1)
     assert L.crisp_prefill(FAKE, FAKE, FAKE, 300, 4, 1, 128, 128, 1.0, None, FAKE, need - 256, FAKE,
@@ -123,3 +124,13 @@ def test_empty_sequence_is_a_no_op(L):
     assert L.crisp_prefill(None, None, None, 0, 4, 1, 128, 128, 1.0, None, None, 0, None, None) == OK
     # the size and option checks still run
     assert L.crisp_prefill(None, None, None, 0, 4, 3, 128, 128, 1.0, None, None, 0, None, None) == SHAPE
+
+
+def test_default_opts_are_the_papers():
+    o = crisp.default_opts()
+    assert (o.tau_proxy, o.gamma, o.k_min_tokens, o.w_sink, o.w_local) == \
+        (pytest.approx(0.2), pytest.approx(0.95), 1024, 128, 128)
+    assert o.router == crisp.ROUTER_CSTRUCT and o.vs_rule == crisp.VS_NOISE_MEAN
+    assert o.tau_jsd == pytest.approx(0.1) and o.gamma_vs == pytest.approx(0.95)
+    f = crisp.flexprefill_opts()
+    assert f.router == crisp.ROUTER_JSD and f.vs_rule == crisp.VS_GAMMA

@@ -169,3 +169,70 @@ def test_select_is_deterministic():
         b = P.host(P.gpu_select(q, k, gr, 1.0, ws))
         for key in a:
             assert np.array_equal(a[key], b[key]), key
+
+
+# -------------------------------------- selection rules and the baseline
+@pytest.mark.parametrize("alpha", [1.0, 2.0])
+def test_median_noise_floor(alpha):
+    """Appendix H's median floor: sets against the oracle, outputs on the
+    oracle's lists, and the prefill equal to the staged calls."""
+    sp = synth.custom_spec(8192 + 300, 8, 2, [synth.VS, synth.VS, synth.VS, synth.DIFFUSE,
+                                              synth.VS, synth.CONC, synth.DIST, synth.DIFFUSE],
+                           seed_id=120)
+    inp = synth.generate(sp)
+    n, hq, hkv = sp.n, sp.hq, sp.hkv
+    opts = crisp.default_opts(vs_rule=crisp.VS_NOISE_MEDIAN)
+    q, k, v = P.to_dev(inp)
+    ws = crisp.alloc_workspace(n, hq, hkv)
+    gr = P.gpu_route(q, k, ws, opts=opts)
+    grh = P.host(gr)
+    orc_r = O.route(inp.q, inp.k, n, hq, hkv)
+    P.check_route(grh, orc_r)
+    gs = P.host(P.gpu_select(q, k, gr, alpha, ws, opts=opts))
+    rep = P.check_select(inp, grh, gs, alpha, orc_r, vs_rule="median")
+    P.log(rep.line() + f" median alpha={alpha}")
+    plan = O.plan(inp.q, inp.k, n, hq, hkv, alpha=alpha, routed=orc_r, vs_rule="median")
+    nb = -(-n // B)
+    rows = P.sample_rows(nb, hq, 12, seed=7)
+    out = P.gpu_attend(q, k, v, plan.row_ptr, plan.col_idx, ws)
+    want = O.attend(inp.q, inp.k, inp.v, n, hq, hkv, 128, plan.row_ptr, plan.col_idx, rows)
+    full = torch.zeros(hq, nb * B, 128)
+    full[:, :n] = out.float().cpu()
+    P.check_outputs(full.numpy().reshape(hq * nb, B, 128)[rows], want, f"median alpha={alpha}")
+    out2 = torch.empty_like(q)
+    crisp.crisp_prefill(q, k, v, alpha, crisp.alloc_workspace(n, hq, hkv), out2, opts=opts)
+    staged = P.gpu_attend(q, k, v, gs["row_ptr"], gs["col_idx"], crisp.alloc_workspace(n, hq, hkv))
+    assert torch.equal(out2.view(torch.int16), staged.view(torch.int16))
+
+
+@pytest.mark.parametrize("name", ["c1", "c2"])
+def test_flexprefill_baseline(name):
+    """Appendix A: JSD routing (Alg. 5) and the cumulative gamma rule with
+    the k_min clip (Alg. 6) against the oracle, then attention parity."""
+    inp = synth.generate(synth.config_spec(name))
+    sp = inp.spec
+    n, hq, hkv = sp.n, sp.hq, sp.hkv
+    opts = crisp.flexprefill_opts()
+    q, k, v = P.to_dev(inp)
+    ws = crisp.alloc_workspace(n, hq, hkv)
+    gr = P.gpu_route(q, k, ws, opts=opts)
+    grh = P.host(gr)
+    orc_r = O.route_jsd(inp.q, inp.k, n, hq, hkv)
+    P.check_route_jsd(grh, orc_r)
+    P.log(f"{name} D_JS: {np.round(orc_r.c_struct, 3).tolist()} VS heads {int(orc_r.pattern.sum())}/{hq}")
+    gs = P.host(P.gpu_select(q, k, gr, 1.0, ws, opts=opts))
+    # heads whose bits agree are compared set by set
+    same = [h for h in range(hq) if grh["pattern"][h] == orc_r.pattern[h]]
+    rep = P.check_select(inp, grh, gs, 1.0, orc_r, heads=same, vs_rule="gamma")
+    P.log(rep.line() + " flexprefill")
+    plan = O.plan(inp.q, inp.k, n, hq, hkv, routed=orc_r, vs_rule="gamma")
+    nb = -(-n // B)
+    rows = P.sample_rows(nb, hq, 8, seed=11)
+    out = P.gpu_attend(q, k, v, plan.row_ptr, plan.col_idx, ws)
+    want = O.attend(inp.q, inp.k, inp.v, n, hq, hkv, 128, plan.row_ptr, plan.col_idx, rows)
+    got = out.float().cpu().numpy().reshape(hq * nb, B, 128)[rows]
+    P.check_outputs(got, want, f"{name} flexprefill attend")
+    out2 = torch.empty_like(q)
+    crisp.crisp_prefill(q, k, v, 1.0, crisp.alloc_workspace(n, hq, hkv), out2, opts=opts)
+    staged = P.gpu_attend(q, k, v, gs["row_ptr"], gs["col_idx"], crisp.alloc_workspace(n, hq, hkv))
+    assert torch.equal(out2.view(torch.int16), staged.view(torch.int16))
