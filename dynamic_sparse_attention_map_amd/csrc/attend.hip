@@ -3,10 +3,10 @@
 // One work-group of 8 wavefronts computes two adjacent query blocks of one
 // query head (256 queries, 32 per wavefront).  It walks the merged union of
 // the two blocks' key-block lists, so every K/V tile is fetched once for both
-// blocks; the listed blocks are streamed as 64-key sub-tiles through
-// double-buffered LDS (K row-major; V transposed, keys permuted so that each
-// operand fragment is one 16-byte read), and each wavefront whose block
-// lists the tile runs
+// blocks; the listed blocks are streamed as 64-key sub-tiles, copied from
+// HBM straight into a 4-stage LDS ring (K row-major, V transposed with keys
+// permuted so that each operand fragment is one 16-byte read; both with
+// XOR-swizzled chunks), and each wavefront whose block lists the tile runs
 //     S^T = K Q^T          (32x32x16 bf16 MFMA, fp32 accumulate)
 //     online softmax       (exp2 domain, fp32 running max / sum)
 //     O^T += V^T P^T       (P rounded to bf16, fp32 accumulate)
@@ -15,8 +15,8 @@
 // needs, so P never leaves registers.  The causal mask is applied only on
 // the diagonal key block; sub-tiles that lie entirely in a wavefront's
 // future are skipped.  Fragment reads are issued several products ahead
-// of the matrix cores (scheduling-group hints), and the exponentials of
-// key group u+1 are interleaved with the PV products of group u.
+// of the matrix cores (scheduling-group hints), and the two wavefronts on
+// each SIMD alternate matrix and vector phases (ping-pong, below).
 #include "crisp_common.h"
 #include "crisp_kernels.h"
 
@@ -25,77 +25,39 @@ namespace crisp {
 namespace {
 
 constexpr int kKT = 64;                   // keys per sub-tile
-constexpr int kKPitch = kD + 8;           // K tile row pitch (bf16), 272 bytes
-constexpr int kVPitch = kKT + 8;          // V^T tile row pitch (bf16), 144 bytes
-constexpr int kKStage = kKT * kKPitch;    // bf16 elements
-constexpr int kVStage = kD * kVPitch;
-constexpr int kStage = kKStage + kVStage;
+constexpr int kImg = kKT * kD;            // one K or V^T sub-tile image, bf16 elements (16 KiB)
+constexpr int kStageBytes = 4 * kImg;     // K image, then V^T image
+constexpr int kStages = 4;                // LDS ring depth
 
 constexpr int kThreads = 512;             // 8 wavefronts: two query blocks x 4
 constexpr int kEnd = 0x7fffffff;           // list exhausted
 
-// Register cache of one row's key-block list: lane x of cur holds entry
-// 64*chunk + x and nxt the next 64 (loaded a whole chunk ahead), so entries
-// are read with wave-uniform readlanes and no tile load waits on the list.
-struct ListCursor {
-    int lbase, len, pos, chunk, cur, nxt;
-    bool dense;                            // implicit list 0 .. len-1
-};
+constexpr int kListWords = kMaxBlocks / 32;   // bitmap words per row
 
-__device__ __forceinline__ void cursor_init(ListCursor& c, const int32_t* __restrict__ col_idx,
-                                            int lbase, int len, bool dense, int lane)
+// 16 bytes per lane from global memory straight into LDS: lane l's bytes
+// land at lds_addr + 16 l (lds_addr wave-uniform).  Written as inline asm so
+// that the compiler, which cannot tell the ring's stages apart, does not put
+// a full vmcnt(0) before every LDS read; completion is awaited explicitly
+// (wait_copies) before the barrier that publishes a tile.  M0 is set here
+// and declared clobbered; the s_nop covers the M0 -> LDS-DMA hazard.
+// (M0 is otherwise unused by this code, so its clobber is harmless.)
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void copy16_to_lds(const void* gptr, uint32_t lds_addr)
 {
-    c.lbase = lbase;
-    c.len = len;
-    c.pos = 0;
-    c.chunk = 0;
-    c.dense = dense;
-    c.cur = c.nxt = -1;
-    if (!dense) {
-        c.cur = (lane < len) ? col_idx[lbase + lane] : -1;
-        c.nxt = (64 + lane < len) ? col_idx[lbase + 64 + lane] : -1;
-    }
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+                 :
+                 : "v"(gptr), "s"(__builtin_amdgcn_readfirstlane(lds_addr))
+                 : "memory", "m0");
 }
+#pragma clang diagnostic pop
 
-__device__ __forceinline__ int cursor_peek(const ListCursor& c)
+// s_waitcnt vmcnt(N) with the other counters left alone (gfx9 encoding)
+template <int N>
+__device__ __forceinline__ void wait_copies()
 {
-    if (c.pos >= c.len) return kEnd;
-    if (c.dense) return c.pos;
-    const int src = ((c.pos >> 6) == c.chunk) ? c.cur : c.nxt;
-    return __builtin_amdgcn_readlane(src, c.pos & 63);
-}
-
-__device__ __forceinline__ void cursor_advance(ListCursor& c, const int32_t* __restrict__ col_idx,
-                                               int lane)
-{
-    ++c.pos;
-    if (!c.dense && (c.pos >> 6) != c.chunk) {
-        c.chunk = c.pos >> 6;
-        c.cur = c.nxt;
-        // lanes past the end keep stale values, which are never read
-        const int e = 64 * (c.chunk + 1) + lane;
-        if (e < c.len) c.nxt = col_idx[c.lbase + e];
-    }
-}
-
-// One step of the merged walk over the two rows' lists: the smallest next
-// key block and which of the two rows lists it.
-struct Entry {
-    int kb;            // kEnd when both lists are exhausted
-    bool hi, lo;
-};
-
-__device__ __forceinline__ Entry next_entry(ListCursor& chi, ListCursor& clo,
-                                            const int32_t* __restrict__ col_idx, int lane)
-{
-    const int a = cursor_peek(chi), b = cursor_peek(clo);
-    Entry e;
-    e.kb = min(a, b);
-    e.hi = (a == e.kb) && a != kEnd;
-    e.lo = (b == e.kb) && b != kEnd;
-    if (e.hi) cursor_advance(chi, col_idx, lane);
-    if (e.lo) cursor_advance(clo, col_idx, lane);
-    return e;
+    static_assert(N >= 0 && N < 16, "vmcnt field");
+    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8));
 }
 
 // Work items: like a grid of ceil(npairs*hkv / 8) * 8 * G items whose item b
@@ -105,7 +67,8 @@ __device__ __forceinline__ Entry next_entry(ListCursor& chi, ListCursor& clo,
 // being blocks Nb-1-2p and Nb-2-2p.  Each XCD keeps whole GQA groups (sharing
 // K/V in its L2) and walks the pairs from the longest causal rows down.
 __device__ __forceinline__ void
-attend_pair(int b, uint16_t* lds, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+attend_pair(int b, uint16_t* lds, uint32_t* list, const uint16_t* __restrict__ q,
+            const uint16_t* __restrict__ k,
             const uint16_t* __restrict__ vt, const int32_t* __restrict__ row_ptr,
             const int32_t* __restrict__ col_idx, int n, int nb, int hkv, int G,
             float scale_log2, uint16_t* __restrict__ out)
@@ -127,20 +90,60 @@ attend_pair(int b, uint16_t* lds, const uint16_t* __restrict__ q, const uint16_t
     const int myqb = half ? qb_lo : qb_hi;
     const bool active = myqb >= 0;
 
-    ListCursor chi, clo;
+    // ---- the merged key-block list of the two rows, built in LDS ----
+    // bits[r][kb / 32] bit kb % 32: row r (0 = qb_hi, 1 = qb_lo) lists key
+    // block kb (blocks outside [0, qb] are ignored); then one wavefront
+    // compacts the union into desc[] = kb | hi << 16 | lo << 17, ascending.
+    uint32_t* bits = list;                       // [2][kListWords]
+    uint32_t* desc = list + 2 * kListWords;      // [kMaxBlocks], then the count
+    for (int i = tid; i < 2 * kListWords; i += kThreads) bits[i] = 0u;
+    __syncthreads();
     if (row_ptr) {
-        const int b_hi = row_ptr[h * (nb + 1) + qb_hi];
-        cursor_init(chi, col_idx, b_hi, row_ptr[h * (nb + 1) + qb_hi + 1] - b_hi, false, lane);
-        if (qb_lo >= 0) {
-            const int b_lo = row_ptr[h * (nb + 1) + qb_lo];
-            cursor_init(clo, col_idx, b_lo, row_ptr[h * (nb + 1) + qb_lo + 1] - b_lo, false, lane);
-        } else {
-            cursor_init(clo, col_idx, 0, 0, true, lane);
+        for (int r = 0; r < 2; ++r) {
+            const int qb = r ? qb_lo : qb_hi;
+            if (qb < 0) continue;
+            const int e0 = row_ptr[h * (nb + 1) + qb], e1 = row_ptr[h * (nb + 1) + qb + 1];
+            for (int e = e0 + tid; e < e1; e += kThreads) {
+                const int kb = col_idx[e];
+                if (kb >= 0 && kb <= qb) atomicOr(&bits[r * kListWords + (kb >> 5)], 1u << (kb & 31));
+            }
         }
     } else {
-        cursor_init(chi, col_idx, 0, qb_hi + 1, true, lane);
-        cursor_init(clo, col_idx, 0, qb_lo + 1, true, lane);
+        for (int i = tid; i < 2 * kListWords; i += kThreads) {
+            const int r = i / kListWords, wd = i % kListWords;
+            const int qb = r ? qb_lo : qb_hi;          // blocks 0 .. qb
+            const int lo = 32 * wd;
+            bits[i] = (qb < lo) ? 0u : (qb >= lo + 31) ? ~0u : ((2u << (qb - lo)) - 1u);
+        }
     }
+    __syncthreads();
+    if (w == 0) {
+        uint32_t wa[2], wb[2];
+        int c = 0;
+        for (int x = 0; x < 2; ++x) {
+            wa[x] = bits[2 * lane + x];
+            wb[x] = bits[kListWords + 2 * lane + x];
+            c += __popc(wa[x] | wb[x]);
+        }
+        int incl = c;
+        for (int o = 1; o < 64; o <<= 1) {
+            const int y = __shfl_up(incl, o);
+            if (lane >= o) incl += y;
+        }
+        int pos = incl - c;
+        for (int x = 0; x < 2; ++x) {
+            uint32_t u = wa[x] | wb[x];
+            while (u) {
+                const int bit = __ffs(u) - 1;
+                u &= u - 1;
+                const int kb = 32 * (2 * lane + x) + bit;
+                desc[pos++] = (uint32_t)kb | (((wa[x] >> bit) & 1u) << 16) | (((wb[x] >> bit) & 1u) << 17);
+            }
+        }
+        if (lane == 63) desc[kMaxBlocks] = (uint32_t)incl;
+    }
+    __syncthreads();
+    const int n_entries = __builtin_amdgcn_readfirstlane((int)desc[kMaxBlocks]);
 
     const int qc = 32 * wq + l32;                         // query within its block
     // a partial last block has rows past the end: they load the last row
@@ -158,33 +161,41 @@ attend_pair(int b, uint16_t* lds, const uint16_t* __restrict__ q, const uint16_t
     const float rescale_gap = 8.0f / scale_log2;   // 2^8 in probability
 
     const uint16_t* kg = k + (size_t)g * n * kD;
-    const size_t n_pad = (size_t)nb * kB;                 // V^T row length
-    const uint16_t* vg = vt + (size_t)g * kD * n_pad;
+    // V^T sub-tile images of this KV head, 2 per key block
+    const uint16_t* vg = vt + (size_t)g * nb * (2 * kImg);
 
-    // staging: 2 x 16 bytes of K and 2 x 16 bytes of V^T per thread
-    u32x4 pk[2], pv[2];
-    auto load_tile = [&](int kb, int sub) {
-        const size_t key0 = (size_t)kb * kB + sub * kKT;
-        for (int i = 0; i < 2; ++i) {
-            const int e = tid + kThreads * i;
-            const int row = e >> 4, ch = e & 15;              // 64 keys x 16 chunks
-            // keys past the end of a partial last block read as zero (every
-            // query that exists masks them: they lie in its future)
-            pk[i] = u32x4{0u, 0u, 0u, 0u};
-            if (key0 + row < (size_t)n)
-                pk[i] = *reinterpret_cast<const u32x4*>(kg + (key0 + row) * kD + 8 * ch);
-            const int dr = e >> 3, vc = e & 7;                // 128 d-rows x 8 chunks
-            pv[i] = *reinterpret_cast<const u32x4*>(vg + (size_t)dr * n_pad + key0 + 8 * vc);
+    // Staging.  Every wavefront copies 2 KiB of K and 2 KiB of V^T per tile,
+    // 1 KiB per copy instruction.  LDS images carry an XOR swizzle of the
+    // 16-byte chunks so that the operand reads below are free of bank
+    // conflicts without padding:
+    //   K    [64 keys][16 chunks]:  chunk c of key r at slot c ^ (r & 15)
+    //   V^T  [128 d][8 chunks]:     chunk c of row d at slot c ^ ((d >> 1) & 7)
+    // K is swizzled by the per-lane source address; V^T is stored in HBM as
+    // these images already (v_transpose_kernel), so its copy is contiguous.
+    int k_row[2];
+    uint32_t k_src[2];
+    for (int j = 0; j < 2; ++j) {
+        const int ci = 2 * w + j;                       // 1 KiB chunk of the image
+        k_row[j] = 4 * ci + (lane >> 4);
+        k_src[j] = (uint32_t)(k_row[j] * kD + 8 * ((lane & 15) ^ (k_row[j] & 15)));
+    }
+    const uint32_t lds_base = (uint32_t)(uintptr_t)(
+        (__attribute__((address_space(3))) uint16_t*)lds);
+    auto issue_tile = [&](int t, uint32_t dsc) {        // tile t into stage t % 4
+        const int kb = (int)(dsc & 0xffffu), sub = t & 1;
+        const int key0 = kb * kB + sub * kKT;
+        const uint32_t sb = lds_base + (uint32_t)((t & 3) * kStageBytes) + 2048u * w;
+        const uint16_t* kt = kg + (size_t)key0 * kD;
+        const bool full = key0 + kKT <= n;
+        for (int j = 0; j < 2; ++j) {
+            // keys past the end of a partial last block repeat the last key
+            // (every query that exists masks them: they lie in its future)
+            const uint16_t* src = full ? kt + k_src[j]
+                                       : kg + (size_t)min(key0 + k_row[j], n - 1) * kD + (k_src[j] % kD);
+            copy16_to_lds(src, sb + 1024u * j);
         }
-    };
-    auto store_tile = [&](int stage) {
-        uint16_t* ks = lds + stage * kStage;
-        uint16_t* vs = ks + kKStage;
-        for (int i = 0; i < 2; ++i) {
-            const int e = tid + kThreads * i;
-            *reinterpret_cast<u32x4*>(ks + (e >> 4) * kKPitch + 8 * (e & 15)) = pk[i];
-            *reinterpret_cast<u32x4*>(vs + (e >> 3) * kVPitch + 8 * (e & 7)) = pv[i];
-        }
+        const uint16_t* vimg = vg + (size_t)(2 * kb + sub) * kImg + 1024 * w + 8 * lane;
+        for (int j = 0; j < 2; ++j) copy16_to_lds(vimg + 512 * j, sb + 2 * kImg + 1024u * j);
     };
 
     // ---- tile stream: two 64-key sub-tiles per merged list entry ----
@@ -193,40 +204,34 @@ attend_pair(int b, uint16_t* lds, const uint16_t* __restrict__ q, const uint16_t
         bool act;      // this wavefront computes the tile
         bool diag;     // the tile is in this wavefront's diagonal block
     };
-    Entry ent = next_entry(chi, clo, col_idx, lane);
-    int ent_sub = 0;
-    auto pull = [&](Tile& d) -> bool {
-        if (ent.kb == kEnd) return false;
-        const bool uh = ent.hi && ent.kb >= 0 && ent.kb <= qb_hi;
-        const bool ul = ent.lo && ent.kb >= 0 && ent.kb <= qb_lo;
-        const bool mine = half ? ul : uh;
-        // a block no row can use is never addressed: block 0 is loaded instead
-        d.kb = (uh || ul) ? ent.kb : 0;
-        d.sub = ent_sub;
-        d.diag = mine && ent.kb == myqb;
+    const int n_tiles = 2 * n_entries;
+    auto tile_of = [&](int t, uint32_t dsc) {
+        Tile d;
+        d.kb = (int)(dsc & 0xffffu);
+        d.sub = t & 1;
+        const bool mine = half ? ((dsc >> 17) & 1u) : ((dsc >> 16) & 1u);
+        d.diag = mine && d.kb == myqb;
         // keys 64..127 of the diagonal block lie after every query < 64
-        d.act = mine && !(d.diag && ent_sub == 1 && wq < 2);
-        if (ent_sub == 0) {
-            ent_sub = 1;
-        } else {
-            ent_sub = 0;
-            ent = next_entry(chi, clo, col_idx, lane);
-        }
-        return true;
+        d.act = mine && !(d.diag && d.sub == 1 && wq < 2);
+        return d;
+    };
+    auto desc_at = [&](int t) -> uint32_t {
+        return __builtin_amdgcn_readfirstlane(desc[min(t, n_tiles - 1) >> 1]);
     };
 
     // Instruction-group masks for __builtin_amdgcn_sched_group_barrier.
     constexpr int kSchedValu = 0x002, kSchedMfma = 0x008, kSchedDsRead = 0x100;
 
+    const int kx = l32 & 15, vx = (l32 >> 1) & 7;   // this lane's swizzles
     f32x16 s[2];
     // S^T = K Q^T for the tile in `stage`.  The 16 K fragments are read in
     // the order the matrix cores consume them, six reads ahead.
     auto qk = [&](int stage) {
-        const uint16_t* kbase = lds + stage * kStage + l32 * kKPitch + 8 * hi;
+        const uint16_t* kbase = lds + stage * (kStageBytes / 2) + l32 * kD;
         bf16x8 kf[16];
         for (int i = 0; i < 16; ++i) {      // i = 2 st + a
             const int st = i >> 1, a = i & 1;
-            kf[i] = *reinterpret_cast<const bf16x8*>(kbase + 32 * a * kKPitch + 16 * st);
+            kf[i] = *reinterpret_cast<const bf16x8*>(kbase + 32 * a * kD + 8 * ((2 * st + hi) ^ kx));
         }
         s[0] = f32x16{};
         s[1] = f32x16{};
@@ -274,62 +279,88 @@ attend_pair(int b, uint16_t* lds, const uint16_t* __restrict__ q, const uint16_t
     // P^T operand, then O^T += V^T P^T.  Probabilities of key group u + 1
     // are computed while the matrix cores run group u; a lane whose keys
     // are all masked so far keeps m = -inf and uses 0 as its reference.
-    auto exp_pv = [&](int stage) {
-        const uint16_t* vbase = lds + stage * kStage + kKStage + l32 * kVPitch + 8 * hi;
+    // p = 2^(c s - c m) (one FMA and one v_exp), rounded to bf16 into the
+    // P^T operand; a lane whose keys are all masked so far keeps m = -inf
+    // and uses 0 as its reference
+    bf16x8 pf[4];
+    auto probs = [&]() {
         const float neg_mc = (m_run == -INFINITY) ? 0.f : -m_run * scale_log2;
-        bf16x8 vf[16];                       // vf[4 u + dt]
-        for (int u = 0; u < 4; ++u)
-            for (int dt = 0; dt < 4; ++dt) {
-                vf[4 * u + dt] = *reinterpret_cast<const bf16x8*>(vbase + 32 * dt * kVPitch + 16 * u);
-            }
-        bf16x8 pf[4];
         float acc[4] = {0.f, 0.f, 0.f, 0.f};
-        for (int u = 0; u < 4; ++u) {        // key group u: s[u >> 1][8 (u & 1) .. +7]
+        for (int u = 0; u < 4; ++u)            // key group u: s[u >> 1][8 (u & 1) .. +7]
             for (int j = 0; j < 8; ++j) {
                 const float p = __builtin_amdgcn_exp2f(fmaf(s[u >> 1][8 * (u & 1) + j], scale_log2, neg_mc));
                 acc[j & 3] += p;
                 pf[u][j] = (__bf16)p;
             }
-        }
+        l_run += (acc[0] + acc[1]) + (acc[2] + acc[3]);
+    };
+    // O^T += V^T P^T for the tile in `stage`
+    auto pv_mfma = [&](int stage) {
+        const uint16_t* vbase = lds + stage * (kStageBytes / 2) + kImg + l32 * kKT;
+        bf16x8 vf[16];                       // vf[4 u + dt]
+        for (int u = 0; u < 4; ++u)
+            for (int dt = 0; dt < 4; ++dt)
+                vf[4 * u + dt] = *reinterpret_cast<const bf16x8*>(vbase + 32 * dt * kKT + 8 * ((2 * u + hi) ^ vx));
         for (int u = 0; u < 4; ++u)
             for (int dt = 0; dt < 4; ++dt) o[dt] = mfma32(vf[4 * u + dt], pf[u], o[dt]);
-        l_run += (acc[0] + acc[1]) + (acc[2] + acc[3]);
-        // schedule: V reads for groups 0, 1 and the probabilities of group
-        // 0 first; then each group's 4 products interleaved with the next
-        // group's probabilities and V reads
-        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 8, 0);
-        __builtin_amdgcn_sched_group_barrier(kSchedValu, 30, 0);
-        for (int u = 0; u < 3; ++u)
-            for (int dt = 0; dt < 4; ++dt) {
-                __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
-                __builtin_amdgcn_sched_group_barrier(kSchedValu, 7, 0);
-                if (u < 2) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
-            }
-        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 4, 0);
+        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 6, 0);
+        for (int i = 0; i < 10; ++i) {
+            __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 6, 0);
     };
 
-    // Sequential schedule: tile t+1 is fetched into registers while tile t
-    // is computed, then stored into the other LDS stage.
-    Tile cur{0, 0, false, false}, nxt{0, 0, false, false};
-    if (pull(cur)) {
-        load_tile(cur.kb, cur.sub);
-        store_tile(0);
-        int stage = 0;
-        for (;;) {
-            const bool has_next = pull(nxt);
-            if (has_next) load_tile(nxt.kb, nxt.sub);
+    // Ping-pong schedule.  Per tile t every wavefront runs a matrix-core
+    // phase M_t = PV(t-1) + QK(t) and then a vector-ALU phase V_t = softmax(t),
+    // with a barrier after each phase.  Half 1 starts one barrier late, so in
+    // every phase the two wavefronts that share a SIMD run different kinds of
+    // work (one half's M beside the other half's V) and the matrix cores and
+    // vector ALUs are busy at the same time.  Half 0 runs M_t in phase 2t and
+    // half 1 in phase 2t+1.
+    // Tiles rotate through 4 LDS stages.  Tile t is read in phases 2t .. 2t+3
+    // (K by QK in both halves' M_t, V^T by PV in their M_{t+1}).  Each half
+    // issues its copies of tile t+2 at the start of its M_t (phase 2t or
+    // 2t+1, after the last read of tile t-2 in the same stage) and waits for
+    // them just before the barrier that ends phase 2t+3; tile t+2 is first
+    // read in phase 2t+4.  That barrier ends half 0's V_{t+1} and half 1's
+    // M_{t+1}; each wavefront then has only tile t+3's 4 copies in flight.
+    if (n_tiles > 0) {
+        uint32_t d0 = desc_at(0), d1 = desc_at(1), d2 = desc_at(2);
+        issue_tile(0, d0);
+        if (n_tiles > 1) issue_tile(1, d1);
+        wait_copies<0>();
+        __syncthreads();
+        if (half == 1) __syncthreads();         // the one-phase skew
+        Tile prev{0, 0, false, false};
+        for (int t = 0; t < n_tiles; ++t) {
+            const Tile cur = tile_of(t, d0);
+            const bool more = t + 2 < n_tiles;
+            // ---- M phase ----
+            if (more) issue_tile(t + 2, d2);
+            if (t >= 1 && prev.act) pv_mfma((t - 1) & 3);
+            if (cur.act) qk(t & 3);
+            if (half == 1) {
+                if (more) wait_copies<4>(); else wait_copies<0>();
+            }
             __syncthreads();
+            // ---- V phase ----
             if (cur.act) {
-                qk(stage);
                 if (cur.diag) mask(cur.sub);
                 update_max();
-                exp_pv(stage);
+                probs();
             }
-            if (!has_next) break;
-            store_tile(stage ^ 1);
-            stage ^= 1;
-            cur = nxt;
+            d0 = d1;
+            d1 = d2;
+            d2 = desc_at(t + 3);
+            if (half == 0) {
+                if (more) wait_copies<4>(); else wait_copies<0>();
+            }
+            __syncthreads();
+            prev = cur;
         }
+        if (prev.act) pv_mfma((n_tiles - 1) & 3);   // PV of the last tile
+        if (half == 0) __syncthreads();         // balances the skew
     }
 
     if (!active) return;
@@ -355,7 +386,8 @@ attend_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
               const int32_t* __restrict__ col_idx, int n, int nb, int hkv, int G,
               float scale_log2, int per_xcd, int* __restrict__ ctr, uint16_t* __restrict__ out)
 {
-    __shared__ __attribute__((aligned(16))) uint16_t lds[2 * kStage];
+    __shared__ __attribute__((aligned(1024))) uint16_t lds[kStages * kStageBytes / 2];
+    __shared__ uint32_t list[2 * kListWords + kMaxBlocks + 1];
     __shared__ int s_item;
     const int home = blockIdx.x & 7;
     int next_q = 0;   // queues home+0 .. home+7 in turn; only thread 0 uses it
@@ -374,7 +406,7 @@ attend_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
         const int item = s_item;
         __syncthreads();
         if (item < 0) break;
-        attend_pair(item, lds, q, k, vt, row_ptr, col_idx, n, nb, hkv, G, scale_log2, out);
+        attend_pair(item, lds, list, q, k, vt, row_ptr, col_idx, n, nb, hkv, G, scale_log2, out);
     }
 }
 
@@ -383,14 +415,16 @@ __global__ void zero_counters_kernel(int* __restrict__ ctr)
     if (threadIdx.x < 8) ctr[threadIdx.x] = 0;
 }
 
-// V^T with keys permuted inside every group of 16 (bits 2 and 3 of the key
-// index swapped): vt[g][d][16 j + pi(c)] = v[g][16 j + c][d].  A lane's 8 keys
-// of a PV operand fragment, {4h .. 4h+3, 8+4h .. 8+4h+3} for lane half h (the
-// order the S^T accumulator holds them in), are then 16 contiguous bytes.
-// Rows have n_pad = N_b * B keys; keys past n are zero.
-// grid (n_pad/64, hkv), 256 threads.
+// V^T as LDS-ready images, one per 64-key sub-tile: image i of KV head g
+// (keys 64 i .. 64 i + 63) holds row d (the 64 keys' values
+// of head dimension d) as 8 chunks of 8 keys, chunk c at slot c ^ ((d >> 1) & 7), and inside
+// every group of 16 keys bits 2 and 3 of the key index are swapped.  A
+// lane's 8 keys of a PV operand fragment, {4h .. 4h+3, 8+4h .. 8+4h+3} of a
+// group for lane half h (the order the S^T accumulator holds them in), are
+// then one 16-byte chunk.  Keys past n are zero.
+// grid (N_b * 2, hkv), 256 threads.
 __global__ void __launch_bounds__(256)
-v_transpose_kernel(const uint16_t* __restrict__ v, int n, int n_pad, uint16_t* __restrict__ vt)
+v_transpose_kernel(const uint16_t* __restrict__ v, int n, int n_img, uint16_t* __restrict__ vt)
 {
     __shared__ uint16_t tile[64][kD + 8];
     const int g = blockIdx.y, key0 = blockIdx.x * 64, tid = threadIdx.x;
@@ -403,17 +437,17 @@ v_transpose_kernel(const uint16_t* __restrict__ v, int n, int n_pad, uint16_t* _
         *reinterpret_cast<u32x4*>(&tile[row][8 * ch]) = val;
     }
     __syncthreads();
-    uint16_t* dst = vt + (size_t)g * kD * n_pad + key0;
+    uint16_t* dst = vt + ((size_t)g * n_img + blockIdx.x) * kImg;
     for (int i = 0; i < 4; ++i) {
-        const int e = tid + 256 * i;
-        const int d = e >> 3, c8 = e & 7;
+        const int e = tid + 256 * i;                    // slot e & 7 of row d
+        const int d = e >> 3, c = (e & 7) ^ ((d >> 1) & 7);
         u32x4 val;
         for (int x = 0; x < 4; ++x) {
-            const int p0 = 8 * c8 + 2 * x;              // positions p0, p0 + 1
+            const int p0 = 8 * c + 2 * x;               // positions p0, p0 + 1
             const int k0 = (p0 & ~12) | ((p0 & 4) << 1) | ((p0 & 8) >> 1);
             val[x] = (uint32_t)tile[k0][d] | ((uint32_t)tile[k0 + 1][d] << 16);
         }
-        *reinterpret_cast<u32x4*>(dst + (size_t)d * n_pad + 8 * c8) = val;
+        *reinterpret_cast<u32x4*>(dst + 8 * e) = val;
     }
 }
 
@@ -421,9 +455,8 @@ v_transpose_kernel(const uint16_t* __restrict__ v, int n, int n_pad, uint16_t* _
 
 hipError_t launch_v_transpose(const uint16_t* v, int n, int hkv, uint16_t* vt, hipStream_t stream)
 {
-    const int n_pad = (n + kB - 1) / kB * kB;
-    hipLaunchKernelGGL(v_transpose_kernel, dim3(n_pad / 64, hkv), dim3(256), 0, stream, v, n, n_pad,
-                       vt);
+    const int n_img = (n + kB - 1) / kB * 2;
+    hipLaunchKernelGGL(v_transpose_kernel, dim3(n_img, hkv), dim3(256), 0, stream, v, n, n_img, vt);
     return hipGetLastError();
 }
 
