@@ -91,6 +91,46 @@ def cpu_baseline(inp, plan_pairs, nb, hq, hkv, n, rows_per_head=2):
     }
 
 
+def crossover(args):
+    """Where sparse prefill starts to beat dense attention (the context-length
+    gate of Sec. 5.3, "Short contexts"): crisp_prefill (route + select +
+    attend) against crisp_attend_dense on the headline head mix at growing n.
+    Prints one JSON line."""
+    import torch
+    from dynamic_sparse_attention_map_amd import crisp, synth
+
+    rows = []
+    for n in (1024, 2048, 4096, 8192, 16384, 32768, 65536):
+        spec = synth.config_spec(WORKLOAD, n=n)
+        inp = synth.generate(spec, threads=16)
+        q, k, v = inp.q.cuda(), inp.k.cuda(), inp.v.cuda()
+        ws = crisp.alloc_workspace(n, spec.hq, spec.hkv)
+        out = torch.empty_like(q)
+
+        def timed(fn, reps=10):
+            for _ in range(3):
+                fn()
+            ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                  for _ in range(reps)]
+            for e0, e1 in ev:
+                e0.record()
+                fn()
+                e1.record()
+            torch.cuda.synchronize()
+            return sorted(e0.elapsed_time(e1) for e0, e1 in ev)[reps // 2]
+
+        sp = timed(lambda: crisp.crisp_prefill(q, k, v, args.alpha, ws, out))
+        de = timed(lambda: crisp.crisp_attend_dense(q, k, v, ws, out))
+        rows.append({"n": n, "prefill_ms": round(sp, 4), "dense_ms": round(de, 4),
+                     "speedup": round(de / sp, 3)})
+        log(f"crossover n={n}: prefill {sp:.4f} ms, dense {de:.4f} ms, x{de / sp:.2f}")
+        del q, k, v, ws, out, inp
+    faster = [r["n"] for r in rows if r["speedup"] > 1.0]
+    print(json.dumps({"metric": "sparse_vs_dense_crossover", "workload": WORKLOAD + " head mix",
+                      "alpha": args.alpha, "rows": rows,
+                      "first_n_sparse_faster": faster[0] if faster else None}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -103,6 +143,8 @@ def main():
                     help="skip the FlexPrefill-baseline timing")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="end with a 1 GiB device-to-device copy (reference for counter runs)")
+    ap.add_argument("--crossover", action="store_true",
+                    help="only sweep n for the sparse/dense crossover and print it")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: every step is per query head and this build runs "
@@ -114,6 +156,9 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     crisp.lib()
+    if args.crossover:
+        crossover(args)
+        return
     spec = synth.config_spec(WORKLOAD)
     n, hq, hkv = spec.n, spec.hq, spec.hkv
     nb = -(-n // B)

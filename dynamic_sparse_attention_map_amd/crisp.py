@@ -32,7 +32,18 @@ class CrispError(RuntimeError):
 class crisp_opts(C.Structure):
     _fields_ = [("tau_proxy", C.c_float), ("gamma", C.c_float), ("k_min_tokens", C.c_int),
                 ("w_sink", C.c_int), ("w_local", C.c_int), ("router", C.c_int),
-                ("tau_jsd", C.c_float), ("vs_rule", C.c_int), ("gamma_vs", C.c_float)]
+                ("tau_jsd", C.c_float), ("vs_rule", C.c_int), ("gamma_vs", C.c_float),
+                ("dense_below_tokens", C.c_int)]
+
+
+class crisp_seq(C.Structure):
+    _fields_ = [("q", C.c_void_p), ("k", C.c_void_p), ("v", C.c_void_p), ("out", C.c_void_p),
+                ("seq_len", C.c_int)]
+
+
+class crisp_strides(C.Structure):
+    _fields_ = [(n, C.c_int64) for n in ("q_head", "q_token", "k_head", "k_token", "v_head",
+                                         "v_token", "out_head", "out_token")]
 
 
 ROUTER_CSTRUCT, ROUTER_JSD = 0, 1
@@ -73,11 +84,13 @@ def lib():
         L.crisp_attend.argtypes = [P, P, P, P, P, i, i, i, i, i, P, sz, P, P]
         L.crisp_attend_dense.argtypes = [P, P, P, i, i, i, i, i, P, sz, P, P]
         L.crisp_prefill.argtypes = [P, P, P, i, i, i, i, i, f, P, P, sz, P, P]
+        L.crisp_prefill_batch.argtypes = [P, i, P, i, i, i, i, f, P, P, sz, P]
         L.crisp_set_stage_events.argtypes = [P, i]
         L.crisp_default_opts.argtypes = [P]
         L.crisp_default_opts.restype = None
         for name in ("crisp_workspace_size", "crisp_route", "crisp_select", "crisp_attend",
-                     "crisp_attend_dense", "crisp_prefill", "crisp_set_stage_events"):
+                     "crisp_attend_dense", "crisp_prefill", "crisp_prefill_batch",
+                     "crisp_set_stage_events"):
             getattr(L, name).restype = i
         _lib = L
     return _lib
@@ -170,6 +183,68 @@ def crisp_prefill(q, k, v, alpha, ws, out, opts=None, block_size=128, stream=Non
     _check(lib().crisp_prefill(_ptr(q), _ptr(k), _ptr(v), n, hq, hkv, d, block_size, float(alpha),
                                _opts(opts), _ptr(ws), ws.numel(), _ptr(out), _stream(stream)),
            "crisp_prefill")
+
+
+def crisp_prefill_batch(qs, ks, vs, outs, alpha, ws, opts=None, block_size=128, stream=None):
+    """Several sequences in one call.  qs, ks, vs, outs: lists of
+    [heads, seq_len, head_dim] tensors.  Either every tensor is contiguous
+    (strides NULL: each sequence [heads][seq_len][head_dim]) or all share one
+    head and token stride per operand (head_dim contiguous).  The workspace
+    must fit the longest sequence."""
+    batch = len(qs)
+    if not (len(ks) == len(vs) == len(outs) == batch):
+        raise ValueError("qs, ks, vs, outs must have the same length")
+    if batch == 0:
+        _check(lib().crisp_prefill_batch(None, 0, None, 1, 1, 128, block_size, float(alpha),
+                                         _opts(opts), _ptr(ws), ws.numel(), _stream(stream)),
+               "crisp_prefill_batch")
+        return
+    hq, hkv, d = qs[0].shape[0], ks[0].shape[0], qs[0].shape[2]
+    if all(t.dim() == 3 and t.is_contiguous() for t in (*qs, *ks, *vs, *outs)):
+        arr = (crisp_seq * batch)()
+        for b in range(batch):
+            n = qs[b].shape[1]
+            if ks[b].shape[1] != n or vs[b].shape[1] != n or outs[b].shape[1] != n:
+                raise ValueError("q, k, v, out of a sequence must have the same length")
+            arr[b] = crisp_seq(qs[b].data_ptr(), ks[b].data_ptr(), vs[b].data_ptr(),
+                               outs[b].data_ptr(), n)
+        _check(lib().crisp_prefill_batch(arr, batch, None, hq, hkv, d, block_size, float(alpha),
+                                         _opts(opts), _ptr(ws), ws.numel(), _stream(stream)),
+               "crisp_prefill_batch")
+        return
+    st = crisp_strides(qs[0].stride(0), qs[0].stride(1), ks[0].stride(0), ks[0].stride(1),
+                       vs[0].stride(0), vs[0].stride(1), outs[0].stride(0), outs[0].stride(1))
+    arr = (crisp_seq * batch)()
+    for b in range(batch):
+        views = (qs[b], ks[b], vs[b], outs[b])
+        for t, (sh, stk) in zip(views, ((st.q_head, st.q_token), (st.k_head, st.k_token),
+                                        (st.v_head, st.v_token), (st.out_head, st.out_token))):
+            if t.dim() != 3 or t.shape[2] != d or t.stride(2) != 1:
+                raise ValueError("each tensor must be a [heads, seq_len, head_dim] view with "
+                                 "contiguous head_dim")
+            if t.shape[1] > 1 and t.stride(1) != stk or t.shape[0] > 1 and t.stride(0) != sh:
+                raise ValueError("all sequences must share the same strides")
+        n = qs[b].shape[1]
+        if ks[b].shape[1] != n or vs[b].shape[1] != n or outs[b].shape[1] != n:
+            raise ValueError("q, k, v, out of a sequence must have the same length")
+        if qs[b].shape[0] != hq or ks[b].shape[0] != hkv or outs[b].shape[0] != hq:
+            raise ValueError("head counts must match across the batch")
+        arr[b] = crisp_seq(qs[b].data_ptr(), ks[b].data_ptr(), vs[b].data_ptr(),
+                           outs[b].data_ptr(), n)
+    _check(lib().crisp_prefill_batch(arr, batch, C.byref(st), hq, hkv, d, block_size, float(alpha),
+                                     _opts(opts), _ptr(ws), ws.numel(), _stream(stream)),
+           "crisp_prefill_batch")
+
+
+def prefill_varlen(q, k, v, cu_seqlens, out, alpha, ws, opts=None, stream=None):
+    """Packed variable-length batch: q, out [total, heads, head_dim] and k, v
+    [total, kv_heads, head_dim]; sequence b holds tokens
+    cu_seqlens[b] .. cu_seqlens[b+1] (a host sequence of ints)."""
+    cu = [int(x) for x in cu_seqlens]
+    sl = [slice(cu[b], cu[b + 1]) for b in range(len(cu) - 1)]
+    crisp_prefill_batch([q[s].transpose(0, 1) for s in sl], [k[s].transpose(0, 1) for s in sl],
+                        [v[s].transpose(0, 1) for s in sl], [out[s].transpose(0, 1) for s in sl],
+                        alpha, ws, opts=opts, stream=stream)
 
 
 def crisp_set_stage_events(events):

@@ -67,11 +67,10 @@ __device__ __forceinline__ void wait_copies()
 // being blocks Nb-1-2p and Nb-2-2p.  Each XCD keeps whole GQA groups (sharing
 // K/V in its L2) and walks the pairs from the longest causal rows down.
 __device__ __forceinline__ void
-attend_pair(int b, uint16_t* lds, uint32_t* list, const uint16_t* __restrict__ q,
-            const uint16_t* __restrict__ k,
+attend_pair(int b, uint16_t* lds, uint32_t* list, Rows q, Rows k,
             const uint16_t* __restrict__ vt, const int32_t* __restrict__ row_ptr,
             const int32_t* __restrict__ col_idx, int n, int nb, int hkv, int G,
-            float scale_log2, uint16_t* __restrict__ out)
+            float scale_log2, OutRows out)
 {
     const int npairs = (nb + 1) >> 1;
     const int slot = b >> 3;
@@ -150,17 +149,17 @@ attend_pair(int b, uint16_t* lds, uint32_t* list, const uint16_t* __restrict__ q
     // (their results are never stored)
     const int qpos = (active ? myqb : 0) * kB + qc;
     const bool q_valid = active && qpos < n;
-    const size_t qrow = (size_t)h * n + min(qpos, n - 1);
+    const uint16_t* qrow = q.row(h, min(qpos, n - 1));
     bf16x8 qf[8];
     for (int s = 0; s < 8; ++s)
-        qf[s] = *reinterpret_cast<const bf16x8*>(q + qrow * kD + 16 * s + 8 * hi);
+        qf[s] = *reinterpret_cast<const bf16x8*>(qrow + 16 * s + 8 * hi);
 
     f32x16 o[4];
     for (int dt = 0; dt < 4; ++dt) o[dt] = f32x16{};
     float m_run = -INFINITY, l_run = 0.f;
     const float rescale_gap = 8.0f / scale_log2;   // 2^8 in probability
 
-    const uint16_t* kg = k + (size_t)g * n * kD;
+    const uint16_t* kg = k.row(g, 0);
     // V^T sub-tile images of this KV head, 2 per key block
     const uint16_t* vg = vt + (size_t)g * nb * (2 * kImg);
 
@@ -172,12 +171,13 @@ attend_pair(int b, uint16_t* lds, uint32_t* list, const uint16_t* __restrict__ q
     //   V^T  [128 d][8 chunks]:     chunk c of row d at slot c ^ ((d >> 1) & 7)
     // K is swizzled by the per-lane source address; V^T is stored in HBM as
     // these images already (v_transpose_kernel), so its copy is contiguous.
-    int k_row[2];
-    uint32_t k_src[2];
+    int k_row[2], k_col[2];
+    long long k_src[2];
     for (int j = 0; j < 2; ++j) {
         const int ci = 2 * w + j;                       // 1 KiB chunk of the image
         k_row[j] = 4 * ci + (lane >> 4);
-        k_src[j] = (uint32_t)(k_row[j] * kD + 8 * ((lane & 15) ^ (k_row[j] & 15)));
+        k_col[j] = 8 * ((lane & 15) ^ (k_row[j] & 15));
+        k_src[j] = k_row[j] * k.st + k_col[j];
     }
     const uint32_t lds_base = (uint32_t)(uintptr_t)(
         (__attribute__((address_space(3))) uint16_t*)lds);
@@ -185,13 +185,13 @@ attend_pair(int b, uint16_t* lds, uint32_t* list, const uint16_t* __restrict__ q
         const int kb = (int)(dsc & 0xffffu), sub = t & 1;
         const int key0 = kb * kB + sub * kKT;
         const uint32_t sb = lds_base + (uint32_t)((t & 3) * kStageBytes) + 2048u * w;
-        const uint16_t* kt = kg + (size_t)key0 * kD;
+        const uint16_t* kt = kg + key0 * k.st;
         const bool full = key0 + kKT <= n;
         for (int j = 0; j < 2; ++j) {
             // keys past the end of a partial last block repeat the last key
             // (every query that exists masks them: they lie in its future)
             const uint16_t* src = full ? kt + k_src[j]
-                                       : kg + (size_t)min(key0 + k_row[j], n - 1) * kD + (k_src[j] % kD);
+                                       : kg + min(key0 + k_row[j], n - 1) * k.st + k_col[j];
             copy16_to_lds(src, sb + 1024u * j);
         }
         const uint16_t* vimg = vg + (size_t)(2 * kb + sub) * kImg + 1024 * w + 8 * lane;
@@ -367,7 +367,7 @@ attend_pair(int b, uint16_t* lds, uint32_t* list, const uint16_t* __restrict__ q
     const float l = l_run + swap_half(l_run);
     if (!q_valid) return;             // after the wave-wide exchange above
     const float inv = (l > 0.f) ? 1.0f / l : 0.f;
-    uint16_t* orow = out + qrow * kD;
+    uint16_t* orow = out.row(h, qpos);
     for (int dt = 0; dt < 4; ++dt)
         for (int j = 0; j < 4; ++j) {
             bf16x4 v4;
@@ -381,10 +381,10 @@ attend_pair(int b, uint16_t* lds, uint32_t* list, const uint16_t* __restrict__ q
 // on XCD b % 8) and moves to the others once that one is empty.  ctr[x]
 // counts items taken from queue x and must be zero at launch.
 __global__ void __launch_bounds__(kThreads)
-attend_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+attend_kernel(Rows q, Rows k,
               const uint16_t* __restrict__ vt, const int32_t* __restrict__ row_ptr,
               const int32_t* __restrict__ col_idx, int n, int nb, int hkv, int G,
-              float scale_log2, int per_xcd, int* __restrict__ ctr, uint16_t* __restrict__ out)
+              float scale_log2, int per_xcd, int* __restrict__ ctr, OutRows out)
 {
     __shared__ __attribute__((aligned(1024))) uint16_t lds[kStages * kStageBytes / 2];
     __shared__ uint32_t list[2 * kListWords + kMaxBlocks + 1];
@@ -424,16 +424,16 @@ __global__ void zero_counters_kernel(int* __restrict__ ctr)
 // then one 16-byte chunk.  Keys past n are zero.
 // grid (N_b * 2, hkv), 256 threads.
 __global__ void __launch_bounds__(256)
-v_transpose_kernel(const uint16_t* __restrict__ v, int n, int n_img, uint16_t* __restrict__ vt)
+v_transpose_kernel(Rows v, int n, int n_img, uint16_t* __restrict__ vt)
 {
     __shared__ uint16_t tile[64][kD + 8];
     const int g = blockIdx.y, key0 = blockIdx.x * 64, tid = threadIdx.x;
-    const uint16_t* src = v + ((size_t)g * n + key0) * kD;
+    const uint16_t* src = v.row(g, key0);
     for (int i = 0; i < 4; ++i) {
         const int e = tid + 256 * i;
         const int row = e >> 4, ch = e & 15;
         u32x4 val = {0u, 0u, 0u, 0u};
-        if (key0 + row < n) val = *reinterpret_cast<const u32x4*>(src + (size_t)row * kD + 8 * ch);
+        if (key0 + row < n) val = *reinterpret_cast<const u32x4*>(src + row * v.st + 8 * ch);
         *reinterpret_cast<u32x4*>(&tile[row][8 * ch]) = val;
     }
     __syncthreads();
@@ -453,16 +453,16 @@ v_transpose_kernel(const uint16_t* __restrict__ v, int n, int n_img, uint16_t* _
 
 }  // namespace
 
-hipError_t launch_v_transpose(const uint16_t* v, int n, int hkv, uint16_t* vt, hipStream_t stream)
+hipError_t launch_v_transpose(Rows v, int n, int hkv, uint16_t* vt, hipStream_t stream)
 {
     const int n_img = (n + kB - 1) / kB * 2;
     hipLaunchKernelGGL(v_transpose_kernel, dim3(n_img, hkv), dim3(256), 0, stream, v, n, n_img, vt);
     return hipGetLastError();
 }
 
-hipError_t launch_attend(const uint16_t* q, const uint16_t* k, const uint16_t* vt,
+hipError_t launch_attend(Rows q, Rows k, const uint16_t* vt,
                          const int32_t* row_ptr, const int32_t* col_idx, int n, int hq, int hkv,
-                         int* counters, uint16_t* out, hipStream_t stream)
+                         int* counters, OutRows out, hipStream_t stream)
 {
     const int nb = (n + kB - 1) / kB, G = hq / hkv;
     const long long chunks = (long long)((nb + 1) / 2) * hkv;

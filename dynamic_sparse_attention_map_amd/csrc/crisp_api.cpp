@@ -107,11 +107,11 @@ bool bad_ptr(const void* p, size_t align = 16)
 
 struct Opts {
     float tau, gamma, tau_jsd, gamma_vs;
-    int kmin_blocks, router, vs_rule;
+    int kmin_blocks, router, vs_rule, dense_below;
 };
 
 constexpr crisp_opts kDefaults = {0.2f, 0.95f, 1024, kB, kB, CRISP_ROUTER_CSTRUCT, 0.1f,
-                                  CRISP_VS_NOISE_MEAN, 0.95f};
+                                  CRISP_VS_NOISE_MEAN, 0.95f, 0};
 
 int check_opts(const crisp_opts* o, Opts* out)
 {
@@ -122,6 +122,7 @@ int check_opts(const crisp_opts* o, Opts* out)
     if (d.k_min_tokens < 0 || d.k_min_tokens % kB != 0) return CRISP_ERR_INVALID_ARG;
     if (d.router != CRISP_ROUTER_CSTRUCT && d.router != CRISP_ROUTER_JSD) return CRISP_ERR_INVALID_ARG;
     if (d.vs_rule < CRISP_VS_NOISE_MEAN || d.vs_rule > CRISP_VS_GAMMA) return CRISP_ERR_INVALID_ARG;
+    if (d.dense_below_tokens < 0) return CRISP_ERR_INVALID_ARG;
     if (d.w_sink != kB || d.w_local != kB) return CRISP_ERR_UNSUPPORTED;
     out->tau = d.tau_proxy;
     out->gamma = d.gamma;
@@ -130,7 +131,24 @@ int check_opts(const crisp_opts* o, Opts* out)
     out->kmin_blocks = d.k_min_tokens / kB;
     out->router = d.router;
     out->vs_rule = d.vs_rule;
+    out->dense_below = d.dense_below_tokens;
     return CRISP_OK;
+}
+
+// Q, K, V and the output of one sequence with their strides.
+struct Operands {
+    Rows q, k, v;
+    OutRows out;
+};
+
+// [H][n][128] contiguous
+Rows packed(const void* p, int n)
+{
+    return Rows{static_cast<const uint16_t*>(p), (long long)n * kD, kD};
+}
+OutRows packed_out(void* p, int n)
+{
+    return OutRows{static_cast<uint16_t*>(p), (long long)n * kD, kD};
 }
 
 thread_local hipEvent_t g_events[5];
@@ -149,7 +167,7 @@ T* at(void* ws, size_t off)
     return reinterpret_cast<T*>(static_cast<char*>(ws) + off);
 }
 
-int do_route(const Shape& s, const Opts& op, const void* q, const void* k, void* ws,
+int do_route(const Shape& s, const Opts& op, Rows q, Rows k, void* ws,
              const Layout& L, uint8_t* pattern, float* c_struct, float* p_v, float* p_s,
              hipStream_t stream)
 {
@@ -161,11 +179,10 @@ int do_route(const Shape& s, const Opts& op, const void* q, const void* k, void*
     ra.part_up = at<float>(ws, L.part_up);
     ra.jsd_kbar = at<float>(ws, L.jsd_kbar);
     ra.jsd_qbar = at<float>(ws, L.jsd_qbar);
-    return hip_status(launch_route(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
-                                   s.n, s.hq, s.hkv, ra, p_v, p_s, c_struct, pattern, stream));
+    return hip_status(launch_route(q, k, s.n, s.hq, s.hkv, ra, p_v, p_s, c_struct, pattern, stream));
 }
 
-int do_select(const Shape& s, const Opts& op, float alpha, const void* q, const void* k,
+int do_select(const Shape& s, const Opts& op, float alpha, Rows q, Rows k,
               const uint8_t* pattern, const float* p_v, const float* p_s, void* ws,
               const Layout& L, int32_t* sel_v, int32_t* sel_s, int32_t* counts,
               int32_t* row_ptr, int32_t* col_idx, hipStream_t stream)
@@ -183,24 +200,53 @@ int do_select(const Shape& s, const Opts& op, float alpha, const void* q, const 
     vr.alpha = alpha;
     vr.gamma_vs = op.gamma_vs;
     vr.kmin_blocks = op.kmin_blocks;
-    return hip_status(launch_select(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
-                                    pattern, p_v, p_s, s.n, s.hq, s.hkv, vr, op.gamma, sc, sel_v,
-                                    sel_s, counts, row_ptr, col_idx, stream));
+    return hip_status(launch_select(q, k, pattern, p_v, p_s, s.n, s.hq, s.hkv, vr, op.gamma, sc,
+                                    sel_v, sel_s, counts, row_ptr, col_idx, stream));
 }
 
-int do_attend(const Shape& s, const void* q, const void* k, const void* v, const int32_t* row_ptr,
-              const int32_t* col_idx, void* ws, const Layout& L, void* out, hipStream_t stream)
+int do_attend(const Shape& s, const Operands& x, const int32_t* row_ptr, const int32_t* col_idx,
+              void* ws, const Layout& L, hipStream_t stream)
 {
     uint16_t* vt = at<uint16_t>(ws, L.vt);
     mark(2, stream);
-    hipError_t e = launch_v_transpose(static_cast<const uint16_t*>(v), s.n, s.hkv, vt, stream);
+    hipError_t e = launch_v_transpose(x.v, s.n, s.hkv, vt, stream);
     if (e != hipSuccess) return CRISP_ERR_HIP;
     mark(3, stream);
-    e = launch_attend(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), vt, row_ptr,
-                      col_idx, s.n, s.hq, s.hkv, at<int>(ws, L.queue), static_cast<uint16_t*>(out),
+    e = launch_attend(x.q, x.k, vt, row_ptr, col_idx, s.n, s.hq, s.hkv, at<int>(ws, L.queue), x.out,
                       stream);
     mark(4, stream);
     return hip_status(e);
+}
+
+// Alg. 1 for one sequence: route, select, attend; or, below the gating
+// length, dense causal attention alone.
+int run_prefill(const Shape& s, const Opts& op, float alpha, const Operands& x, void* ws,
+                const Layout& L, hipStream_t st)
+{
+    if (s.n < op.dense_below) {
+        mark(0, st);
+        mark(1, st);
+        return do_attend(s, x, nullptr, nullptr, ws, L, st);
+    }
+    uint8_t* pattern = at<uint8_t>(ws, L.pattern);
+    float* p_v = at<float>(ws, L.p_v);
+    float* p_s = at<float>(ws, L.p_s);
+    int32_t* row_ptr = at<int32_t>(ws, L.row_ptr);
+    int32_t* col_idx = at<int32_t>(ws, L.col_idx);
+    mark(0, st);
+    int rc = do_route(s, op, x.q, x.k, ws, L, pattern, at<float>(ws, L.c_struct), p_v, p_s, st);
+    if (rc) return rc;
+    mark(1, st);
+    rc = do_select(s, op, alpha, x.q, x.k, pattern, p_v, p_s, ws, L, at<int32_t>(ws, L.sel_v),
+                   at<int32_t>(ws, L.sel_s), at<int32_t>(ws, L.counts), row_ptr, col_idx, st);
+    if (rc) return rc;
+    return do_attend(s, x, row_ptr, col_idx, ws, L, st);
+}
+
+// element strides: positive, rows 16-byte aligned
+bool bad_strides(long long sh, long long st)
+{
+    return sh <= 0 || st <= 0 || sh % 8 != 0 || st % 8 != 0;
 }
 
 }  // namespace
@@ -270,7 +316,7 @@ int crisp_route(const void* q, const void* k, int seq_len, int n_heads, int n_kv
     if (ws_bytes < L.route_end) return CRISP_ERR_WORKSPACE;
     hipStream_t st = static_cast<hipStream_t>(stream);
     mark(0, st);
-    rc = do_route(s, op, q, k, ws, L, pattern, c_struct, p_v, p_s, st);
+    rc = do_route(s, op, packed(q, s.n), packed(k, s.n), ws, L, pattern, c_struct, p_v, p_s, st);
     mark(1, st);
     return rc;
 }
@@ -296,8 +342,8 @@ int crisp_select(const void* q, const void* k, const uint8_t* pattern, const flo
     if (ws_bytes < L.select_end || csr_capacity < L.csr_capacity) return CRISP_ERR_WORKSPACE;
     hipStream_t st = static_cast<hipStream_t>(stream);
     mark(1, st);
-    rc = do_select(s, op, alpha, q, k, pattern, p_v, p_s, ws, L, sel_v, sel_s, sel_counts, row_ptr,
-                   col_idx, st);
+    rc = do_select(s, op, alpha, packed(q, s.n), packed(k, s.n), pattern, p_v, p_s, ws, L, sel_v,
+                   sel_s, sel_counts, row_ptr, col_idx, st);
     mark(2, st);
     return rc;
 }
@@ -315,7 +361,8 @@ int crisp_attend(const void* q, const void* k, const void* v, const int32_t* row
         return CRISP_ERR_INVALID_ARG;
     const Layout L = make_layout(s);
     if (ws_bytes < L.attend_end) return CRISP_ERR_WORKSPACE;
-    return do_attend(s, q, k, v, row_ptr, col_idx, ws, L, out, static_cast<hipStream_t>(stream));
+    const Operands x{packed(q, s.n), packed(k, s.n), packed(v, s.n), packed_out(out, s.n)};
+    return do_attend(s, x, row_ptr, col_idx, ws, L, static_cast<hipStream_t>(stream));
 }
 
 int crisp_attend_dense(const void* q, const void* k, const void* v, int seq_len, int n_heads,
@@ -330,7 +377,8 @@ int crisp_attend_dense(const void* q, const void* k, const void* v, int seq_len,
         return CRISP_ERR_INVALID_ARG;
     const Layout L = make_layout(s);
     if (ws_bytes < L.attend_end) return CRISP_ERR_WORKSPACE;
-    return do_attend(s, q, k, v, nullptr, nullptr, ws, L, out, static_cast<hipStream_t>(stream));
+    const Operands x{packed(q, s.n), packed(k, s.n), packed(v, s.n), packed_out(out, s.n)};
+    return do_attend(s, x, nullptr, nullptr, ws, L, static_cast<hipStream_t>(stream));
 }
 
 int crisp_prefill(const void* q, const void* k, const void* v, int seq_len, int n_heads,
@@ -348,20 +396,53 @@ int crisp_prefill(const void* q, const void* k, const void* v, int seq_len, int 
         return CRISP_ERR_INVALID_ARG;
     const Layout L = make_layout(s);
     if (ws_bytes < L.total) return CRISP_ERR_WORKSPACE;
-    hipStream_t st = static_cast<hipStream_t>(stream);
-    uint8_t* pattern = at<uint8_t>(ws, L.pattern);
-    float* p_v = at<float>(ws, L.p_v);
-    float* p_s = at<float>(ws, L.p_s);
-    int32_t* row_ptr = at<int32_t>(ws, L.row_ptr);
-    int32_t* col_idx = at<int32_t>(ws, L.col_idx);
-    mark(0, st);
-    rc = do_route(s, op, q, k, ws, L, pattern, at<float>(ws, L.c_struct), p_v, p_s, st);
+    const Operands x{packed(q, s.n), packed(k, s.n), packed(v, s.n), packed_out(out, s.n)};
+    return run_prefill(s, op, alpha, x, ws, L, static_cast<hipStream_t>(stream));
+}
+
+int crisp_prefill_batch(const crisp_seq* seqs, int batch, const crisp_strides* strides,
+                        int n_heads, int n_kv_heads, int head_dim, int block_size, float alpha,
+                        const crisp_opts* opts, void* ws, size_t ws_bytes, void* stream)
+{
+    if (batch < 0 || (batch > 0 && seqs == nullptr)) return CRISP_ERR_INVALID_ARG;
+    Opts op;
+    int rc = check_opts(opts, &op);
     if (rc) return rc;
-    mark(1, st);
-    rc = do_select(s, op, alpha, q, k, pattern, p_v, p_s, ws, L, at<int32_t>(ws, L.sel_v),
-                   at<int32_t>(ws, L.sel_s), at<int32_t>(ws, L.counts), row_ptr, col_idx, st);
-    if (rc) return rc;
-    return do_attend(s, q, k, v, row_ptr, col_idx, ws, L, out, st);
+    if (!std::isfinite(alpha) || alpha < 0.0f) return CRISP_ERR_INVALID_ARG;
+    if (strides && (bad_strides(strides->q_head, strides->q_token) ||
+                    bad_strides(strides->k_head, strides->k_token) ||
+                    bad_strides(strides->v_head, strides->v_token) ||
+                    bad_strides(strides->out_head, strides->out_token)))
+        return CRISP_ERR_INVALID_ARG;
+    // validate every sequence before the first launch
+    for (int b = 0; b < batch; ++b) {
+        Shape s;
+        if ((rc = check_shape(seqs[b].seq_len, n_heads, n_kv_heads, head_dim, block_size, &s)))
+            return rc;
+        if (s.n == 0) continue;
+        if (bad_ptr(seqs[b].q) || bad_ptr(seqs[b].k) || bad_ptr(seqs[b].v) || bad_ptr(seqs[b].out) ||
+            bad_ptr(ws, kAlign))
+            return CRISP_ERR_INVALID_ARG;
+        if (ws_bytes < make_layout(s).total) return CRISP_ERR_WORKSPACE;
+    }
+    const hipStream_t st = static_cast<hipStream_t>(stream);
+    for (int b = 0; b < batch; ++b) {
+        Shape s;
+        (void)check_shape(seqs[b].seq_len, n_heads, n_kv_heads, head_dim, block_size, &s);
+        if (s.n == 0) continue;
+        Operands x;
+        if (strides) {
+            x.q = Rows{static_cast<const uint16_t*>(seqs[b].q), strides->q_head, strides->q_token};
+            x.k = Rows{static_cast<const uint16_t*>(seqs[b].k), strides->k_head, strides->k_token};
+            x.v = Rows{static_cast<const uint16_t*>(seqs[b].v), strides->v_head, strides->v_token};
+            x.out = OutRows{static_cast<uint16_t*>(seqs[b].out), strides->out_head, strides->out_token};
+        } else {
+            x = Operands{packed(seqs[b].q, s.n), packed(seqs[b].k, s.n), packed(seqs[b].v, s.n),
+                         packed_out(seqs[b].out, s.n)};
+        }
+        if ((rc = run_prefill(s, op, alpha, x, ws, make_layout(s), st))) return rc;
+    }
+    return CRISP_OK;
 }
 
 }  // extern "C"

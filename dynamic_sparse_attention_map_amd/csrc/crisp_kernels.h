@@ -10,6 +10,19 @@ constexpr int kD = 128;            // head_dim
 constexpr int kB = 128;            // block size B (tokens per block)
 constexpr int kMaxBlocks = 4096;   // largest N_b (seq_len 524288 at B = 128)
 
+// A bf16 operand [heads][tokens][128] with arbitrary head and token strides
+// in elements; the 128 head-dimension values of one row are contiguous.
+struct Rows {
+    const uint16_t* p;
+    long long sh, st;               // head stride, token stride
+    __host__ __device__ const uint16_t* row(int h, long long i) const { return p + h * sh + i * st; }
+};
+struct OutRows {
+    uint16_t* p;
+    long long sh, st;
+    __host__ __device__ uint16_t* row(int h, long long i) const { return p + h * sh + i * st; }
+};
+
 // Per-head state of the PE radix select (device memory, 64 bytes).
 struct PeState {
     unsigned long long need;        // fixed-point mass still to cover
@@ -38,7 +51,7 @@ struct RouteArgs {
     float* jsd_qbar;                // [hq][128] mean representative query (router 1)
 };
 
-hipError_t launch_route(const uint16_t* q, const uint16_t* k, int n, int hq, int hkv,
+hipError_t launch_route(Rows q, Rows k, int n, int hq, int hkv,
                         const RouteArgs& a, float* p_v, float* p_s, float* c_struct,
                         uint8_t* pattern, hipStream_t stream);
 
@@ -59,18 +72,18 @@ struct SelectScratch {
     uint8_t* bitmap;                // [hq][2][Nb]
 };
 
-hipError_t launch_select(const uint16_t* q, const uint16_t* k, const uint8_t* pattern,
+hipError_t launch_select(Rows q, Rows k, const uint8_t* pattern,
                          const float* p_v, const float* p_s, int n, int hq, int hkv,
                          const VsRule& vs, float gamma, const SelectScratch& s, int32_t* sel_v,
                          int32_t* sel_s, int32_t* sel_counts, int32_t* row_ptr, int32_t* col_idx,
                          hipStream_t stream);
 
-hipError_t launch_v_transpose(const uint16_t* v, int n, int hkv, uint16_t* vt, hipStream_t stream);
+hipError_t launch_v_transpose(Rows v, int n, int hkv, uint16_t* vt, hipStream_t stream);
 
 // row_ptr / col_idx == nullptr: dense causal lists.
 // counters: 8 ints of device scratch (zeroed by the launch itself).
-hipError_t launch_attend(const uint16_t* q, const uint16_t* k, const uint16_t* vt,
+hipError_t launch_attend(Rows q, Rows k, const uint16_t* vt,
                          const int32_t* row_ptr, const int32_t* col_idx, int n, int hq, int hkv,
-                         int* counters, uint16_t* out, hipStream_t stream);
+                         int* counters, OutRows out, hipStream_t stream);
 
 }  // namespace crisp

@@ -35,7 +35,7 @@ constexpr int kKRow = kD + 8;   // LDS row pitch of a K tile (bf16): 272 bytes
 // split column and the causal cut are compile-time per (chunk, key group).
 template <bool Aligned>
 __global__ void __launch_bounds__(256)
-proxy_map_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, int n, int nb,
+proxy_map_kernel(Rows q, Rows k, int n, int nb,
                  int G, int tiles_per_wg, float scale_log2,
                  float* __restrict__ part_m, float* __restrict__ part_lo,
                  float* __restrict__ part_up)
@@ -59,16 +59,16 @@ proxy_map_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     // (rows past R, which exist only when n < B, repeat the last row)
     bf16x8 qf[4][8];
     {
-        const uint16_t* qh = q + ((size_t)h * n + q0) * kD;
+        const uint16_t* qh = q.row(h, q0);
 #pragma unroll
         for (int c = 0; c < 4; ++c)
 #pragma unroll
             for (int s = 0; s < 8; ++s)
                 qf[c][s] = *reinterpret_cast<const bf16x8*>(
-                    qh + (size_t)min(32 * c + l32, R - 1) * kD + 16 * s + 8 * hi);
+                    qh + min(32 * c + l32, R - 1) * q.st + 16 * s + 8 * hi);
     }
 
-    const uint16_t* kg = k + (size_t)kv * n * kD;
+    const uint16_t* kg = k.row(kv, 0);
     const int t0 = blockIdx.x * tiles_per_wg;
     const int t1 = min(nb, t0 + tiles_per_wg);
     for (int t = t0; t < t1; ++t) {
@@ -79,14 +79,14 @@ proxy_map_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
             for (int e = threadIdx.x; e < kTileKeys * (kD / 8); e += 256) {
                 const int row = e >> 4, ch = e & 15;
                 *reinterpret_cast<u32x4*>(&ks[row * kKRow + 8 * ch]) =
-                    *reinterpret_cast<const u32x4*>(kg + ((size_t)t * kTileKeys + row) * kD + 8 * ch);
+                    *reinterpret_cast<const u32x4*>(kg + ((long long)t * kTileKeys + row) * k.st + 8 * ch);
             }
         } else {
             for (int e = threadIdx.x; e < kTileKeys * (kD / 8); e += 256) {
                 const int row = e >> 4, ch = e & 15;
-                const size_t key = (size_t)t * kTileKeys + row;
+                const long long key = (long long)t * kTileKeys + row;
                 u32x4 val = {0u, 0u, 0u, 0u};
-                if (key < (size_t)n) val = *reinterpret_cast<const u32x4*>(kg + key * kD + 8 * ch);
+                if (key < n) val = *reinterpret_cast<const u32x4*>(kg + key * k.st + 8 * ch);
                 *reinterpret_cast<u32x4*>(&ks[row * kKRow + 8 * ch]) = val;
             }
         }
@@ -258,28 +258,31 @@ mass_reduce_kernel(const float* __restrict__ part_m, const float* __restrict__ p
 // y over the tokens it holds; y >= hkv (x == 0 only): mean of the R
 // representative query rows of head y - hkv.
 __global__ void __launch_bounds__(256)
-jsd_pool_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, int n, int nb,
+jsd_pool_kernel(Rows q, Rows k, int n, int nb,
                 int hkv, float* __restrict__ kbar, float* __restrict__ qbar)
 {
     __shared__ float red[16][kD];
     const int x = blockIdx.x, y = blockIdx.y, tid = threadIdx.x;
     const uint16_t* src;
+    long long st;
     float* dst;
     int len;
     if (y < hkv) {
         len = min(kB, n - x * kB);
-        src = k + ((size_t)y * n + (size_t)x * kB) * kD;
+        src = k.row(y, (long long)x * kB);
+        st = k.st;
         dst = kbar + ((size_t)y * nb + x) * kD;
     } else {
         if (x != 0) return;
         len = min(kB, n);
-        src = q + ((size_t)(y - hkv) * n + (n - len)) * kD;
+        src = q.row(y - hkv, n - len);
+        st = q.st;
         dst = qbar + (size_t)(y - hkv) * kD;
     }
     const int dc = tid & 15, tg = tid >> 4;
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     for (int t = tg * 8; t < min(tg * 8 + 8, len); ++t) {
-        const u32x4 raw = *reinterpret_cast<const u32x4*>(src + (size_t)t * kD + 8 * dc);
+        const u32x4 raw = *reinterpret_cast<const u32x4*>(src + t * st + 8 * dc);
         for (int e = 0; e < 4; ++e) {
             acc[2 * e] += __uint_as_float(raw[e] << 16);
             acc[2 * e + 1] += __uint_as_float(raw[e] & 0xffff0000u);
@@ -360,7 +363,7 @@ jsd_route_kernel(const float* __restrict__ kbar, const float* __restrict__ qbar,
 
 }  // namespace
 
-hipError_t launch_route(const uint16_t* q, const uint16_t* k, int n, int hq, int hkv,
+hipError_t launch_route(Rows q, Rows k, int n, int hq, int hkv,
                         const RouteArgs& a, float* p_v, float* p_s, float* c_struct,
                         uint8_t* pattern, hipStream_t stream)
 {

@@ -273,7 +273,7 @@ __device__ __forceinline__ bool group_has_pe(const uint8_t* pattern, int g, int 
 // grid (Nb, hq + hkv): block means of Q (PE heads) and K (groups with a PE
 // head), over the tokens each block holds (the last block may be partial).
 __global__ void __launch_bounds__(256)
-pe_pool_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+pe_pool_kernel(Rows q, Rows k,
                const uint8_t* __restrict__ pattern, int n, int hq, int G,
                float* __restrict__ qbar, float* __restrict__ kbar)
 {
@@ -282,21 +282,24 @@ pe_pool_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const int nb = (n + kB - 1) / kB;
     const int len = min(kB, n - qb * kB);           // tokens in block qb
     const uint16_t* src;
+    long long st;
     float* dst;
     if (y < hq) {
         if (pattern[y]) return;
-        src = q + ((size_t)y * n + (size_t)qb * kB) * kD;
+        src = q.row(y, (long long)qb * kB);
+        st = q.st;
         dst = qbar + ((size_t)y * nb + qb) * kD;
     } else {
         const int g = y - hq;
         if (!group_has_pe(pattern, g, G)) return;
-        src = k + ((size_t)g * n + (size_t)qb * kB) * kD;
+        src = k.row(g, (long long)qb * kB);
+        st = k.st;
         dst = kbar + ((size_t)g * nb + qb) * kD;
     }
     const int dc = tid & 15, tg = tid >> 4;
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     for (int t = tg * 8; t < min(tg * 8 + 8, len); ++t) {
-        const u32x4 raw = *reinterpret_cast<const u32x4*>(src + (size_t)t * kD + 8 * dc);
+        const u32x4 raw = *reinterpret_cast<const u32x4*>(src + t * st + 8 * dc);
         for (int e = 0; e < 4; ++e) {
             acc[2 * e] += __uint_as_float(raw[e] << 16);
             acc[2 * e + 1] += __uint_as_float(raw[e] & 0xffff0000u);
@@ -623,7 +626,7 @@ expand_fill_kernel(const uint8_t* __restrict__ pattern, int nb, const uint8_t* _
 
 }  // namespace
 
-hipError_t launch_select(const uint16_t* q, const uint16_t* k, const uint8_t* pattern,
+hipError_t launch_select(Rows q, Rows k, const uint8_t* pattern,
                          const float* p_v, const float* p_s, int n, int hq, int hkv,
                          const VsRule& vs, float gamma, const SelectScratch& s, int32_t* sel_v,
                          int32_t* sel_s, int32_t* sel_counts, int32_t* row_ptr, int32_t* col_idx,

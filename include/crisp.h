@@ -14,6 +14,7 @@
  * Tensors: bf16, contiguous, batch 1.  q is [n_heads][seq_len][head_dim];
  *   k, v are [n_kv_heads][seq_len][head_dim]; query head h reads KV head
  *   h / (n_heads / n_kv_heads) (grouped-query attention).  out has q's shape.
+ *   crisp_prefill_batch alone takes several sequences and strided layouts.
  * Device pointers: every array argument is device memory, 16-byte aligned
  *   (the workspace 256-byte aligned).  opts is a host pointer (may be NULL).
  * Sizes: head_dim == 128 and block_size == 128 (B in the paper); any
@@ -70,7 +71,7 @@ enum crisp_vs_rule {
  * Hyper-parameters (Section 5, "Setup"; Section 3.2; Appendices A and H).
  * NULL selects the defaults crisp_default_opts() writes:
  * {0.2, 0.95, 1024, 128, 128, CRISP_ROUTER_CSTRUCT, 0.1, CRISP_VS_NOISE_MEAN,
- * 0.95}.
+ * 0.95, 0}.
  *   tau_proxy     routing threshold: VS iff C_struct >= tau_proxy (Alg. 2)
  *   gamma         PE coverage target (Alg. 4), in (0, 1]
  *   k_min_tokens  minimum budget per VS direction, in tokens (a multiple of
@@ -81,6 +82,12 @@ enum crisp_vs_rule {
  *   tau_jsd       threshold of CRISP_ROUTER_JSD (not given by the paper; 0.1)
  *   vs_rule       enum crisp_vs_rule
  *   gamma_vs      coverage target of CRISP_VS_GAMMA, in (0, 1]
+ *   dense_below_tokens  context-length gate (Section 5.3, "Short contexts":
+ *                 routing is a fixed cost that outweighs its savings on short
+ *                 sequences): crisp_prefill and crisp_prefill_batch run dense
+ *                 causal attention, skipping routing and selection, for a
+ *                 sequence with seq_len < dense_below_tokens.  >= 0; 0 (the
+ *                 default) never gates.
  * CRISP itself is router 0 with rule 0; router 1 with rule 2 is the
  * FlexPrefill baseline the paper compares against (Appendix A).
  */
@@ -94,6 +101,7 @@ typedef struct crisp_opts {
     float tau_jsd;
     int vs_rule;
     float gamma_vs;
+    int dense_below_tokens;
 } crisp_opts;
 
 /* Writes the defaults listed above into *opts (host pointer, not NULL). */
@@ -167,7 +175,8 @@ int crisp_select(const void *q, const void *k, const uint8_t *pattern, const flo
  * (any absolute layout with unique lists; row_ptr must stay inside col_idx).
  * Listed blocks outside [0, qb] are ignored; a row with no valid block yields
  * zeros.  Accumulates in fp32, writes bf16 out (rows < seq_len only).
- * Uses the workspace for V re-laid out as V^T padded to N_b * B keys.
+ * Uses the workspace for V re-laid out as transposed 64-key tiles (zero past
+ * seq_len).
  */
 int crisp_attend(const void *q, const void *k, const void *v, const int32_t *row_ptr,
                  const int32_t *col_idx, int seq_len, int n_heads, int n_kv_heads, int head_dim,
@@ -181,10 +190,53 @@ int crisp_attend_dense(const void *q, const void *k, const void *v, int seq_len,
 /*
  * Alg. 1 end to end: crisp_route -> crisp_select -> crisp_attend, with
  * every intermediate kept in the workspace and no host synchronisation.
+ * Below opts->dense_below_tokens it runs crisp_attend_dense instead.
  */
 int crisp_prefill(const void *q, const void *k, const void *v, int seq_len, int n_heads,
                   int n_kv_heads, int head_dim, int block_size, float alpha,
                   const crisp_opts *opts, void *ws, size_t ws_bytes, void *out, void *stream);
+
+/* One sequence of a batch: device pointers to token 0 of head 0 of its q, k,
+ * v and out, and its length (>= 0; 0 skips the sequence). */
+typedef struct crisp_seq {
+    const void *q;
+    const void *k;
+    const void *v;
+    void *out;
+    int seq_len;
+} crisp_seq;
+
+/* Element strides of the four tensors: row (h, t) of q starts at
+ * q + h * q_head + t * q_token, and likewise for k, v (KV heads) and out.
+ * The head_dim values of a row stay contiguous.  Every stride is positive
+ * and a multiple of 8 elements (16-byte aligned rows).  Examples, with H
+ * query and H_kv KV heads, d = head_dim:
+ *   [heads][tokens][d] per sequence:   q_head = seq_len * d, q_token = d
+ *   [tokens][heads][d] (packed varlen
+ *   or [batch][seq][heads][d]):         q_head = d, q_token = H * d
+ *                                       (k, v: k_head = d, k_token = H_kv * d) */
+typedef struct crisp_strides {
+    int64_t q_head, q_token;
+    int64_t k_head, k_token;
+    int64_t v_head, v_token;
+    int64_t out_head, out_token;
+} crisp_strides;
+
+/*
+ * crisp_prefill over `batch` independent sequences of any lengths (variable-
+ * length batches), each routed, selected and attended on its own as in
+ * Alg. 1, one after another on `stream`, reusing one workspace.
+ *   seqs      host array [batch] (may be NULL when batch == 0)
+ *   strides   host pointer; NULL means each sequence is contiguous
+ *             [heads][seq_len][head_dim] as in crisp_prefill
+ *   ws_bytes  at least crisp_workspace_size of the longest sequence
+ * All sequences are validated before the first launch; an error leaves
+ * every output untouched.  Sequences with seq_len < dense_below_tokens run
+ * dense attention.  The stage events, when set, time the last sequence.
+ */
+int crisp_prefill_batch(const crisp_seq *seqs, int batch, const crisp_strides *strides,
+                        int n_heads, int n_kv_heads, int head_dim, int block_size, float alpha,
+                        const crisp_opts *opts, void *ws, size_t ws_bytes, void *stream);
 
 /*
  * Stage timing for measurement: events is an array of `count` hipEvent_t

@@ -132,5 +132,55 @@ def test_default_opts_are_the_papers():
         (pytest.approx(0.2), pytest.approx(0.95), 1024, 128, 128)
     assert o.router == crisp.ROUTER_CSTRUCT and o.vs_rule == crisp.VS_NOISE_MEAN
     assert o.tau_jsd == pytest.approx(0.1) and o.gamma_vs == pytest.approx(0.95)
+    assert o.dense_below_tokens == 0            # no context-length gate by default
     f = crisp.flexprefill_opts()
     assert f.router == crisp.ROUTER_JSD and f.vs_rule == crisp.VS_GAMMA
+
+
+def _seqs(*items):
+    arr = (crisp.crisp_seq * len(items))()
+    for i, (ptr, n) in enumerate(items):
+        arr[i] = crisp.crisp_seq(ptr, ptr, ptr, ptr, n)
+    return arr
+
+
+def _strides(**kw):
+    st = crisp.crisp_strides(128, 128 * 4, 128, 128, 128, 128, 128, 128 * 4)
+    for k, v in kw.items():
+        setattr(st, k, v)
+    return C.byref(st)
+
+
+def test_batch_validation_before_launch(L):
+    """crisp_prefill_batch checks every sequence before the first launch."""
+    f = 1 << 20
+    _, need, _ = ws_size(1000, 4, 1)
+    B = L.crisp_prefill_batch
+    # empty batch, and sequences of length 0 need no pointers
+    assert B(None, 0, None, 4, 1, 128, 128, 1.0, None, None, 0, None) == OK
+    assert B(_seqs((None, 0), (None, 0)), 2, None, 4, 1, 128, 128, 1.0, None, None, 0, None) == OK
+    assert B(None, 1, None, 4, 1, 128, 128, 1.0, None, FAKE, need, None) == INVALID
+    assert B(None, -1, None, 4, 1, 128, 128, 1.0, None, FAKE, need, None) == INVALID
+    # a bad later sequence fails the call before anything runs
+    assert B(_seqs((f, 300), (f + 2, 300)), 2, None, 4, 1, 128, 128, 1.0, None, FAKE, need,
+             None) == INVALID
+    assert B(_seqs((f, 300), (f, -5)), 2, None, 4, 1, 128, 128, 1.0, None, FAKE, need, None) == SHAPE
+    # the workspace must fit the longest sequence
+    assert B(_seqs((f, 300), (f, 1025)), 2, None, 4, 1, 128, 128, 1.0, None, FAKE, need,
+             None) == WORKSPACE
+    # strides: positive multiples of 8 elements
+    for bad in (dict(q_token=0), dict(k_head=-128), dict(v_token=12), dict(out_head=4)):
+        assert B(_seqs((f, 300)), 1, _strides(**bad), 4, 1, 128, 128, 1.0, None, FAKE, need,
+                 None) == INVALID, bad
+    # options and alpha as in crisp_prefill
+    assert B(_seqs((f, 300)), 1, None, 4, 1, 128, 128, 1.0, _opts(dense_below_tokens=-1), FAKE,
+             need, None) == INVALID
+    assert B(_seqs((f, 300)), 1, None, 4, 1, 128, 128, -1.0, None, FAKE, need, None) == INVALID
+    assert B(_seqs((f, 300)), 1, None, 4, 3, 128, 128, 1.0, None, FAKE, need, None) == SHAPE
+
+
+def test_gate_option_validated(L):
+    assert L.crisp_prefill(FAKE, FAKE, FAKE, 256, 4, 1, 128, 128, 1.0, _opts(dense_below_tokens=-1),
+                           FAKE, 1 << 30, FAKE, None) == INVALID
+    assert L.crisp_prefill(None, None, None, 0, 4, 1, 128, 128, 1.0,
+                           _opts(dense_below_tokens=1 << 20), None, 0, None, None) == OK

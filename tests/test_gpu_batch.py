@@ -1,0 +1,174 @@
+"""Several sequences per call, strided layouts and the context-length gate
+(needs an MI355X).
+
+crisp_prefill_batch runs Alg. 1 on each sequence in turn.  Each output is
+checked bit for bit against crisp_prefill on a contiguous copy of that
+sequence: the same kernels see the same values. crisp_prefill itself is
+checked against the oracle (routing, selection and attention) on the same
+sequences.  The gate (Section 5.3, "Short contexts") must reproduce
+crisp_attend_dense bit for bit and the oracle's dense causal attention.
+"""
+import ctypes as C
+
+import numpy as np
+import pytest
+import torch
+
+import _parity as P
+from dynamic_sparse_attention_map_amd import crisp, synth
+from oracle import oracle as O
+
+pytestmark = pytest.mark.gpu
+
+B = 128
+HQ, HKV = 4, 2
+KINDS = [synth.VS, synth.DIFFUSE, synth.VS, synth.VS]
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    crisp.lib()
+
+
+def gen(n, seed_id):
+    """A seeded sequence of n >= 1 tokens (None for n == 0)."""
+    return synth.generate(synth.custom_spec(n, HQ, HKV, KINDS, seed_id=seed_id)) if n else None
+
+
+def single(q, k, v, alpha=1.0, opts=None):
+    """crisp_prefill on contiguous [heads, n, 128] device tensors."""
+    n = q.shape[1]
+    out = torch.empty_like(q)
+    crisp.crisp_prefill(q, k, v, alpha, crisp.alloc_workspace(n, HQ, HKV), out, opts=opts)
+    return out
+
+
+def same_bits(a, b):
+    return torch.equal(a.contiguous().view(torch.int16), b.contiguous().view(torch.int16))
+
+
+def oracle_check(inp, got, alpha=1.0, tag=""):
+    """The oracle's routing and selection against the GPU stages on the same
+    sequence, and the oracle's attention on the GPU's own lists against
+    `got`."""
+    n = inp.spec.n
+    qd, kd = inp.q.cuda(), inp.k.cuda()
+    ws = crisp.alloc_workspace(n, HQ, HKV)
+    gr = P.gpu_route(qd, kd, ws)
+    grh = P.host(gr)
+    orc_r = O.route(inp.q, inp.k, n, HQ, HKV)
+    P.check_route(grh, orc_r)
+    gs = P.host(P.gpu_select(qd, kd, gr, alpha, ws))
+    P.check_select(inp, grh, gs, alpha, orc_r)
+    nb = -(-n // B)
+    rows = np.arange(HQ * nb, dtype=np.int32)
+    want = O.attend(inp.q, inp.k, inp.v, n, HQ, HKV, 128, gs["row_ptr"].reshape(-1), gs["col_idx"],
+                    rows)
+    full = torch.zeros(HQ, nb * B, 128)
+    full[:, :n] = got.float().cpu()
+    P.check_outputs(full.numpy().reshape(HQ * nb, B, 128), want, f"batch {tag}")
+
+
+def test_varlen_packed_tokens_major():
+    """[total, heads, d] packed sequences with cumulative offsets (ragged,
+    one of length 1, one empty), one call, one workspace."""
+    lens = [300, 1, 0, 1000, 129, 2048]
+    cu = np.concatenate([[0], np.cumsum(lens)]).tolist()
+    total = cu[-1]
+    P.log(f"varlen lens={lens}")
+    inps = [gen(n, 300 + i) for i, n in enumerate(lens)]
+    q = torch.zeros(total, HQ, 128, dtype=torch.bfloat16)
+    k = torch.zeros(total, HKV, 128, dtype=torch.bfloat16)
+    v = torch.zeros(total, HKV, 128, dtype=torch.bfloat16)
+    for b, n in enumerate(lens):
+        if n:
+            q[cu[b]:cu[b + 1]] = inps[b].q.transpose(0, 1)
+            k[cu[b]:cu[b + 1]] = inps[b].k.transpose(0, 1)
+            v[cu[b]:cu[b + 1]] = inps[b].v.transpose(0, 1)
+    qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
+    out = torch.full_like(qd, float("nan"))
+    crisp.prefill_varlen(qd, kd, vd, cu, out, 1.0, crisp.alloc_workspace(max(lens), HQ, HKV))
+    torch.cuda.synchronize()
+    for b, n in enumerate(lens):
+        if n == 0:
+            continue
+        ref = single(inps[b].q.cuda(), inps[b].k.cuda(), inps[b].v.cuda())
+        got = out[cu[b]:cu[b + 1]].transpose(0, 1)
+        assert same_bits(got, ref), f"sequence {b} (n={n}) differs from crisp_prefill"
+        oracle_check(inps[b], got, tag=f"varlen seq {b} n={n}")
+
+
+def test_batch_seq_heads_layout():
+    """Equal lengths in a [batch, seq, heads, d] tensor."""
+    n, batch = 1024, 2
+    inps = [gen(n, 320 + b) for b in range(batch)]
+    q = torch.stack([i.q.transpose(0, 1) for i in inps]).cuda()     # [B, n, H, d]
+    k = torch.stack([i.k.transpose(0, 1) for i in inps]).cuda()
+    v = torch.stack([i.v.transpose(0, 1) for i in inps]).cuda()
+    out = torch.empty_like(q)
+    crisp.crisp_prefill_batch([q[b].transpose(0, 1) for b in range(batch)],
+                              [k[b].transpose(0, 1) for b in range(batch)],
+                              [v[b].transpose(0, 1) for b in range(batch)],
+                              [out[b].transpose(0, 1) for b in range(batch)],
+                              1.0, crisp.alloc_workspace(n, HQ, HKV))
+    for b in range(batch):
+        ref = single(inps[b].q.cuda(), inps[b].k.cuda(), inps[b].v.cuda())
+        assert same_bits(out[b].transpose(0, 1), ref), f"batch element {b}"
+
+
+def test_batch_contiguous_default_strides():
+    """strides == NULL: each sequence contiguous [heads, n, d], separate
+    allocations, called through the C ABI directly."""
+    lens = [640, 77, 1500]
+    inps = [gen(n, 340 + i) for i, n in enumerate(lens)]
+    dev = [(i.q.cuda(), i.k.cuda(), i.v.cuda()) for i in inps]
+    outs = [torch.empty_like(d[0]) for d in dev]
+    arr = (crisp.crisp_seq * len(lens))()
+    for b, ((q, k, v), o) in enumerate(zip(dev, outs)):
+        arr[b] = crisp.crisp_seq(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lens[b])
+    ws = crisp.alloc_workspace(max(lens), HQ, HKV)
+    rc = crisp.lib().crisp_prefill_batch(arr, len(lens), None, HQ, HKV, 128, 128, 1.0, None,
+                                         C.c_void_p(ws.data_ptr()), ws.numel(),
+                                         C.c_void_p(torch.cuda.current_stream().cuda_stream))
+    assert rc == crisp.CRISP_OK, crisp.status_string(rc)
+    for b, (q, k, v) in enumerate(dev):
+        assert same_bits(outs[b], single(q, k, v)), f"sequence {b}"
+
+
+def test_gate_runs_dense_below_threshold():
+    n = 3000                      # N_b = 24: the sparse path keeps a strict subset
+    inp = gen(n, 360)
+    q, k, v = inp.q.cuda(), inp.k.cuda(), inp.v.cuda()
+    ws = crisp.alloc_workspace(n, HQ, HKV)
+    gated = single(q, k, v, opts=crisp.default_opts(dense_below_tokens=n + 1))
+    dense = torch.empty_like(q)
+    crisp.crisp_attend_dense(q, k, v, ws, dense)
+    assert same_bits(gated, dense)
+    nb = -(-n // B)
+    rp, ci = O.full_causal_lists(HQ, nb)
+    want = O.attend(inp.q, inp.k, inp.v, n, HQ, HKV, 128, rp, ci, np.arange(HQ * nb, dtype=np.int32))
+    full = torch.zeros(HQ, nb * B, 128)
+    full[:, :n] = gated.float().cpu()
+    P.check_outputs(full.numpy().reshape(HQ * nb, B, 128), want, "gated dense")
+    # at the threshold itself the sparse path runs
+    ungated = single(q, k, v)
+    assert same_bits(single(q, k, v, opts=crisp.default_opts(dense_below_tokens=n)), ungated)
+    assert not same_bits(gated, ungated)
+
+
+def test_gate_inside_a_batch():
+    """A gate between the lengths: short sequences dense, long ones sparse."""
+    lens = [3000, 5000]
+    inps = [gen(n, 380 + i) for i, n in enumerate(lens)]
+    opts = crisp.default_opts(dense_below_tokens=4096)
+    dev = [(i.q.cuda(), i.k.cuda(), i.v.cuda()) for i in inps]
+    outs = [torch.empty_like(d[0]) for d in dev]
+    crisp.crisp_prefill_batch([d[0] for d in dev], [d[1] for d in dev], [d[2] for d in dev], outs,
+                              1.0, crisp.alloc_workspace(max(lens), HQ, HKV), opts=opts)
+    q, k, v = dev[0]
+    dense = torch.empty_like(q)
+    crisp.crisp_attend_dense(q, k, v, crisp.alloc_workspace(lens[0], HQ, HKV), dense)
+    assert same_bits(outs[0], dense)
+    assert not same_bits(outs[0], single(*dev[0]))
+    assert same_bits(outs[1], single(*dev[1]))

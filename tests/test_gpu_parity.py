@@ -152,6 +152,31 @@ def test_alpha_extremes(alpha):
                 assert gs["row_ptr"][h][qb + 1] - gs["row_ptr"][h][qb] == qb + 1
 
 
+@pytest.mark.parametrize("alpha", [0.75, 1.25, 1.5])
+def test_alpha_sweep_values(alpha):
+    """The other alpha settings the paper evaluates (Sec. 5 setup, App. E)."""
+    inp = synth.generate(synth.config_spec("c2"))
+    rows = P.sample_rows(32768 // B, 32, 3, seed=int(alpha * 100))
+    case(inp, alpha=alpha, rows=rows, tag=f"-a{alpha}")
+
+
+@pytest.mark.parametrize("tau", [0.15, 0.25])
+def test_tau_sweep_values(tau):
+    """Routing thresholds of the paper's robustness check (App. E): bits exact,
+    then selection on the routes they give."""
+    inp = synth.generate(synth.config_spec("c2"))
+    n, hq, hkv = 32768, 32, 8
+    q, k, _ = P.to_dev(inp)
+    ws = crisp.alloc_workspace(n, hq, hkv)
+    opts = crisp.default_opts(tau_proxy=tau)
+    gr = P.gpu_route(q, k, ws, opts=opts)
+    orc = O.route(inp.q, inp.k, n, hq, hkv, tau=tau)
+    grh = P.host(gr)
+    P.check_route(grh, orc)
+    gs = P.host(P.gpu_select(q, k, gr, 1.0, ws, opts=opts))
+    P.log(P.check_select(inp, grh, gs, 1.0, orc).line() + f" tau={tau}")
+
+
 def test_c2_parity_sampled_rows():
     inp = synth.generate(synth.config_spec("c2"))
     nb = 32768 // B
