@@ -33,6 +33,7 @@ constexpr int kThreads = 512;             // 8 wavefronts: two query blocks x 4
 constexpr int kEnd = 0x7fffffff;           // list exhausted
 
 constexpr int kListWords = kMaxBlocks / 32;   // bitmap words per row
+constexpr int kPairRun = 256;                  // longest run of one head's pairs
 
 // 16 bytes per lane from global memory straight into LDS: lane l's bytes
 // land at lds_addr + 16 l (lds_addr wave-uniform).  Written as inline asm so
@@ -60,25 +61,32 @@ __device__ __forceinline__ void wait_copies()
     __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8));
 }
 
-// Work items: like a grid of ceil(npairs*hkv / 8) * 8 * G items whose item b
-// belongs to XCD b % 8: its j = b / 8-th slot there takes chunk
-// (j / G) * 8 + b % 8 and head j % G of that chunk, where chunk c covers the G
-// query heads of KV head c % hkv at query-block pair c / hkv, the pair p
-// being blocks Nb-1-2p and Nb-2-2p.  Each XCD keeps whole GQA groups (sharing
-// K/V in its L2) and walks the pairs from the longest causal rows down.
+// Work items.  Pair p is query blocks Nb-1-2p and Nb-2-2p.  A chunk is `run`
+// consecutive pairs of the G query heads of one KV head: chunk c covers KV
+// head c % hkv and pairs run * (c / hkv) onward, and holds its G x run items
+// head-major (one head's run of pairs, then the next head's).  Item b belongs
+// to XCD b % 8; its j = b / 8-th slot there is item j % (G run) of chunk
+// (j / (G run)) * 8 + b % 8.  So each XCD keeps whole GQA groups and walks
+// the pairs from the longest causal rows down in runs, and the work-groups of
+// an XCD start one head's adjacent pairs close together in time: their lists
+// are alike, they walk them in step, and all but the first find most K/V
+// tiles in L2.  (Interleaving the heads instead, pair by pair, leaves almost
+// no reuse: the long rows of diffuse heads start far apart in time.)
 __device__ __forceinline__ void
 attend_pair(int b, uint16_t* lds, uint32_t* list, Rows q, Rows k,
             const uint16_t* __restrict__ vt, const int32_t* __restrict__ row_ptr,
-            const int32_t* __restrict__ col_idx, int n, int nb, int hkv, int G,
+            const int32_t* __restrict__ col_idx, int n, int nb, int hkv, int G, int run,
             float scale_log2, OutRows out)
 {
     const int npairs = (nb + 1) >> 1;
     const int slot = b >> 3;
-    const int chunk = (slot / G) * 8 + (b & 7);
-    if (chunk >= npairs * hkv) return;
-    const int pair = chunk / hkv;
+    const int per_chunk = G * run;
+    const int chunk = (slot / per_chunk) * 8 + (b & 7);
+    const int r = slot % per_chunk;
+    const int pair = (chunk / hkv) * run + r % run;
+    if (pair >= npairs) return;
     const int g = chunk % hkv;
-    const int h = g * G + slot % G;
+    const int h = g * G + r / run;
     const int qb_hi = nb - 1 - 2 * pair;
     const int qb_lo = qb_hi - 1;                   // -1: no second block
 
@@ -383,7 +391,7 @@ attend_pair(int b, uint16_t* lds, uint32_t* list, Rows q, Rows k,
 __global__ void __launch_bounds__(kThreads)
 attend_kernel(Rows q, Rows k,
               const uint16_t* __restrict__ vt, const int32_t* __restrict__ row_ptr,
-              const int32_t* __restrict__ col_idx, int n, int nb, int hkv, int G,
+              const int32_t* __restrict__ col_idx, int n, int nb, int hkv, int G, int run,
               float scale_log2, int per_xcd, int* __restrict__ ctr, OutRows out)
 {
     __shared__ __attribute__((aligned(1024))) uint16_t lds[kStages * kStageBytes / 2];
@@ -406,7 +414,8 @@ attend_kernel(Rows q, Rows k,
         const int item = s_item;
         __syncthreads();
         if (item < 0) break;
-        attend_pair(item, lds, list, q, k, vt, row_ptr, col_idx, n, nb, hkv, G, scale_log2, out);
+        attend_pair(item, lds, list, q, k, vt, row_ptr, col_idx, n, nb, hkv, G, run, scale_log2,
+                    out);
     }
 }
 
@@ -465,8 +474,10 @@ hipError_t launch_attend(Rows q, Rows k, const uint16_t* vt,
                          int* counters, OutRows out, hipStream_t stream)
 {
     const int nb = (n + kB - 1) / kB, G = hq / hkv;
-    const long long chunks = (long long)((nb + 1) / 2) * hkv;
-    const long long items = ((chunks + 7) / 8) * 8 * G;
+    const int npairs = (nb + 1) / 2;
+    const int run = npairs < kPairRun ? npairs : kPairRun;
+    const long long chunks = (long long)((npairs + run - 1) / run) * hkv;
+    const long long items = ((chunks + 7) / 8) * 8 * G * run;
     const int per_xcd = (int)(items / 8);
     int dev = 0, cus = 256;
     if (hipGetDevice(&dev) == hipSuccess)
@@ -477,7 +488,7 @@ hipError_t launch_attend(Rows q, Rows k, const uint16_t* vt,
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(attend_kernel, dim3(groups), dim3(kThreads), 0, stream, q, k, vt, row_ptr, col_idx,
-                       n, nb, hkv, G, scale_log2, per_xcd, counters, out);
+                       n, nb, hkv, G, run, scale_log2, per_xcd, counters, out);
     return hipGetLastError();
 }
 
