@@ -26,6 +26,7 @@ struct Shape {
 // stream); region P after it holds crisp_prefill's intermediates.
 struct Layout {
     size_t part_m, part_lo, part_up, jsd_kbar, jsd_qbar;   // route (in S)
+    size_t seg_m, seg_l, row_mx, row_inv, tile_sums;       // route reduction (in S)
     size_t qbar, kbar, abar, hist_mass, hist_count, state, bitmap;   // select (in S)
     size_t vt, queue;                                      // attend (in S)
     size_t route_end, select_end, attend_end;              // bytes of S each stage needs
@@ -51,6 +52,11 @@ Layout make_layout(const Shape& s)
     L.part_up = take(part);
     L.jsd_kbar = take(hkv * nb * kD * sizeof(float));      // JSD router only
     L.jsd_qbar = take(hq * kD * sizeof(float));
+    L.seg_m = take(hq * kRouteSegs * kB * sizeof(float));
+    L.seg_l = take(hq * kRouteSegs * kB * sizeof(double));
+    L.row_mx = take(hq * kB * sizeof(float));
+    L.row_inv = take(hq * kB * sizeof(float));
+    L.tile_sums = take(hq * 4 * nb * sizeof(float));
     L.route_end = o;
     o = 0;
     L.qbar = take(hq * nb * kD * sizeof(float));
@@ -179,6 +185,11 @@ int do_route(const Shape& s, const Opts& op, Rows q, Rows k, void* ws,
     ra.part_up = at<float>(ws, L.part_up);
     ra.jsd_kbar = at<float>(ws, L.jsd_kbar);
     ra.jsd_qbar = at<float>(ws, L.jsd_qbar);
+    ra.seg_m = at<float>(ws, L.seg_m);
+    ra.seg_l = at<double>(ws, L.seg_l);
+    ra.row_mx = at<float>(ws, L.row_mx);
+    ra.row_inv = at<float>(ws, L.row_inv);
+    ra.tile_sums = at<float>(ws, L.tile_sums);
     return hip_status(launch_route(q, k, s.n, s.hq, s.hkv, ra, p_v, p_s, c_struct, pattern, stream));
 }
 

@@ -9,6 +9,7 @@ namespace crisp {
 constexpr int kD = 128;            // head_dim
 constexpr int kB = 128;            // block size B (tokens per block)
 constexpr int kMaxBlocks = 4096;   // largest N_b (seq_len 524288 at B = 128)
+constexpr int kRouteSegs = 64;     // tile segments per head in the routing row reduction
 
 // A bf16 operand [heads][tokens][128] with arbitrary head and token strides
 // in elements; the 128 head-dimension values of one row are contiguous.
@@ -49,6 +50,11 @@ struct RouteArgs {
     float* part_up;
     float* jsd_kbar;                // [hkv][Nb][128] block key means (router 1)
     float* jsd_qbar;                // [hq][128] mean representative query (router 1)
+    float* seg_m;                   // [hq][kRouteSegs][128] per (tile segment, row) max
+    double* seg_l;                  //                and normaliser
+    float* row_mx;                  // [hq][128] row max
+    float* row_inv;                 // [hq][128] 1 / row normaliser
+    float* tile_sums;               // [hq][4][Nb] slash-part sums per tile
 };
 
 hipError_t launch_route(Rows q, Rows k, int n, int hq, int hkv,

@@ -13,7 +13,7 @@
 // c > b_i, i.e. slash block t + e_i and t + e_i + 1 with
 // e_i = N_b - 1 - floor(q_i / B) (0 or 1; always 0 when B divides n).  So
 // lower + upper pools the tile's column mass (vertical score) and lower /
-// upper split it between two slash blocks.  mass_reduce_kernel rescales the
+// upper split it between two slash blocks.  Four reduction kernels rescale the
 // partials with the global row maxima and normalisers.  Under the JSD router
 // (FlexPrefill's Alg. 5, kept as the baseline) two more kernels pool the
 // keys and the representative queries and compare the pooled estimate with
@@ -28,25 +28,28 @@ namespace {
 constexpr int kTileKeys = 128;
 constexpr int kKRow = kD + 8;   // LDS row pitch of a K tile (bf16): 272 bytes
 
-// grid: (ceil(Nb / tiles_per_wg), n_kv_heads * ceil(G / 4)); block: 4
-// wavefronts sharing one staged K tile.  Wave w handles query head
-// kv*G + 4*sub + w (idle when that is >= G; it still helps stage K).
+// grid: (ceil(Nb / tiles_per_wg), n_kv_heads * ceil(G / 4)); block: 16
+// wavefronts sharing one staged K tile (double-buffered in LDS).  Wave w
+// handles proxy rows 32 (w % 4) .. +31 of query head kv*G + 4*sub + w / 4
+// (idle when that head is >= G; it still helps stage K).
 // Aligned (B divides n): row i sits at column i of the last tile, so the
 // split column and the causal cut are compile-time per (chunk, key group).
 template <bool Aligned>
-__global__ void __launch_bounds__(256)
+__global__ void __launch_bounds__(1024)
 proxy_map_kernel(Rows q, Rows k, int n, int nb,
                  int G, int tiles_per_wg, float scale_log2,
                  float* __restrict__ part_m, float* __restrict__ part_lo,
                  float* __restrict__ part_up)
 {
-    __shared__ __attribute__((aligned(16))) uint16_t ks[kTileKeys * kKRow];
+    __shared__ __attribute__((aligned(16))) uint16_t ks[2][kTileKeys * kKRow];
 
-    const int lane = threadIdx.x & 63;
-    const int w = threadIdx.x >> 6;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int w = tid >> 6;
+    const int c = w & 3;                            // row chunk
     const int subs = (G + 3) / 4;
     const int kv = blockIdx.y / subs;
-    const int hg = 4 * (blockIdx.y % subs) + w;     // head within the KV group
+    const int hg = 4 * (blockIdx.y % subs) + (w >> 2);   // head within the KV group
     const bool active = hg < G;
     const int h = kv * G + (active ? hg : 0);
     const int l32 = lane & 31;
@@ -54,200 +57,222 @@ proxy_map_kernel(Rows q, Rows k, int n, int nb,
     const int R = min(kB, n);                       // proxy rows
     const int q0 = n - R;                           // position of proxy row 0
 
-    // representative query block Q^ of head h as MFMA B-operands:
-    // chunk c holds rows 32c .. 32c+31, step s holds d = 16s .. 16s+15
-    // (rows past R, which exist only when n < B, repeat the last row)
-    bf16x8 qf[4][8];
+    // rows 32c .. 32c+31 of the representative block Q^ as MFMA B-operands,
+    // step s holding d = 16s .. 16s+15 (rows past R, which exist only when
+    // n < B, repeat the last row)
+    bf16x8 qf[8];
     {
-        const uint16_t* qh = q.row(h, q0);
-#pragma unroll
-        for (int c = 0; c < 4; ++c)
-#pragma unroll
-            for (int s = 0; s < 8; ++s)
-                qf[c][s] = *reinterpret_cast<const bf16x8*>(
-                    qh + min(32 * c + l32, R - 1) * q.st + 16 * s + 8 * hi);
+        const uint16_t* qr = q.row(h, q0) + min(32 * c + l32, R - 1) * q.st;
+        for (int s = 0; s < 8; ++s) qf[s] = *reinterpret_cast<const bf16x8*>(qr + 16 * s + 8 * hi);
     }
 
     const uint16_t* kg = k.row(kv, 0);
     const int t0 = blockIdx.x * tiles_per_wg;
     const int t1 = min(nb, t0 + tiles_per_wg);
-    for (int t = t0; t < t1; ++t) {
-        // stage K tile t: 128 rows x 256 bytes as 16-byte chunks; rows past
-        // the end of the sequence are zero (and masked below)
-        __syncthreads();
-        if ((t + 1) * kTileKeys <= n) {
-            for (int e = threadIdx.x; e < kTileKeys * (kD / 8); e += 256) {
-                const int row = e >> 4, ch = e & 15;
-                *reinterpret_cast<u32x4*>(&ks[row * kKRow + 8 * ch]) =
-                    *reinterpret_cast<const u32x4*>(kg + ((long long)t * kTileKeys + row) * k.st + 8 * ch);
-            }
-        } else {
-            for (int e = threadIdx.x; e < kTileKeys * (kD / 8); e += 256) {
-                const int row = e >> 4, ch = e & 15;
-                const long long key = (long long)t * kTileKeys + row;
-                u32x4 val = {0u, 0u, 0u, 0u};
-                if (key < n) val = *reinterpret_cast<const u32x4*>(kg + key * k.st + 8 * ch);
-                *reinterpret_cast<u32x4*>(&ks[row * kKRow + 8 * ch]) = val;
-            }
+    // stage K tile t into buffer `buf`: 128 rows x 256 bytes as 2048 16-byte
+    // chunks, two per thread; rows past the end of the sequence are zero
+    // (and masked below)
+    auto stage = [&](int t, int buf) {
+        for (int e = tid; e < kTileKeys * (kD / 8); e += 1024) {
+            const int row = e >> 4, ch = e & 15;
+            const long long key = (long long)t * kTileKeys + row;
+            u32x4 val = {0u, 0u, 0u, 0u};
+            if (key < n) val = *reinterpret_cast<const u32x4*>(kg + key * k.st + 8 * ch);
+            *reinterpret_cast<u32x4*>(&ks[buf][row * kKRow + 8 * ch]) = val;
         }
-        __syncthreads();
+    };
+    if (t0 < t1) stage(t0, 0);
+    for (int t = t0; t < t1; ++t) {
+        const int buf = (t - t0) & 1;
+        __syncthreads();                            // tile t staged, buffer buf ^ 1 free
+        if (t + 1 < t1) stage(t + 1, buf ^ 1);
         if (!active) continue;
 
-        // the tile holds keys after some proxy row's position
-        const bool maybe_future = t * kTileKeys + kTileKeys - 1 > q0;
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            // S^T for keys 32a.. of the tile against query rows 32c..
-            f32x16 acc[4];
-            for (int a = 0; a < 4; ++a) acc[a] = f32x16{};
-            for (int s = 0; s < 8; ++s)
-                for (int a = 0; a < 4; ++a) {
-                    const bf16x8 kf = *reinterpret_cast<const bf16x8*>(&ks[(32 * a + l32) * kKRow + 16 * s + 8 * hi]);
-                    acc[a] = mfma32(kf, qf[c][s], acc[a]);
-                }
-
-            // this lane: query row i at position qi, 64 of the tile's 128 keys
-            const int i = 32 * c + l32;
-            const int qi = q0 + i;
-            const int bi = Aligned ? i : (qi & (kB - 1));
-            const int rel = Aligned ? i : qi - t * kTileKeys;     // last visible column
-            const bool cut = Aligned ? (t == nb - 1) : maybe_future;
-            float m = -INFINITY;
-            for (int a = 0; a < 4; ++a)
-                for (int r = 0; r < 16; ++r) {
-                    const int col = 32 * a + 8 * (r >> 2) + 4 * hi + (r & 3);
-                    float x = acc[a][r] * scale_log2;
-                    if (cut && col > rel) x = -INFINITY;   // causal
-                    acc[a][r] = x;
-                    m = fmaxf(m, x);
-                }
-            m = fmaxf(m, swap_half(m));
-            // a tile wholly in the row's future keeps m = -inf and sums 0
-            const float mref = (m == -INFINITY) ? 0.f : m;
-            float lo = 0.f, up = 0.f;
-            for (int a = 0; a < 4; ++a)
-                for (int r = 0; r < 16; ++r) {
-                    const int col = 32 * a + 8 * (r >> 2) + 4 * hi + (r & 3);
-                    const float e = exp2f(acc[a][r] - mref);
-                    if (col <= bi) lo += e; else up += e;
-                }
-            lo += swap_half(lo);
-            up += swap_half(up);
-            if (hi == 0 && i < R) {
-                const size_t o = ((size_t)h * nb + t) * kB + i;
-                part_m[o] = m;
-                part_lo[o] = lo;
-                part_up[o] = up;
+        // S^T for keys 32a .. 32a+31 of the tile against this wave's rows
+        f32x16 acc[4];
+        for (int a = 0; a < 4; ++a) acc[a] = f32x16{};
+        for (int s = 0; s < 8; ++s)
+            for (int a = 0; a < 4; ++a) {
+                const bf16x8 kf = *reinterpret_cast<const bf16x8*>(&ks[buf][(32 * a + l32) * kKRow + 16 * s + 8 * hi]);
+                acc[a] = mfma32(kf, qf[s], acc[a]);
             }
+
+        // this lane: query row i at position qi, 64 of the tile's 128 keys
+        const int i = 32 * c + l32;
+        const int qi = q0 + i;
+        const int bi = Aligned ? i : (qi & (kB - 1));
+        const int rel = Aligned ? i : qi - t * kTileKeys;     // last visible column
+        const bool cut = Aligned ? (t == nb - 1) : (t * kTileKeys + kTileKeys - 1 > q0);
+        float m = -INFINITY;
+        for (int a = 0; a < 4; ++a)
+            for (int r = 0; r < 16; ++r) {
+                const int col = 32 * a + 8 * (r >> 2) + 4 * hi + (r & 3);
+                if (cut && col > rel) acc[a][r] = -INFINITY;   // causal
+                m = fmaxf(m, acc[a][r]);
+            }
+        m = fmaxf(m, swap_half(m));
+        // scaled logits in the exp2 domain; a tile wholly in the row's future
+        // keeps m = -inf and sums 0
+        const float ms = m * scale_log2;
+        const float nref = (m == -INFINITY) ? 0.f : -ms;
+        float lo = 0.f, up = 0.f;
+        for (int a = 0; a < 4; ++a)
+            for (int r = 0; r < 16; ++r) {
+                const int col = 32 * a + 8 * (r >> 2) + 4 * hi + (r & 3);
+                const float e = __builtin_amdgcn_exp2f(fmaf(acc[a][r], scale_log2, nref));
+                if (col <= bi) lo += e; else up += e;
+            }
+        lo += swap_half(lo);
+        up += swap_half(up);
+        if (hi == 0 && i < R) {
+            const size_t o = ((size_t)h * nb + t) * kB + i;
+            part_m[o] = ms;
+            part_lo[o] = lo;
+            part_up[o] = up;
         }
     }
 }
 
-// One work-group (256 threads) per query head; rows i < R = min(B, n).
-//   m_i   = max_t M[t][i],  l_i = sum_t exp2(M[t][i] - m_i) (LO + UP)[t][i]
-//   w_ti  = exp2(M[t][i] - m_i) / l_i
-//   p_v[t] = (1/R) sum_i w_ti (LO + UP)[t][i]
-//   p_s[t] = (1/R) sum_i (w_(t-e_i)i LO[t-e_i][i] + w_(t-e_i-1)i UP[t-e_i-1][i])
-// Tiles wholly in a row's future carry M = -inf and are skipped.
-// 1024 threads: eight per row in phase 1, sixteen wavefronts over the tiles
-// in phase 2.
-__global__ void __launch_bounds__(1024)
-mass_reduce_kernel(const float* __restrict__ part_m, const float* __restrict__ part_lo,
-                   const float* __restrict__ part_up, int n, int nb, float tau, int route_here,
-                   float* __restrict__ p_v, float* __restrict__ p_s,
-                   float* __restrict__ c_struct, uint8_t* __restrict__ pattern)
+// The block-mass reduction runs in four small kernels so that it spreads over
+// the whole chip:
+//   row_part_kernel   per (head, segment of tiles, row): online max m and
+//                     normaliser l = sum_t e^(m_t - m) (lo_t + up_t)
+//   row_norm_kernel   per (head, row): combine the segments into the row's
+//                     max m_i and 1 / l_i
+//   tile_mass_kernel  per (head, tile): weights w_{i,t} = e^(m_{i,t} - m_i) / l_i,
+//                     p_v[t] and the lower / upper slash sums of the tile,
+//                     split by e_i
+//   finalize_kernel   per head: p_s from the tile sums; C_struct and the
+//                     routing bit (Eq. 2, Alg. 2) under the C_struct router
+constexpr int kSegs = kRouteSegs;
+
+// grid (kSegs, hq), kB threads: thread i = proxy row i, tiles t = seg (mod kSegs)
+__global__ void __launch_bounds__(kB)
+row_part_kernel(const float* __restrict__ part_m, const float* __restrict__ part_lo,
+                const float* __restrict__ part_up, int n, int nb, float* __restrict__ seg_m,
+                double* __restrict__ seg_l)
 {
-    __shared__ float row_m[8][kB];
-    __shared__ double row_l[8][kB];
-    __shared__ float row_inv[kB];
-    __shared__ float row_mx[kB];
-    // lower / upper slash sums of each tile, for rows with e_i = 0 and 1
-    __shared__ float lo_sum[2][kMaxBlocks];
-    __shared__ float up_sum[2][kMaxBlocks];
-    __shared__ float pv_ends[2];
-
-    const int h = blockIdx.x;
-    const int tid = threadIdx.x;
+    const int seg = blockIdx.x, h = blockIdx.y, i = threadIdx.x;
+    const int R = min(kB, n);
     const size_t base = (size_t)h * nb * kB;
-    const int R = min(kB, n), q0 = n - R;
-
-    // phase 1: per-row online max / normaliser, eight threads per row
-    {
-        const int i = tid & (kB - 1), part = tid >> 7;
-        float m = -INFINITY;
-        double l = 0.0;
-        if (i < R) {
-            for (int t = part; t < nb; t += 8) {
-                const size_t o = base + (size_t)t * kB + i;
-                const float mt = part_m[o];
-                if (mt == -INFINITY) continue;
-                const double s = (double)part_lo[o] + (double)part_up[o];
-                if (mt > m) {
-                    l = l * (double)exp2f(m - mt) + s;
-                    m = mt;
-                } else {
-                    l += s * (double)exp2f(mt - m);
-                }
-            }
-        }
-        row_m[part][i] = m;
-        row_l[part][i] = l;
-    }
-    __syncthreads();
-    if (tid < R) {
-        float m = -INFINITY;
-        for (int x = 0; x < 8; ++x) m = fmaxf(m, row_m[x][tid]);
-        double l = 0.0;
-        for (int x = 0; x < 8; ++x)
-            if (row_m[x][tid] > -INFINITY) l += row_l[x][tid] * (double)exp2f(row_m[x][tid] - m);
-        row_mx[tid] = m;
-        row_inv[tid] = (float)(1.0 / l);
-    }
-    __syncthreads();
-
-    // phase 2: one wavefront per tile, lanes over the R rows
-    const int lane = tid & 63, w = tid >> 6;
-    for (int t = w; t < nb; t += 16) {
-        double sv = 0.0, slo0 = 0.0, sup0 = 0.0, slo1 = 0.0, sup1 = 0.0;
-        for (int i = lane; i < R; i += 64) {
+    float m = -INFINITY;
+    double l = 0.0;
+    if (i < R) {
+        for (int t = seg; t < nb; t += kSegs) {
             const size_t o = base + (size_t)t * kB + i;
             const float mt = part_m[o];
             if (mt == -INFINITY) continue;
-            const float wt = exp2f(mt - row_mx[i]) * row_inv[i];
-            const float lo = part_lo[o] * wt, up = part_up[o] * wt;
-            sv += (double)lo + (double)up;
-            const int ei = nb - 1 - (q0 + i) / kB;
-            if (ei == 0) { slo0 += lo; sup0 += up; }
-            else { slo1 += lo; sup1 += up; }
+            const double sum = (double)part_lo[o] + (double)part_up[o];
+            if (mt > m) {
+                l = l * (double)exp2f(m - mt) + sum;
+                m = mt;
+            } else {
+                l += sum * (double)exp2f(mt - m);
+            }
         }
-        sv = wave_sum(sv);
-        slo0 = wave_sum(slo0);
-        sup0 = wave_sum(sup0);
-        slo1 = wave_sum(slo1);
-        sup1 = wave_sum(sup1);
-        if (lane == 0) {
-            const float pv = (float)(sv / R);
-            p_v[(size_t)h * nb + t] = pv;
-            if (t == 0) pv_ends[0] = pv;
-            if (t == nb - 1) pv_ends[1] = pv;
-            lo_sum[0][t] = (float)(slo0 / R);
-            up_sum[0][t] = (float)(sup0 / R);
-            lo_sum[1][t] = (float)(slo1 / R);
-            up_sum[1][t] = (float)(sup1 / R);
-        }
+    }
+    const size_t o = ((size_t)h * kSegs + seg) * kB + i;
+    seg_m[o] = m;
+    seg_l[o] = l;
+}
+
+// grid hq, 1024 threads: eight threads per row, each over every eighth segment
+__global__ void __launch_bounds__(1024)
+row_norm_kernel(const float* __restrict__ seg_m, const double* __restrict__ seg_l, int n,
+                float* __restrict__ row_mx, float* __restrict__ row_inv)
+{
+    __shared__ float pm[8][kB];
+    __shared__ double pl[8][kB];
+    const int h = blockIdx.x, i = threadIdx.x & (kB - 1), part = threadIdx.x >> 7;
+    const size_t b = (size_t)h * kSegs * kB + i;
+    float m = -INFINITY;
+    for (int x = part; x < kSegs; x += 8) m = fmaxf(m, seg_m[b + (size_t)x * kB]);
+    double l = 0.0;
+    for (int x = part; x < kSegs; x += 8) {
+        const float mx = seg_m[b + (size_t)x * kB];
+        if (mx > -INFINITY) l += seg_l[b + (size_t)x * kB] * (double)exp2f(mx - m);
+    }
+    pm[part][i] = m;
+    pl[part][i] = l;
+    __syncthreads();
+    if (part != 0 || i >= min(kB, n)) return;
+    float mt = -INFINITY;
+    for (int x = 0; x < 8; ++x) mt = fmaxf(mt, pm[x][i]);
+    double lt = 0.0;
+    for (int x = 0; x < 8; ++x)
+        if (pm[x][i] > -INFINITY) lt += pl[x][i] * (double)exp2f(pm[x][i] - mt);
+    row_mx[(size_t)h * kB + i] = mt;
+    row_inv[(size_t)h * kB + i] = (float)(1.0 / lt);
+}
+
+// grid (ceil(Nb / 16), hq), 1024 threads: one wavefront per tile, lanes over
+// the R rows.  tile_sums[h][4][Nb] = lower / upper sums for rows with e_i = 0,
+// then for rows with e_i = 1, each divided by R.
+__global__ void __launch_bounds__(1024)
+tile_mass_kernel(const float* __restrict__ part_m, const float* __restrict__ part_lo,
+                 const float* __restrict__ part_up, const float* __restrict__ row_mx,
+                 const float* __restrict__ row_inv, int n, int nb, float* __restrict__ p_v,
+                 float* __restrict__ tile_sums)
+{
+    __shared__ float mx[kB], inv[kB];
+    const int h = blockIdx.y, tid = threadIdx.x;
+    const int R = min(kB, n), q0 = n - R;
+    if (tid < R) {
+        mx[tid] = row_mx[(size_t)h * kB + tid];
+        inv[tid] = row_inv[(size_t)h * kB + tid];
     }
     __syncthreads();
-    // slash block t: lower parts of tile t (e = 0) and t-1 (e = 1), upper
-    // parts of tile t-1 (e = 0) and t-2 (e = 1)
-    for (int t = tid; t < nb; t += 1024) {
-        float ps = lo_sum[0][t];
-        if (t >= 1) ps += up_sum[0][t - 1] + lo_sum[1][t - 1];
-        if (t >= 2) ps += up_sum[1][t - 2];
+    const int lane = tid & 63;
+    const int t = blockIdx.x * 16 + (tid >> 6);
+    if (t >= nb) return;
+    double sv = 0.0, slo0 = 0.0, sup0 = 0.0, slo1 = 0.0, sup1 = 0.0;
+    for (int i = lane; i < R; i += 64) {
+        const size_t o = ((size_t)h * nb + t) * kB + i;
+        const float mt = part_m[o];
+        if (mt == -INFINITY) continue;
+        const float wt = exp2f(mt - mx[i]) * inv[i];
+        const float lo = part_lo[o] * wt, up = part_up[o] * wt;
+        sv += (double)lo + (double)up;
+        const int ei = nb - 1 - (q0 + i) / kB;
+        if (ei == 0) { slo0 += lo; sup0 += up; }
+        else { slo1 += lo; sup1 += up; }
+    }
+    sv = wave_sum(sv);
+    slo0 = wave_sum(slo0);
+    sup0 = wave_sum(sup0);
+    slo1 = wave_sum(slo1);
+    sup1 = wave_sum(sup1);
+    if (lane == 0) {
+        p_v[(size_t)h * nb + t] = (float)(sv / R);
+        float* ts = tile_sums + (size_t)h * 4 * nb;
+        ts[t] = (float)(slo0 / R);
+        ts[nb + t] = (float)(sup0 / R);
+        ts[2 * nb + t] = (float)(slo1 / R);
+        ts[3 * nb + t] = (float)(sup1 / R);
+    }
+}
+
+// grid (ceil(Nb / 256), hq), 256 threads.  Slash block t collects the lower
+// parts of tile t (rows with e = 0) and t-1 (e = 1) and the upper parts of
+// tile t-1 (e = 0) and t-2 (e = 1).
+__global__ void __launch_bounds__(256)
+finalize_kernel(const float* __restrict__ tile_sums, const float* __restrict__ p_v, int nb,
+                float tau, int route_here, float* __restrict__ p_s, float* __restrict__ c_struct,
+                uint8_t* __restrict__ pattern)
+{
+    const int h = blockIdx.y;
+    const int t = blockIdx.x * 256 + threadIdx.x;
+    const float* ts = tile_sums + (size_t)h * 4 * nb;
+    if (t < nb) {
+        float ps = ts[t];
+        if (t >= 1) ps += ts[nb + t - 1] + ts[2 * nb + t - 1];
+        if (t >= 2) ps += ts[3 * nb + t - 2];
         p_s[(size_t)h * nb + t] = ps;
     }
-    if (tid == 0 && route_here) {
+    if (blockIdx.x == 0 && threadIdx.x == 0 && route_here) {
         // Eq. 2 with w_sink = w_local = B: the first and the last key block
-        const float cs = (nb > 1) ? pv_ends[0] + pv_ends[1] : pv_ends[0];
+        const float* pv = p_v + (size_t)h * nb;
+        const float cs = (nb > 1) ? pv[0] + pv[nb - 1] : pv[0];
         c_struct[h] = cs;
         pattern[h] = (cs >= tau) ? 1 : 0;
     }
@@ -370,22 +395,31 @@ hipError_t launch_route(Rows q, Rows k, int n, int hq, int hkv,
     const int nb = (n + kB - 1) / kB;
     const int G = hq / hkv;
     const float scale_log2 = kLog2e / sqrtf((float)kD);
-    // enough work-groups to fill 256 CUs several times over
+    // enough work-groups to fill 256 CUs a few times over
     int tiles_per_wg = 1;
     while (tiles_per_wg < 8 && (size_t)((nb + 2 * tiles_per_wg - 1) / (2 * tiles_per_wg)) * hkv >= 1024)
         tiles_per_wg *= 2;
     dim3 grid((nb + tiles_per_wg - 1) / tiles_per_wg, hkv * ((G + 3) / 4));
     if (n % kB == 0)
-        hipLaunchKernelGGL(proxy_map_kernel<true>, grid, dim3(256), 0, stream, q, k, n, nb, G,
+        hipLaunchKernelGGL(proxy_map_kernel<true>, grid, dim3(1024), 0, stream, q, k, n, nb, G,
                            tiles_per_wg, scale_log2, a.part_m, a.part_lo, a.part_up);
     else
-        hipLaunchKernelGGL(proxy_map_kernel<false>, grid, dim3(256), 0, stream, q, k, n, nb, G,
+        hipLaunchKernelGGL(proxy_map_kernel<false>, grid, dim3(1024), 0, stream, q, k, n, nb, G,
                            tiles_per_wg, scale_log2, a.part_m, a.part_lo, a.part_up);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int route_here = a.router == 0;
-    hipLaunchKernelGGL(mass_reduce_kernel, dim3(hq), dim3(1024), 0, stream, a.part_m, a.part_lo,
-                       a.part_up, n, nb, a.tau, route_here, p_v, p_s, c_struct, pattern);
+    hipLaunchKernelGGL(row_part_kernel, dim3(kSegs, hq), dim3(kB), 0, stream, a.part_m, a.part_lo,
+                       a.part_up, n, nb, a.seg_m, a.seg_l);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL(row_norm_kernel, dim3(hq), dim3(1024), 0, stream, a.seg_m, a.seg_l, n,
+                       a.row_mx, a.row_inv);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL(tile_mass_kernel, dim3((nb + 15) / 16, hq), dim3(1024), 0, stream, a.part_m,
+                       a.part_lo, a.part_up, a.row_mx, a.row_inv, n, nb, p_v, a.tile_sums);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL(finalize_kernel, dim3((nb + 255) / 256, hq), dim3(256), 0, stream, a.tile_sums,
+                       p_v, nb, a.tau, route_here, p_s, c_struct, pattern);
     if ((e = hipGetLastError()) != hipSuccess || route_here) return e;
     hipLaunchKernelGGL(jsd_pool_kernel, dim3(nb, hkv + hq), dim3(256), 0, stream, q, k, n, nb, hkv,
                        a.jsd_kbar, a.jsd_qbar);

@@ -314,43 +314,69 @@ pe_pool_kernel(Rows q, Rows k,
     }
 }
 
-// grid (ceil(Nb/16), hq): scaled pooled logits of 16 query blocks against
-// every causal key block, log2 domain, triangular row layout.
+// grid (ceil(Nb/32), ceil(Nb/128), hq), 256 threads: scaled pooled logits
+// Q̄ K̄^T of a 32-query-block tile against four 32-key-block tiles, one per
+// wavefront, on the fp32 matrix cores (v_mfma_f32_32x32x2_f32, 64 steps
+// over d), log2 domain, triangular row layout; tiles above the diagonal
+// are skipped.
 __global__ void __launch_bounds__(256)
 pe_logits_kernel(const float* __restrict__ qbar, const float* __restrict__ kbar,
                  const uint8_t* __restrict__ pattern, int nb, int G, float scale_log2,
                  float* __restrict__ abar)
 {
-    __shared__ float qs[16][kD];
-    __shared__ float kst[64][kD + 1];
-    const int h = blockIdx.y, tid = threadIdx.x;
+    constexpr int kP = kD + 1;                   // LDS pitch (floats)
+    __shared__ float qs[32 * kP];
+    __shared__ float kst[128 * kP];
+    const int h = blockIdx.z, tid = threadIdx.x;
     if (pattern[h]) return;
+    const int qt = blockIdx.x, kt0 = 4 * blockIdx.y;
+    if (kt0 > qt) return;                        // every tile above the diagonal
     const int g = h / G;
-    const int r0 = blockIdx.x * 16;
-    const size_t tri_total = tri(nb);
-    for (int e = tid; e < 16 * kD; e += 256) {
-        const int r = e / kD, c = e % kD;
-        qs[r][c] = (r0 + r < nb) ? qbar[((size_t)h * nb + r0 + r) * kD + c] : 0.f;
+    // stage both operands with every load in flight at once: 4 + 16 float4
+    // per thread, then the LDS stores
+    f32x4 qv[4], kv[16];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int e = tid + 256 * j, r = e >> 5, qb = 32 * qt + r;
+        qv[j] = (qb < nb) ? *reinterpret_cast<const f32x4*>(qbar + ((size_t)h * nb + qb) * kD + 4 * (e & 31))
+                          : f32x4{0.f, 0.f, 0.f, 0.f};
     }
-    const int row = tid >> 4, c4 = (tid & 15) * 4;
-    const int qb = r0 + row;
-    const int kb_end = min(nb, r0 + 16);
-    for (int kb0 = 0; kb0 < kb_end; kb0 += 64) {
-        __syncthreads();
-        for (int e = tid; e < 64 * kD; e += 256) {
-            const int r = e / kD, c = e % kD;
-            kst[r][c] = (kb0 + r < nb) ? kbar[((size_t)g * nb + kb0 + r) * kD + c] : 0.f;
-        }
-        __syncthreads();
-        float acc[4] = {0.f, 0.f, 0.f, 0.f};
-        for (int c = 0; c < kD; ++c) {
-            const float x = qs[row][c];
-            for (int j = 0; j < 4; ++j) acc[j] += x * kst[c4 + j][c];
-        }
-        for (int j = 0; j < 4; ++j) {
-            const int kb = kb0 + c4 + j;
-            if (qb < nb && kb <= qb) abar[(size_t)h * tri_total + tri(qb) + kb] = acc[j] * scale_log2;
-        }
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+        const int e = tid + 256 * j, r = e >> 5, kb = 32 * kt0 + r;
+        kv[j] = (kb < nb) ? *reinterpret_cast<const f32x4*>(kbar + ((size_t)g * nb + kb) * kD + 4 * (e & 31))
+                          : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int e = tid + 256 * j;
+        for (int x = 0; x < 4; ++x) qs[(e >> 5) * kP + 4 * (e & 31) + x] = qv[j][x];
+    }
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+        const int e = tid + 256 * j;
+        for (int x = 0; x < 4; ++x) kst[(e >> 5) * kP + 4 * (e & 31) + x] = kv[j][x];
+    }
+    __syncthreads();
+    const int w = tid >> 6, lane = tid & 63, l32 = lane & 31, hi = lane >> 5;
+    const int kt = kt0 + w;
+    if (kt > qt) return;
+    // D[m][n] = sum_d Q̄[32 qt + m][d] K̄[32 kt + n][d]; step s covers d = 2s, 2s+1
+    // (A: lane l holds row l % 32, d = 2s + l / 32; B likewise for keys)
+    // (two independent accumulation chains over alternate steps)
+    f32x16 acc = f32x16{}, acc1 = f32x16{};
+    const float* qa = qs + l32 * kP + hi;
+    const float* kb_ = kst + (32 * w + l32) * kP + hi;
+    for (int s = 0; s < kD / 2; s += 2) {
+        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(qa[2 * s], kb_[2 * s], acc, 0, 0, 0);
+        acc1 = __builtin_amdgcn_mfma_f32_32x32x2f32(qa[2 * s + 2], kb_[2 * s + 2], acc1, 0, 0, 0);
+    }
+    acc += acc1;
+    const size_t base = (size_t)h * tri(nb);
+    const int kb = 32 * kt + l32;
+    for (int r = 0; r < 16; ++r) {
+        const int qb = 32 * qt + 8 * (r >> 2) + 4 * hi + (r & 3);
+        if (qb < nb && kb <= qb) abar[base + tri(qb) + kb] = acc[r] * scale_log2;
     }
 }
 
@@ -646,7 +672,8 @@ hipError_t launch_select(Rows q, Rows k, const uint8_t* pattern,
                        hq, G, s.qbar, s.kbar);
     CRISP_CHECK_LAUNCH();
     const float scale_log2 = kLog2e / sqrtf((float)kD);
-    hipLaunchKernelGGL(pe_logits_kernel, dim3((nb + 15) / 16, hq), dim3(256), 0, stream, s.qbar,
+    hipLaunchKernelGGL(pe_logits_kernel, dim3((nb + 31) / 32, (nb + 127) / 128, hq), dim3(256), 0,
+                       stream, s.qbar,
                        s.kbar, pattern, nb, G, scale_log2, s.abar);
     CRISP_CHECK_LAUNCH();
     hipLaunchKernelGGL(pe_softmax_kernel, dim3((nb + 3) / 4, hq), dim3(256), 0, stream, pattern, nb,
