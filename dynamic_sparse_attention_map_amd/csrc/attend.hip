@@ -284,10 +284,6 @@ attend_pair(int b, uint16_t* lds, uint32_t* list, Rows q, Rows k,
         }
     };
     // p = 2^(c s - c m) (one FMA and one v_exp), rounded to bf16 into the
-    // P^T operand, then O^T += V^T P^T.  Probabilities of key group u + 1
-    // are computed while the matrix cores run group u; a lane whose keys
-    // are all masked so far keeps m = -inf and uses 0 as its reference.
-    // p = 2^(c s - c m) (one FMA and one v_exp), rounded to bf16 into the
     // P^T operand; a lane whose keys are all masked so far keeps m = -inf
     // and uses 0 as its reference
     bf16x8 pf[4];
