@@ -27,7 +27,7 @@ struct Shape {
 struct Layout {
     size_t part_m, part_lo, part_up, jsd_kbar, jsd_qbar;   // route (in S)
     size_t seg_m, seg_l, row_mx, row_inv, tile_sums;       // route reduction (in S)
-    size_t qbar, kbar, abar, hist_mass, hist_count, state, bitmap;   // select (in S)
+    size_t qbar, kbar, abar, hist_mass, hist_count, pass_ctr, state, bitmap;   // select (in S)
     size_t vt, queue;                                      // attend (in S)
     size_t route_end, select_end, attend_end;              // bytes of S each stage needs
     size_t pattern, c_struct, p_v, p_s, sel_v, sel_s, counts, row_ptr, col_idx;  // P
@@ -62,8 +62,9 @@ Layout make_layout(const Shape& s)
     L.qbar = take(hq * nb * kD * sizeof(float));
     L.kbar = take(hkv * nb * kD * sizeof(float));
     L.abar = take(hq * tri * sizeof(float));
-    L.hist_mass = take(hq * 256 * sizeof(unsigned long long));
-    L.hist_count = take(hq * 256 * sizeof(uint32_t));
+    L.hist_mass = take(hq * kValPasses * kValBins * sizeof(unsigned long long));
+    L.hist_count = take(hq * kRadixPasses * kFlatBins * sizeof(uint32_t));
+    L.pass_ctr = take(hq * kRadixPasses * sizeof(uint32_t));
     L.state = take(hq * sizeof(PeState));
     L.bitmap = take(hq * 2 * nb);
     L.select_end = o;
@@ -204,6 +205,7 @@ int do_select(const Shape& s, const Opts& op, float alpha, Rows q, Rows k,
     sc.abar = at<float>(ws, L.abar);
     sc.hist_mass = at<unsigned long long>(ws, L.hist_mass);
     sc.hist_count = at<uint32_t>(ws, L.hist_count);
+    sc.pass_ctr = at<uint32_t>(ws, L.pass_ctr);
     sc.state = at<PeState>(ws, L.state);
     sc.bitmap = at<uint8_t>(ws, L.bitmap);
     VsRule vr;

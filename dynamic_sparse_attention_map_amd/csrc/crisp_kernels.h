@@ -39,6 +39,12 @@ struct PeState {
     uint32_t pad[4];
 };
 
+// Radix select of the PE cut-off: value-key passes and flat-index passes.
+constexpr int kValPasses = 3;      // 11 + 11 + 10 bits of the 32-bit key
+constexpr int kRadixPasses = 5;    // then 12 + 12 bits of the 24-bit flat index
+constexpr int kValBins = 2048;
+constexpr int kFlatBins = 4096;
+
 // Fixed point used for masses: value * 2^62 truncated (values are <= 1).
 constexpr double kFix = 4611686018427387904.0;
 
@@ -72,8 +78,9 @@ struct SelectScratch {
     float* qbar;                    // [hq][Nb][128]
     float* kbar;                    // [hkv][Nb][128]
     float* abar;                    // [hq][Nb(Nb+1)/2] triangular rows
-    unsigned long long* hist_mass;  // [hq][256]
-    uint32_t* hist_count;           // [hq][256]
+    unsigned long long* hist_mass;  // [hq][kValPasses][kValBins]
+    uint32_t* hist_count;           // [hq][kRadixPasses][kFlatBins]
+    uint32_t* pass_ctr;             // [hq][kRadixPasses]
     PeState* state;                 // [hq]
     uint8_t* bitmap;                // [hq][2][Nb]
 };

@@ -248,18 +248,26 @@ vs_select_kernel(const uint8_t* __restrict__ pattern, const float* __restrict__ 
     if (tid == 0) counts[h * 3 + dir] = kept;
 }
 
-__global__ void pe_init_kernel(const uint8_t* __restrict__ pattern, float gamma,
-                               unsigned long long* __restrict__ hist_mass,
-                               uint32_t* __restrict__ hist_count, PeState* __restrict__ state)
+// grid (hq), 1024 threads: clear the head's radix histograms and pass
+// counters, and seed its cut-off state.
+__global__ void __launch_bounds__(1024)
+pe_init_kernel(const uint8_t* __restrict__ pattern, float gamma,
+               unsigned long long* __restrict__ hist_mass, uint32_t* __restrict__ hist_count,
+               uint32_t* __restrict__ pass_ctr, PeState* __restrict__ state)
 {
     const int h = blockIdx.x, tid = threadIdx.x;
-    hist_mass[h * 256 + tid] = 0ull;
-    hist_count[h * 256 + tid] = 0u;
+    if (pattern[h] == 0) {
+        for (int i = tid; i < kValPasses * kValBins; i += 1024)
+            hist_mass[(size_t)h * kValPasses * kValBins + i] = 0ull;
+        for (int i = tid; i < kRadixPasses * kFlatBins; i += 1024)
+            hist_count[(size_t)h * kRadixPasses * kFlatBins + i] = 0u;
+        if (tid < kRadixPasses) pass_ctr[h * kRadixPasses + tid] = 0u;
+    }
     if (tid == 0) {
-        PeState s = {};
-        s.need = (unsigned long long)((double)gamma * kFix);
-        s.done = pattern[h] ? 1u : 0u;
-        state[h] = s;
+        PeState st = {};
+        st.need = (unsigned long long)((double)gamma * kFix);
+        st.done = pattern[h] ? 1u : 0u;
+        state[h] = st;
     }
 }
 
@@ -399,134 +407,202 @@ pe_softmax_kernel(const uint8_t* __restrict__ pattern, int nb, float* __restrict
     for (int kb = lane; kb <= qb; kb += 64) row[kb] = (float)((double)exp2f(row[kb] - m) * inv);
 }
 
-// One radix digit of the cut-off: pass 0..3 histogram the value key (value
-// descending == key ascending) 8 bits at a time, weighting by mass; pass
-// 4..6 histogram the flat index qb*Nb+kb of the entries equal to the cut-off
-// value, by count.  grid (ceil(Nb/8), hq).
-__global__ void __launch_bounds__(256)
-pe_hist_kernel(const uint8_t* __restrict__ pattern, int nb, int pass,
-               const float* __restrict__ abar, const PeState* __restrict__ state,
-               unsigned long long* __restrict__ hist_mass, uint32_t* __restrict__ hist_count)
+// The gamma cut-off of a PE head (Alg. 4: the shortest prefix of the map
+// sorted by value, descending, ties by flat index qb*Nb+kb ascending, whose
+// mass reaches gamma) as a mass-weighted radix select in five passes.  Keys
+// are key = ~bits(value), ascending in value-descending order.  Passes 0-2
+// histogram the key 11, 11 and 10 bits at a time (count and fixed-point
+// mass per digit) among the entries that match the digits resolved so far;
+// passes 3-4 histogram the flat index (12 + 12 bits) of the entries whose
+// key equals the cut-off key, by count.  Each work-group takes a contiguous
+// range of the head's triangular map; the last work-group of a pass to
+// finish (a per-head counter) scans the global histogram and resolves the
+// pass's digit into the head's state.
+constexpr int kRadixChunk = 4096;          // map entries per work-group
+
+__device__ __forceinline__ int pass_shift(int pass)
 {
-    __shared__ uint32_t cnt[256];
-    __shared__ unsigned long long mass[256];
-    const int h = blockIdx.y, tid = threadIdx.x;
-    if (pattern[h]) return;
-    const PeState st = state[h];
-    if (st.done) return;
-    cnt[tid] = 0u;
-    mass[tid] = 0ull;
+    return pass == 0 ? 21 : pass == 1 ? 10 : pass == 2 ? 0 : pass == 3 ? 12 : 0;
+}
+__device__ __forceinline__ int pass_bits(int pass)
+{
+    return pass < 2 ? 11 : pass == 2 ? 10 : 12;
+}
+
+// Exclusive scan of one value per thread over a 256-thread block; total too.
+template <typename T>
+__device__ T block_scan_256(T v, T* wsum, T* total)
+{
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    T x = v;
+    for (int o = 1; o < 64; o <<= 1) {
+        const T y = __shfl_up(x, o);
+        if (lane >= o) x += y;
+    }
+    if (lane == 63) wsum[w] = x;
     __syncthreads();
-    const float* base = abar + (size_t)h * tri(nb);
-    const int r0 = blockIdx.x * 8, r1 = min(nb, r0 + 8);
-    for (int qb = r0; qb < r1; ++qb) {
-        const float* row = base + tri(qb);
-        for (int kb = tid; kb <= qb; kb += 256) {
-            const float v = row[kb];
-            const uint32_t key = ~__float_as_uint(v);
-            if (pass < 4) {
-                const int shift = 24 - 8 * pass;
-                if (pass > 0 && (key >> (shift + 8)) != st.key_prefix) continue;
-                const int dgt = (key >> shift) & 255;
-                atomicAdd(&cnt[dgt], 1u);
-                atomicAdd(&mass[dgt], to_fix(v));
-            } else {
-                if (key != st.key_star) continue;
-                const uint32_t flat = (uint32_t)qb * (uint32_t)nb + (uint32_t)kb;
-                const int shift = 16 - 8 * (pass - 4);
-                if (pass > 4 && (flat >> (shift + 8)) != st.flat_prefix) continue;
-                atomicAdd(&cnt[(flat >> shift) & 255], 1u);
-            }
+    T before = 0;
+    for (int i = 0; i < w; ++i) before += wsum[i];
+    *total = wsum[0] + wsum[1] + wsum[2] + wsum[3];
+    __syncthreads();
+    return before + x - v;
+}
+
+// grid (ceil(tri(Nb) / kRadixChunk), hq), 256 threads
+__global__ void __launch_bounds__(256)
+pe_radix_kernel(int nb, int pass,
+                const float* __restrict__ abar, PeState* __restrict__ state,
+                unsigned long long* __restrict__ hist_mass, uint32_t* __restrict__ hist_count,
+                uint32_t* __restrict__ pass_ctr)
+{
+    __shared__ uint32_t cnt[kFlatBins];
+    __shared__ unsigned long long mass[kValBins];
+    __shared__ unsigned long long wsum_m[4];
+    __shared__ uint32_t wsum_c[4];
+    __shared__ int s_last;
+    const int h = blockIdx.y, tid = threadIdx.x;
+    const PeState st = state[h];
+    if (st.done) return;                // VS heads start done (pe_init_kernel)
+    const bool val = pass < kValPasses;
+    const int shift = pass_shift(pass), bits = pass_bits(pass);
+    const int bins = 1 << bits;
+    for (int i = tid; i < bins; i += 256) {
+        cnt[i] = 0u;
+        if (val) mass[i] = 0ull;
+    }
+    __syncthreads();
+    const size_t total = tri(nb);
+    const float* base = abar + (size_t)h * total;
+    const size_t e0 = (size_t)blockIdx.x * kRadixChunk;
+    const size_t e1 = min(total, e0 + kRadixChunk);
+    // all of this thread's entries in flight at once
+    constexpr int kPer = kRadixChunk / 256;
+    float vals[kPer];
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+        const size_t e = e0 + tid + 256 * j;
+        vals[j] = (e < e1) ? base[e] : 0.f;
+    }
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+        const size_t e = e0 + tid + 256 * j;
+        if (e >= e1) break;
+        const float v = vals[j];
+        const uint32_t key = ~__float_as_uint(v);
+        if (val) {
+            if (pass > 0 && (key >> (shift + bits)) != st.key_prefix) continue;
+            const int d = (key >> shift) & (bins - 1);
+            atomicAdd(&cnt[d], 1u);
+            atomicAdd(&mass[d], to_fix(v));
+        } else {
+            if (key != st.key_star) continue;
+            // row of entry e: the largest qb with qb (qb + 1) / 2 <= e
+            int qb = (int)((sqrt(8.0 * (double)e + 1.0) - 1.0) * 0.5);
+            while (tri(qb + 1) <= e) ++qb;
+            while (tri(qb) > e) --qb;
+            const uint32_t flat = (uint32_t)qb * (uint32_t)nb + (uint32_t)(e - tri(qb));
+            if (pass > kValPasses && (flat >> (shift + bits)) != st.flat_prefix) continue;
+            atomicAdd(&cnt[(flat >> shift) & (bins - 1)], 1u);
         }
     }
     __syncthreads();
-    if (cnt[tid]) {
-        atomicAdd(&hist_count[h * 256 + tid], cnt[tid]);
-        if (pass < 4) atomicAdd(&hist_mass[h * 256 + tid], mass[tid]);
+    uint32_t* gc = hist_count + ((size_t)h * kRadixPasses + pass) * kFlatBins;
+    unsigned long long* gm = hist_mass + ((size_t)h * kValPasses + (val ? pass : 0)) * kValBins;
+    for (int i = tid; i < bins; i += 256) {
+        if (cnt[i]) {
+            atomicAdd(&gc[i], cnt[i]);
+            if (val) atomicAdd(&gm[i], mass[i]);
+        }
     }
-}
+    // The histogram atomics are performed at the device's coherence point;
+    // waiting for them to complete (vmcnt) before the counter increment
+    // orders them without a cache write-back (a __threadfence() writes back
+    // and invalidates the XCD's L2, which costs more than the pass itself).
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (tid == 0) {
+        const uint32_t nwg = gridDim.x;
+        s_last = atomicAdd(&pass_ctr[h * kRadixPasses + pass], 1u) == nwg - 1;
+    }
+    __syncthreads();
+    if (!s_last) return;
+    // every other work-group's atomics are complete: read them coherently
 
-// grid hq, 256 threads (one per digit): pick the digit where the running
-// mass (count, for flat passes) reaches what is still needed.
-__global__ void __launch_bounds__(256)
-pe_resolve_kernel(const uint8_t* __restrict__ pattern, int nb, int pass,
-                  unsigned long long* __restrict__ hist_mass, uint32_t* __restrict__ hist_count,
-                  PeState* __restrict__ state)
-{
-    __shared__ unsigned long long smass[256];
-    __shared__ uint32_t scnt[256];
-    __shared__ PeState cur;
-    const int h = blockIdx.x, tid = threadIdx.x;
-    if (pattern[h]) return;
-    if (tid == 0) cur = state[h];
-    __syncthreads();
-    if (cur.done) return;
-    const uint32_t c = hist_count[h * 256 + tid];
-    const unsigned long long m = hist_mass[h * 256 + tid];
-    scnt[tid] = c;
-    smass[tid] = m;
-    __syncthreads();
-    // inclusive scans (Hillis-Steele; 256 entries)
-    for (int o = 1; o < 256; o <<= 1) {
-        const uint32_t yc = (tid >= o) ? scnt[tid - o] : 0u;
-        const unsigned long long ym = (tid >= o) ? smass[tid - o] : 0ull;
-        __syncthreads();
-        scnt[tid] += yc;
-        smass[tid] += ym;
-        __syncthreads();
+    // ---- resolve: this work-group saw every other one finish the pass ----
+    const int per = bins / 256;                       // consecutive bins per thread
+    uint32_t c_loc = 0;
+    unsigned long long m_loc = 0;
+    for (int j = 0; j < per; ++j) {
+        const int i = tid * per + j;
+        cnt[i] = __hip_atomic_load(&gc[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        c_loc += cnt[i];
+        if (val) {
+            mass[i] = __hip_atomic_load(&gm[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            m_loc += mass[i];
+        }
     }
-    hist_count[h * 256 + tid] = 0u;
-    hist_mass[h * 256 + tid] = 0ull;
-    const uint32_t incl_c = scnt[tid], excl_c = incl_c - c;
-    const unsigned long long incl_m = smass[tid], excl_m = incl_m - m;
-    PeState& st = state[h];   // written by exactly one thread below
-    if (pass < 4) {
-        const unsigned long long need = cur.need;
-        if (smass[255] < need) {
+    uint32_t c_all;
+    unsigned long long m_all;
+    uint32_t c_before = block_scan_256(c_loc, wsum_c, &c_all);
+    unsigned long long m_before = val ? block_scan_256(m_loc, wsum_m, &m_all) : 0ull;
+    if (val) {
+        const unsigned long long need = st.need;
+        if (m_all < need) {
             // the kept mass never reaches gamma: keep every causal entry
             if (tid == 0) {
-                PeState nx = cur;
+                PeState nx = st;
                 nx.key_star = 0xffffffffu;
                 nx.flat_star = 0xffffffffu;
-                nx.kstar = (uint32_t)tri(nb);
+                nx.kstar = (uint32_t)total;
                 nx.done = 1u;
-                st = nx;
+                state[h] = nx;
             }
             return;
         }
-        if (incl_m >= need && excl_m < need) {
-            PeState nx = cur;
-            nx.need = need - excl_m;
-            nx.before = cur.before + excl_c;
-            nx.key_prefix = (cur.key_prefix << 8) | (uint32_t)tid;
-            if (pass == 3) {
-                nx.key_star = nx.key_prefix;
-                const float tv = __uint_as_float(~nx.key_star);
-                const unsigned long long tf = to_fix(tv);
-                const unsigned long long ties = (nx.need + tf - 1) / tf;
-                nx.tfix = tf;
-                if (ties >= c) {
-                    nx.flat_star = 0xffffffffu;
-                    nx.kstar = nx.before + c;
-                    nx.done = 1u;
-                } else {
-                    nx.tie_need = (uint32_t)ties;
-                    nx.kstar = nx.before + (uint32_t)ties;
+        for (int j = 0; j < per; ++j) {
+            const int i = tid * per + j;
+            const unsigned long long incl = m_before + mass[i];
+            if (m_before < need && incl >= need) {
+                PeState nx = st;
+                nx.need = need - m_before;
+                nx.before = st.before + c_before;
+                nx.key_prefix = (st.key_prefix << bits) | (uint32_t)i;
+                if (pass == kValPasses - 1) {
+                    nx.key_star = nx.key_prefix;
+                    const float tv = __uint_as_float(~nx.key_star);
+                    const unsigned long long tf = to_fix(tv);
+                    const unsigned long long ties = (nx.need + tf - 1) / tf;
+                    nx.tfix = tf;
+                    if (ties >= cnt[i]) {
+                        nx.flat_star = 0xffffffffu;
+                        nx.kstar = nx.before + cnt[i];
+                        nx.done = 1u;
+                    } else {
+                        nx.tie_need = (uint32_t)ties;
+                        nx.kstar = nx.before + (uint32_t)ties;
+                    }
                 }
+                state[h] = nx;
             }
-            st = nx;
+            m_before = incl;
+            c_before += cnt[i];
         }
     } else {
-        const uint32_t need = cur.tie_need;
-        if (incl_c >= need && excl_c < need) {
-            PeState nx = cur;
-            nx.tie_need = need - excl_c;
-            nx.flat_prefix = (cur.flat_prefix << 8) | (uint32_t)tid;
-            if (pass == 6) {
-                nx.flat_star = nx.flat_prefix;
-                nx.done = 1u;
+        const uint32_t need = st.tie_need;
+        for (int j = 0; j < per; ++j) {
+            const int i = tid * per + j;
+            const uint32_t incl = c_before + cnt[i];
+            if (c_before < need && incl >= need) {
+                PeState nx = st;
+                nx.tie_need = need - c_before;
+                nx.flat_prefix = (st.flat_prefix << bits) | (uint32_t)i;
+                if (pass == kRadixPasses - 1) {
+                    nx.flat_star = nx.flat_prefix;
+                    nx.done = 1u;
+                }
+                state[h] = nx;
             }
-            st = nx;
+            c_before = incl;
         }
     }
 }
@@ -665,8 +741,8 @@ hipError_t launch_select(Rows q, Rows k, const uint8_t* pattern,
     hipLaunchKernelGGL(vs_select_kernel, dim3(hq, 2), dim3(1024), 0, stream, pattern, p_v, p_s, nb,
                        vs, sel_v, sel_s, sel_counts, s.bitmap);
     CRISP_CHECK_LAUNCH();
-    hipLaunchKernelGGL(pe_init_kernel, dim3(hq), dim3(256), 0, stream, pattern, gamma, s.hist_mass,
-                       s.hist_count, s.state);
+    hipLaunchKernelGGL(pe_init_kernel, dim3(hq), dim3(1024), 0, stream, pattern, gamma, s.hist_mass,
+                       s.hist_count, s.pass_ctr, s.state);
     CRISP_CHECK_LAUNCH();
     hipLaunchKernelGGL(pe_pool_kernel, dim3(nb, hq + hkv), dim3(256), 0, stream, q, k, pattern, n,
                        hq, G, s.qbar, s.kbar);
@@ -679,12 +755,11 @@ hipError_t launch_select(Rows q, Rows k, const uint8_t* pattern,
     hipLaunchKernelGGL(pe_softmax_kernel, dim3((nb + 3) / 4, hq), dim3(256), 0, stream, pattern, nb,
                        s.abar);
     CRISP_CHECK_LAUNCH();
-    for (int pass = 0; pass < 7; ++pass) {
-        hipLaunchKernelGGL(pe_hist_kernel, dim3((nb + 7) / 8, hq), dim3(256), 0, stream, pattern, nb,
-                           pass, s.abar, s.state, s.hist_mass, s.hist_count);
-        CRISP_CHECK_LAUNCH();
-        hipLaunchKernelGGL(pe_resolve_kernel, dim3(hq), dim3(256), 0, stream, pattern, nb, pass,
-                           s.hist_mass, s.hist_count, s.state);
+    const long long tri_nb = (long long)nb * (nb + 1) / 2;
+    const dim3 radix_grid((unsigned)((tri_nb + kRadixChunk - 1) / kRadixChunk), hq);
+    for (int pass = 0; pass < kRadixPasses; ++pass) {
+        hipLaunchKernelGGL(pe_radix_kernel, radix_grid, dim3(256), 0, stream, nb, pass,
+                           s.abar, s.state, s.hist_mass, s.hist_count, s.pass_ctr);
         CRISP_CHECK_LAUNCH();
     }
     const dim3 rows_grid((nb + kRowsPerGroup - 1) / kRowsPerGroup, hq);
