@@ -30,7 +30,6 @@ constexpr int kStageBytes = 4 * kImg;     // K image, then V^T image
 constexpr int kStages = 4;                // LDS ring depth
 
 constexpr int kThreads = 512;             // 8 wavefronts: two query blocks x 4
-constexpr int kEnd = 0x7fffffff;           // list exhausted
 
 constexpr int kListWords = kMaxBlocks / 32;   // bitmap words per row
 constexpr int kPairRun = 256;                  // longest run of one head's pairs
@@ -228,7 +227,7 @@ attend_pair(int b, uint16_t* lds, uint32_t* list, Rows q, Rows k,
     };
 
     // Instruction-group masks for __builtin_amdgcn_sched_group_barrier.
-    constexpr int kSchedValu = 0x002, kSchedMfma = 0x008, kSchedDsRead = 0x100;
+    constexpr int kSchedMfma = 0x008, kSchedDsRead = 0x100;
 
     const int kx = l32 & 15, vx = (l32 >> 1) & 7;   // this lane's swizzles
     f32x16 s[2];
