@@ -184,3 +184,19 @@ def test_gate_option_validated(L):
                            FAKE, 1 << 30, FAKE, None) == INVALID
     assert L.crisp_prefill(None, None, None, 0, 4, 1, 128, 128, 1.0,
                            _opts(dense_below_tokens=1 << 20), None, 0, None, None) == OK
+
+
+def test_batch_binding_rejects_mismatched_views():
+    """The binding's own checks (no call reaches the library)."""
+    import torch
+    q = torch.zeros(4, 10, 128, dtype=torch.bfloat16)
+    k = torch.zeros(1, 10, 128, dtype=torch.bfloat16)
+    ws = torch.zeros(256, dtype=torch.uint8)
+    with pytest.raises(ValueError):
+        crisp.crisp_prefill_batch([q], [k, k], [k], [q], 1.0, ws)
+    with pytest.raises(ValueError):          # lengths differ inside a sequence
+        crisp.crisp_prefill_batch([q], [k[:, :5]], [k], [q], 1.0, ws)
+    with pytest.raises(ValueError):          # head_dim not contiguous
+        qt = torch.zeros(4, 128, 10, dtype=torch.bfloat16).transpose(1, 2)
+        crisp.crisp_prefill_batch([qt], [k.transpose(1, 2).contiguous().transpose(1, 2)], [k], [q],
+                                  1.0, ws)

@@ -261,3 +261,30 @@ def test_flexprefill_baseline(name):
     crisp.crisp_prefill(q, k, v, 1.0, crisp.alloc_workspace(n, hq, hkv), out2, opts=opts)
     staged = P.gpu_attend(q, k, v, gs["row_ptr"], gs["col_idx"], crisp.alloc_workspace(n, hq, hkv))
     assert torch.equal(out2.view(torch.int16), staged.view(torch.int16))
+
+
+def test_flexprefill_ragged():
+    """The baseline's router and rule on a ragged length (partial last block
+    in the key means, the pooled estimate and the gamma rule)."""
+    n, hq, hkv = 3000 + 57, 4, 2
+    sp = synth.custom_spec(n, hq, hkv, [synth.VS, synth.DIFFUSE, synth.VS, synth.VS], seed_id=130)
+    inp = synth.generate(sp)
+    nb = -(-n // B)
+    opts = crisp.flexprefill_opts()
+    q, k, v = P.to_dev(inp)
+    ws = crisp.alloc_workspace(n, hq, hkv)
+    gr = P.gpu_route(q, k, ws, opts=opts)
+    grh = P.host(gr)
+    orc_r = O.route_jsd(inp.q, inp.k, n, hq, hkv)
+    P.check_route_jsd(grh, orc_r)
+    gs = P.host(P.gpu_select(q, k, gr, 1.0, ws, opts=opts))
+    same = [h for h in range(hq) if grh["pattern"][h] == orc_r.pattern[h]]
+    P.log(P.check_select(inp, grh, gs, 1.0, orc_r, heads=same, vs_rule="gamma").line() + " ragged fp")
+    out = torch.empty_like(q)
+    crisp.crisp_prefill(q, k, v, 1.0, crisp.alloc_workspace(n, hq, hkv), out, opts=opts)
+    rows = np.arange(hq * nb, dtype=np.int32)
+    want = O.attend(inp.q, inp.k, inp.v, n, hq, hkv, 128, gs["row_ptr"].reshape(-1), gs["col_idx"],
+                    rows)
+    full = torch.zeros(hq, nb * B, 128)
+    full[:, :n] = out.float().cpu()
+    P.check_outputs(full.numpy().reshape(hq * nb, B, 128), want, "ragged flexprefill prefill")
