@@ -10,6 +10,8 @@ timed on the same inputs for the speedup, and so is the FlexPrefill baseline
 Prints one JSON line.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu]
+    python bench.py --workload c4        # another configuration (context)
+    python bench.py --crossover          # sparse/dense crossover sweep
 """
 from __future__ import annotations
 
@@ -143,6 +145,8 @@ def main():
                     help="skip the FlexPrefill-baseline timing")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="end with a 1 GiB device-to-device copy (reference for counter runs)")
+    ap.add_argument("--workload", default=WORKLOAD,
+                    help="configuration to time (h128, the headline, by default; c1-c4 for context)")
     ap.add_argument("--crossover", action="store_true",
                     help="only sweep n for the sparse/dense crossover and print it")
     args = ap.parse_args()
@@ -159,10 +163,11 @@ def main():
     if args.crossover:
         crossover(args)
         return
-    spec = synth.config_spec(WORKLOAD)
+    workload = args.workload
+    spec = synth.config_spec(workload)
     n, hq, hkv = spec.n, spec.hq, spec.hkv
     nb = -(-n // B)
-    log(f"generating {WORKLOAD}: n={n} hq={hq} hkv={hkv}")
+    log(f"generating {workload}: n={n} hq={hq} hkv={hkv}")
     t0 = time.perf_counter()
     inp = synth.generate(spec, threads=16)
     log(f"generated in {time.perf_counter() - t0:.1f} s")
@@ -286,7 +291,7 @@ def main():
         del out_d
 
     achieved = pairs * PAIR_FLOP / (attend_ms * 1e-3) / 1e12
-    traffic = measured_traffic()
+    traffic = measured_traffic() if workload == WORKLOAD else None
     roofline = {
         "bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS,
         "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
@@ -299,8 +304,11 @@ def main():
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 3),
         "higher_is_better": False, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": "h128: one attention layer, 32 query / 8 KV heads, head_dim 128, "
-                               "131072 tokens, alpha 1.0, 24 vertical-slash + 8 diffuse heads",
+        "config": {"workload": f"{workload}: one attention layer, {hq} query / {hkv} KV heads, "
+                               f"head_dim 128, {n} tokens, alpha {args.alpha:g}, "
+                               f"{sum(1 for hp in spec.heads if hp.kind != synth.DIFFUSE)} "
+                               f"vertical-slash + "
+                               f"{sum(1 for hp in spec.heads if hp.kind == synth.DIFFUSE)} diffuse heads",
                    "seq_len": n, "n_heads": hq, "n_kv_heads": hkv, "head_dim": 128,
                    "block": B, "alpha": args.alpha, "global_batch": 1, "parallelism": "none"},
         "speedup_vs_dense": round(dense_ms / ms_step, 3) if dense_ms else None,
@@ -324,7 +332,7 @@ def main():
         dst.copy_(src)             # reads and writes exactly 1 GiB
         torch.cuda.synchronize()
         del src, dst
-    if not args.no_cpu:
+    if not args.no_cpu and workload == WORKLOAD:
         log("timing the CPU oracle on a bounded sample ...")
         res["cpu_baseline"] = cpu_baseline(inp, pairs, nb, hq, hkv, n)
     print(json.dumps(res), flush=True)
