@@ -314,41 +314,35 @@ attend_pair(int b, uint16_t* lds, uint32_t* list, Rows q, Rows k,
         __builtin_amdgcn_sched_group_barrier(kSchedMfma, 6, 0);
     };
 
-    // Ping-pong schedule.  Per tile t every wavefront runs a matrix-core
-    // phase M_t = PV(t-1) + QK(t) and then a vector-ALU phase V_t = softmax(t),
-    // with a barrier after each phase.  Half 1 starts one barrier late, so in
-    // every phase the two wavefronts that share a SIMD run different kinds of
-    // work (one half's M beside the other half's V) and the matrix cores and
-    // vector ALUs are busy at the same time.  Half 0 runs M_t in phase 2t and
-    // half 1 in phase 2t+1.
-    // Tiles rotate through 4 LDS stages.  Tile t is read in phases 2t .. 2t+3
-    // (K by QK in both halves' M_t, V^T by PV in their M_{t+1}).  Each half
-    // issues its copies of tile t+2 at the start of its M_t (phase 2t or
-    // 2t+1, after the last read of tile t-2 in the same stage) and waits for
-    // them just before the barrier that ends phase 2t+3; tile t+2 is first
-    // read in phase 2t+4.  That barrier ends half 0's V_{t+1} and half 1's
-    // M_{t+1}; each wavefront then has only tile t+3's 4 copies in flight.
+    // Schedule.  Per tile t every wavefront runs a matrix phase M_t = PV(t-1)
+    // + QK(t) and a vector phase V_t = softmax(t); one barrier ends each
+    // iteration.  Half 0 runs M_t then V_t; half 1 runs V_{t-1} then M_t, so
+    // the two wavefronts sharing a SIMD start each iteration on different
+    // units and stay out of each other's way without a barrier in between.
+    // Tiles rotate through 4 LDS stages: tile t is read in iterations t (K)
+    // and t+1 (V^T).  Each wavefront issues its copies of tile t+2 at the
+    // start of iteration t, into the stage of tile t-2 (last read in
+    // iteration t-1), and waits for those of tile t+1 before the barrier
+    // that ends iteration t.
     if (n_tiles > 0) {
         uint32_t d0 = desc_at(0), d1 = desc_at(1), d2 = desc_at(2);
         issue_tile(0, d0);
         if (n_tiles > 1) issue_tile(1, d1);
         wait_copies<0>();
         __syncthreads();
-        if (half == 1) __syncthreads();         // the one-phase skew
         Tile prev{0, 0, false, false};
         for (int t = 0; t < n_tiles; ++t) {
             const Tile cur = tile_of(t, d0);
             const bool more = t + 2 < n_tiles;
-            // ---- M phase ----
             if (more) issue_tile(t + 2, d2);
-            if (t >= 1 && prev.act) pv_mfma((t - 1) & 3);
-            if (cur.act) qk(t & 3);
-            if (half == 1) {
-                if (more) wait_copies<4>(); else wait_copies<0>();
+            if (half == 1 && t >= 1 && prev.act) {          // V_{t-1}
+                if (prev.diag) mask(prev.sub);
+                update_max();
+                probs();
             }
-            __syncthreads();
-            // ---- V phase ----
-            if (cur.act) {
+            if (t >= 1 && prev.act) pv_mfma((t - 1) & 3);   // M_t
+            if (cur.act) qk(t & 3);
+            if (half == 0 && cur.act) {                     // V_t
                 if (cur.diag) mask(cur.sub);
                 update_max();
                 probs();
@@ -356,14 +350,16 @@ attend_pair(int b, uint16_t* lds, uint32_t* list, Rows q, Rows k,
             d0 = d1;
             d1 = d2;
             d2 = desc_at(t + 3);
-            if (half == 0) {
-                if (more) wait_copies<4>(); else wait_copies<0>();
-            }
+            if (more) wait_copies<4>(); else wait_copies<0>();
             __syncthreads();
             prev = cur;
         }
-        if (prev.act) pv_mfma((n_tiles - 1) & 3);   // PV of the last tile
-        if (half == 0) __syncthreads();         // balances the skew
+        if (half == 1 && prev.act) {                        // V of the last tile
+            if (prev.diag) mask(prev.sub);
+            update_max();
+            probs();
+        }
+        if (prev.act) pv_mfma((n_tiles - 1) & 3);           // PV of the last tile
     }
 
     if (!active) return;
