@@ -195,7 +195,8 @@ def main():
     pairs = int((rp[:, nb] - rp[:, 0]).sum())
     dense_pairs = hq * nb * (nb + 1) // 2
     pattern_h = pattern.cpu().numpy()
-    del ws2, col_idx
+    row_pairs = rp[:, nb] - rp[:, 0]
+    del ws2
 
     def events(m):
         evs = [torch.cuda.Event(enable_timing=True) for _ in range(m)]
@@ -221,6 +222,7 @@ def main():
     total_ms = t_start.elapsed_time(t_end)
     ms_step = total_ms / args.steps
     stage = np.array([[e[i].elapsed_time(e[i + 1]) for i in range(4)] for e in step_ev])
+    per_step = np.array([e[0].elapsed_time(e[4]) for e in step_ev])
     st = stage.mean(axis=0)
     route_ms, select_ms, vt_ms, attend_ms = [float(x) for x in st]
     log(f"prefill {ms_step:.3f} ms/step (wall {wall / args.steps * 1e3:.3f}); stages "
@@ -290,6 +292,42 @@ def main():
         log(f"dense {dense_ms:.3f} ms (attention kernel {dense_attend_ms:.3f} ms)")
         del out_d
 
+    # ---- attention time per head type: the same lists with the other
+    # type's rows emptied.  Empty rows still cost their work items' set-up,
+    # so the time of a run with every row empty, scaled by the share of
+    # emptied heads, is also taken off ("net") ----
+    by_type = {}
+    out_t = torch.empty_like(q)
+
+    def attend_ms_on(keep):
+        rp_t = row_ptr.clone()
+        drop = torch.from_numpy(np.nonzero(~keep)[0]).cuda()
+        if drop.numel():
+            rp_t[drop] = rp_t[drop, :1].expand(-1, nb + 1)
+        crisp.crisp_attend(q, k, v, rp_t, col_idx, ws, out_t)
+        t_ev = [events(5) for _ in range(3)]
+        for e in t_ev:
+            crisp.crisp_set_stage_events(e)
+            crisp.crisp_attend(q, k, v, rp_t, col_idx, ws, out_t)
+        crisp.crisp_set_stage_events(None)
+        torch.cuda.synchronize()
+        return float(np.median([e[3].elapsed_time(e[4]) for e in t_ev]))
+
+    empty_ms = attend_ms_on(np.zeros(hq, dtype=bool))
+    for name, sel in (("vertical_slash", pattern_h == 1), ("pooled_estimation", pattern_h == 0)):
+        if not sel.any():
+            continue
+        t_ms = attend_ms_on(sel)
+        net_ms = t_ms - empty_ms * float((~sel).sum()) / hq
+        t_pairs = int(row_pairs[sel].sum())
+        by_type[name] = {"heads": int(sel.sum()), "computed_pairs": t_pairs,
+                         "pairs_per_head": round(t_pairs / int(sel.sum()), 1),
+                         "attend_ms": round(t_ms, 3), "attend_ms_net": round(net_ms, 3),
+                         "attend_tflops_net": round(t_pairs * PAIR_FLOP / (net_ms * 1e-3) / 1e12, 1)}
+        log(f"attention on {name} heads only: {t_ms:.3f} ms ({net_ms:.3f} net), {t_pairs} pairs")
+    by_type["all_rows_empty_ms"] = round(empty_ms, 3)
+    del out_t, col_idx
+
     achieved = pairs * PAIR_FLOP / (attend_ms * 1e-3) / 1e12
     traffic = measured_traffic() if workload == WORKLOAD else None
     roofline = {
@@ -318,6 +356,10 @@ def main():
         "stages_ms": {"route": round(route_ms, 3), "select": round(select_ms, 3),
                       "v_relayout": round(vt_ms, 3), "attend": round(attend_ms, 3)},
         "route_select_frac": round((route_ms + select_ms) / ms_step, 4),
+        "step_ms": {"p10": round(float(np.percentile(per_step, 10)), 3),
+                    "median": round(float(np.median(per_step)), 3),
+                    "p90": round(float(np.percentile(per_step, 90)), 3)},
+        "per_head_type": by_type,
         "effective_tflops": round(causal_flop / (ms_step * 1e-3) / 1e12, 1),
         "computed_pairs": pairs, "dense_pairs": dense_pairs,
         "density": round(pairs / dense_pairs, 4),

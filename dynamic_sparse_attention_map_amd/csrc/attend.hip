@@ -411,24 +411,21 @@ attend_kernel(Rows q, Rows k,
     }
 }
 
-__global__ void zero_counters_kernel(int* __restrict__ ctr)
-{
-    if (threadIdx.x < 8) ctr[threadIdx.x] = 0;
-}
-
 // V^T as LDS-ready images, one per 64-key sub-tile: image i of KV head g
 // (keys 64 i .. 64 i + 63) holds row d (the 64 keys' values
 // of head dimension d) as 8 chunks of 8 keys, chunk c at slot c ^ ((d >> 1) & 7), and inside
 // every group of 16 keys bits 2 and 3 of the key index are swapped.  A
 // lane's 8 keys of a PV operand fragment, {4h .. 4h+3, 8+4h .. 8+4h+3} of a
 // group for lane half h (the order the S^T accumulator holds them in), are
-// then one 16-byte chunk.  Keys past n are zero.
+// then one 16-byte chunk.  Keys past n are zero.  The first work-group also
+// clears the attention kernel's eight per-XCD queue counters.
 // grid (N_b * 2, hkv), 256 threads.
 __global__ void __launch_bounds__(256)
-v_transpose_kernel(Rows v, int n, int n_img, uint16_t* __restrict__ vt)
+v_transpose_kernel(Rows v, int n, int n_img, uint16_t* __restrict__ vt, int* __restrict__ queue)
 {
     __shared__ uint16_t tile[64][kD + 8];
     const int g = blockIdx.y, key0 = blockIdx.x * 64, tid = threadIdx.x;
+    if (blockIdx.x == 0 && g == 0 && tid < 8) queue[tid] = 0;
     const uint16_t* src = v.row(g, key0);
     for (int i = 0; i < 4; ++i) {
         const int e = tid + 256 * i;
@@ -454,10 +451,12 @@ v_transpose_kernel(Rows v, int n, int n_img, uint16_t* __restrict__ vt)
 
 }  // namespace
 
-hipError_t launch_v_transpose(Rows v, int n, int hkv, uint16_t* vt, hipStream_t stream)
+hipError_t launch_v_transpose(Rows v, int n, int hkv, uint16_t* vt, int* queue,
+                              hipStream_t stream)
 {
     const int n_img = (n + kB - 1) / kB * 2;
-    hipLaunchKernelGGL(v_transpose_kernel, dim3(n_img, hkv), dim3(256), 0, stream, v, n, n_img, vt);
+    hipLaunchKernelGGL(v_transpose_kernel, dim3(n_img, hkv), dim3(256), 0, stream, v, n, n_img, vt,
+                       queue);
     return hipGetLastError();
 }
 
@@ -476,9 +475,6 @@ hipError_t launch_attend(Rows q, Rows k, const uint16_t* vt,
         (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
     const int groups = cus;   // one resident work-group of 8 wavefronts per CU
     const float scale_log2 = kLog2e / sqrtf((float)kD);
-    hipLaunchKernelGGL(zero_counters_kernel, dim3(1), dim3(64), 0, stream, counters);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
     hipLaunchKernelGGL(attend_kernel, dim3(groups), dim3(kThreads), 0, stream, q, k, vt, row_ptr, col_idx,
                        n, nb, hkv, G, run, scale_log2, per_xcd, counters, out);
     return hipGetLastError();

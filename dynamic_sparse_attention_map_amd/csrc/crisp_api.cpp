@@ -222,7 +222,7 @@ int do_attend(const Shape& s, const Operands& x, const int32_t* row_ptr, const i
 {
     uint16_t* vt = at<uint16_t>(ws, L.vt);
     mark(2, stream);
-    hipError_t e = launch_v_transpose(x.v, s.n, s.hkv, vt, stream);
+    hipError_t e = launch_v_transpose(x.v, s.n, s.hkv, vt, at<int>(ws, L.queue), stream);
     if (e != hipSuccess) return CRISP_ERR_HIP;
     mark(3, stream);
     e = launch_attend(x.q, x.k, vt, row_ptr, col_idx, s.n, s.hq, s.hkv, at<int>(ws, L.queue), x.out,

@@ -91,10 +91,13 @@ hipError_t launch_select(Rows q, Rows k, const uint8_t* pattern,
                          int32_t* sel_s, int32_t* sel_counts, int32_t* row_ptr, int32_t* col_idx,
                          hipStream_t stream);
 
-hipError_t launch_v_transpose(Rows v, int n, int hkv, uint16_t* vt, hipStream_t stream);
+// queue: the attention kernel's 8 ints of device scratch, cleared here.
+hipError_t launch_v_transpose(Rows v, int n, int hkv, uint16_t* vt, int* queue,
+                              hipStream_t stream);
 
 // row_ptr / col_idx == nullptr: dense causal lists.
-// counters: 8 ints of device scratch (zeroed by the launch itself).
+// counters: 8 ints of device scratch, zero on entry (launch_v_transpose
+// clears them on the same stream).
 hipError_t launch_attend(Rows q, Rows k, const uint16_t* vt,
                          const int32_t* row_ptr, const int32_t* col_idx, int n, int hq, int hkv,
                          int* counters, OutRows out, hipStream_t stream);

@@ -46,7 +46,7 @@ proxy_map_kernel(Rows q, Rows k, int n, int nb,
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int w = tid >> 6;
-    const int c = w & 3;                            // row chunk
+    const int c = __builtin_amdgcn_readfirstlane(w & 3);   // row chunk (uniform)
     const int subs = (G + 3) / 4;
     const int kv = blockIdx.y / subs;
     const int hg = 4 * (blockIdx.y % subs) + (w >> 2);   // head within the KV group
@@ -88,40 +88,85 @@ proxy_map_kernel(Rows q, Rows k, int n, int nb,
         if (t + 1 < t1) stage(t + 1, buf ^ 1);
         if (!active) continue;
 
-        // S^T for keys 32a .. 32a+31 of the tile against this wave's rows
+        // S^T of this wave's rows against key group (a + c) % 4 of the tile
+        // (keys 32 g .. 32 g + 31) in acc[a]: acc[0] holds the group of the
+        // wave's own rows' columns
         f32x16 acc[4];
         for (int a = 0; a < 4; ++a) acc[a] = f32x16{};
         for (int s = 0; s < 8; ++s)
             for (int a = 0; a < 4; ++a) {
-                const bf16x8 kf = *reinterpret_cast<const bf16x8*>(&ks[buf][(32 * a + l32) * kKRow + 16 * s + 8 * hi]);
+                const int g = (a + c) & 3;
+                const bf16x8 kf = *reinterpret_cast<const bf16x8*>(&ks[buf][(32 * g + l32) * kKRow + 16 * s + 8 * hi]);
                 acc[a] = mfma32(kf, qf[s], acc[a]);
             }
 
-        // this lane: query row i at position qi, 64 of the tile's 128 keys
+        // this lane: query row i at position qi, 64 of the tile's 128 keys;
+        // element r of acc[a] is column 32 g + off(r), g = (a + c) % 4.
+        // Aligned: row i = 32 c + l32 is column i of the last tile, so acc[0]
+        // (g = c) needs a per-element test at offset l32, and acc[a], a > 0,
+        // lies wholly after column i when a + c < 4 (g > c) and wholly
+        // before it otherwise.
         const int i = 32 * c + l32;
         const int qi = q0 + i;
-        const int bi = Aligned ? i : (qi & (kB - 1));
-        const int rel = Aligned ? i : qi - t * kTileKeys;     // last visible column
-        const bool cut = Aligned ? (t == nb - 1) : (t * kTileKeys + kTileKeys - 1 > q0);
-        float m = -INFINITY;
-        for (int a = 0; a < 4; ++a)
-            for (int r = 0; r < 16; ++r) {
-                const int col = 32 * a + 8 * (r >> 2) + 4 * hi + (r & 3);
-                if (cut && col > rel) acc[a][r] = -INFINITY;   // causal
-                m = fmaxf(m, acc[a][r]);
+        float m;
+        if (Aligned) {
+            if (t == nb - 1) {                                // causal cut
+                for (int r = 0; r < 16; ++r)
+                    if (8 * (r >> 2) + 4 * hi + (r & 3) > l32) acc[0][r] = -INFINITY;
+                for (int a = 1; a < 4; ++a)
+                    if (a + c < 4)
+                        for (int r = 0; r < 16; ++r) acc[a][r] = -INFINITY;
             }
+            float t4[4];
+            for (int a = 0; a < 4; ++a) {
+                float x[5];
+                for (int j = 0; j < 5; ++j)
+                    x[j] = fmaxf(fmaxf(acc[a][3 * j], acc[a][3 * j + 1]), acc[a][3 * j + 2]);
+                t4[a] = fmaxf(fmaxf(fmaxf(x[0], x[1]), x[2]), fmaxf(fmaxf(x[3], x[4]), acc[a][15]));
+            }
+            m = fmaxf(fmaxf(t4[0], t4[1]), fmaxf(t4[2], t4[3]));
+        } else {
+            const int rel = qi - t * kTileKeys;               // last visible column
+            const bool cut = t * kTileKeys + kTileKeys - 1 > q0;
+            m = -INFINITY;
+            for (int a = 0; a < 4; ++a)
+                for (int r = 0; r < 16; ++r) {
+                    const int col = 32 * ((a + c) & 3) + 8 * (r >> 2) + 4 * hi + (r & 3);
+                    if (cut && col > rel) acc[a][r] = -INFINITY;   // causal
+                    m = fmaxf(m, acc[a][r]);
+                }
+        }
         m = fmaxf(m, swap_half(m));
         // scaled logits in the exp2 domain; a tile wholly in the row's future
         // keeps m = -inf and sums 0
         const float ms = m * scale_log2;
         const float nref = (m == -INFINITY) ? 0.f : -ms;
         float lo = 0.f, up = 0.f;
-        for (int a = 0; a < 4; ++a)
+        if (Aligned) {
             for (int r = 0; r < 16; ++r) {
-                const int col = 32 * a + 8 * (r >> 2) + 4 * hi + (r & 3);
-                const float e = __builtin_amdgcn_exp2f(fmaf(acc[a][r], scale_log2, nref));
-                if (col <= bi) lo += e; else up += e;
+                const float e = __builtin_amdgcn_exp2f(fmaf(acc[0][r], scale_log2, nref));
+                if (8 * (r >> 2) + 4 * hi + (r & 3) <= l32) lo += e;
+                else up += e;
             }
+            for (int a = 1; a < 4; ++a) {
+                float e[16];
+                for (int r = 0; r < 16; ++r)
+                    e[r] = __builtin_amdgcn_exp2f(fmaf(acc[a][r], scale_log2, nref));
+                float s4[4];
+                for (int j = 0; j < 4; ++j) s4[j] = (e[j] + e[4 + j]) + (e[8 + j] + e[12 + j]);
+                const float sa = (s4[0] + s4[1]) + (s4[2] + s4[3]);
+                if (a + c < 4) up += sa;
+                else lo += sa;
+            }
+        } else {
+            const int bi = qi & (kB - 1);
+            for (int a = 0; a < 4; ++a)
+                for (int r = 0; r < 16; ++r) {
+                    const int col = 32 * ((a + c) & 3) + 8 * (r >> 2) + 4 * hi + (r & 3);
+                    const float e = __builtin_amdgcn_exp2f(fmaf(acc[a][r], scale_log2, nref));
+                    if (col <= bi) lo += e; else up += e;
+                }
+        }
         lo += swap_half(lo);
         up += swap_half(up);
         if (hi == 0 && i < R) {
@@ -278,6 +323,127 @@ finalize_kernel(const float* __restrict__ tile_sums, const float* __restrict__ p
     }
 }
 
+// grid hq, 1024 threads, N_b <= kRouteSmall: the four kernels above for one
+// head in one work-group.  Every sum runs in the same order as there (thread
+// (row i, part p) walks segments p, p+8, .. and, within each, tiles
+// seg, seg+64, ..; wave w takes tiles w, w+16, ..), so p_v, p_s, C_struct
+// and the routing bit are the same bits.
+constexpr int kRouteSmall = 256;
+
+__global__ void __launch_bounds__(1024)
+route_small_kernel(const float* __restrict__ part_m, const float* __restrict__ part_lo,
+                   const float* __restrict__ part_up, int n, int nb, float tau, int route_here,
+                   float* __restrict__ p_v, float* __restrict__ p_s, float* __restrict__ c_struct,
+                   uint8_t* __restrict__ pattern)
+{
+    __shared__ float pm[8][kB];
+    __shared__ double pl[8][kB];
+    __shared__ float mx[kB], inv[kB];
+    __shared__ float ts[4 * kRouteSmall];
+    __shared__ float pv_l[kRouteSmall];
+    const int h = blockIdx.x, tid = threadIdx.x;
+    const int R = min(kB, n), q0 = n - R;
+    {
+        // row statistics: row_part_kernel per segment, row_norm_kernel per part
+        const int i = tid & (kB - 1), part = tid >> 7;
+        const size_t base = (size_t)h * nb * kB;
+        // segment j = part + 8 jj visits tiles seg, seg + 64, .. in order;
+        // round rr loads tile seg + 64 rr of all eight segments at once
+        float sm[kSegs / 8];
+        double sl[kSegs / 8];
+        for (int j = 0; j < kSegs / 8; ++j) {
+            sm[j] = -INFINITY;
+            sl[j] = 0.0;
+        }
+        if (i < R) {
+            for (int t0 = 0; t0 < nb; t0 += kSegs) {
+                float mt[kSegs / 8], lo[kSegs / 8], up[kSegs / 8];
+                for (int j = 0; j < kSegs / 8; ++j) {
+                    const int t = t0 + part + 8 * j;
+                    mt[j] = -INFINITY;
+                    if (t < nb) {
+                        const size_t o = base + (size_t)t * kB + i;
+                        mt[j] = part_m[o];
+                        lo[j] = part_lo[o];
+                        up[j] = part_up[o];
+                    }
+                }
+                for (int j = 0; j < kSegs / 8; ++j) {
+                    if (mt[j] == -INFINITY) continue;
+                    const double sum = (double)lo[j] + (double)up[j];
+                    if (mt[j] > sm[j]) {
+                        sl[j] = sl[j] * (double)exp2f(sm[j] - mt[j]) + sum;
+                        sm[j] = mt[j];
+                    } else {
+                        sl[j] += sum * (double)exp2f(mt[j] - sm[j]);
+                    }
+                }
+            }
+        }
+        float m = -INFINITY;
+        for (int j = 0; j < kSegs / 8; ++j) m = fmaxf(m, sm[j]);
+        double l = 0.0;
+        for (int j = 0; j < kSegs / 8; ++j)
+            if (sm[j] > -INFINITY) l += sl[j] * (double)exp2f(sm[j] - m);
+        pm[part][i] = m;
+        pl[part][i] = l;
+        __syncthreads();
+        if (part == 0 && i < R) {
+            float mt = -INFINITY;
+            for (int x = 0; x < 8; ++x) mt = fmaxf(mt, pm[x][i]);
+            double lt = 0.0;
+            for (int x = 0; x < 8; ++x)
+                if (pm[x][i] > -INFINITY) lt += pl[x][i] * (double)exp2f(pm[x][i] - mt);
+            mx[i] = mt;
+            inv[i] = (float)(1.0 / lt);
+        }
+        __syncthreads();
+    }
+    // tile masses: tile_mass_kernel, one wavefront per tile
+    const int lane = tid & 63;
+    for (int t = tid >> 6; t < nb; t += 16) {
+        double sv = 0.0, slo0 = 0.0, sup0 = 0.0, slo1 = 0.0, sup1 = 0.0;
+        for (int i = lane; i < R; i += 64) {
+            const size_t o = ((size_t)h * nb + t) * kB + i;
+            const float mt = part_m[o];
+            if (mt == -INFINITY) continue;
+            const float wt = exp2f(mt - mx[i]) * inv[i];
+            const float lo = part_lo[o] * wt, up = part_up[o] * wt;
+            sv += (double)lo + (double)up;
+            const int ei = nb - 1 - (q0 + i) / kB;
+            if (ei == 0) { slo0 += lo; sup0 += up; }
+            else { slo1 += lo; sup1 += up; }
+        }
+        sv = wave_sum(sv);
+        slo0 = wave_sum(slo0);
+        sup0 = wave_sum(sup0);
+        slo1 = wave_sum(slo1);
+        sup1 = wave_sum(sup1);
+        if (lane == 0) {
+            const float v = (float)(sv / R);
+            p_v[(size_t)h * nb + t] = v;
+            pv_l[t] = v;
+            ts[t] = (float)(slo0 / R);
+            ts[nb + t] = (float)(sup0 / R);
+            ts[2 * nb + t] = (float)(slo1 / R);
+            ts[3 * nb + t] = (float)(sup1 / R);
+        }
+    }
+    __syncthreads();
+    // finalize_kernel
+    for (int t = tid; t < nb; t += 1024) {
+        float ps = ts[t];
+        if (t >= 1) ps += ts[nb + t - 1] + ts[2 * nb + t - 1];
+        if (t >= 2) ps += ts[3 * nb + t - 2];
+        p_s[(size_t)h * nb + t] = ps;
+    }
+    if (tid == 0 && route_here) {
+        const float cs = (nb > 1) ? pv_l[0] + pv_l[nb - 1] : pv_l[0];
+        c_struct[h] = cs;
+        pattern[h] = (cs >= tau) ? 1 : 0;
+    }
+}
+
 // FlexPrefill's router (Alg. 5), the baseline CRISP replaces.
 // grid (Nb, hkv + hq), 256 threads: y < hkv: mean of key block x of KV head
 // y over the tokens it holds; y >= hkv (x == 0 only): mean of the R
@@ -409,17 +575,23 @@ hipError_t launch_route(Rows q, Rows k, int n, int hq, int hkv,
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int route_here = a.router == 0;
-    hipLaunchKernelGGL(row_part_kernel, dim3(kSegs, hq), dim3(kB), 0, stream, a.part_m, a.part_lo,
-                       a.part_up, n, nb, a.seg_m, a.seg_l);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL(row_norm_kernel, dim3(hq), dim3(1024), 0, stream, a.seg_m, a.seg_l, n,
-                       a.row_mx, a.row_inv);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL(tile_mass_kernel, dim3((nb + 15) / 16, hq), dim3(1024), 0, stream, a.part_m,
-                       a.part_lo, a.part_up, a.row_mx, a.row_inv, n, nb, p_v, a.tile_sums);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL(finalize_kernel, dim3((nb + 255) / 256, hq), dim3(256), 0, stream, a.tile_sums,
-                       p_v, nb, a.tau, route_here, p_s, c_struct, pattern);
+    if (nb <= kRouteSmall) {
+        hipLaunchKernelGGL(route_small_kernel, dim3(hq), dim3(1024), 0, stream, a.part_m, a.part_lo,
+                           a.part_up, n, nb, a.tau, route_here, p_v, p_s, c_struct, pattern);
+    } else {
+        hipLaunchKernelGGL(row_part_kernel, dim3(kSegs, hq), dim3(kB), 0, stream, a.part_m,
+                           a.part_lo, a.part_up, n, nb, a.seg_m, a.seg_l);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        hipLaunchKernelGGL(row_norm_kernel, dim3(hq), dim3(1024), 0, stream, a.seg_m, a.seg_l, n,
+                           a.row_mx, a.row_inv);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        hipLaunchKernelGGL(tile_mass_kernel, dim3((nb + 15) / 16, hq), dim3(1024), 0, stream,
+                           a.part_m, a.part_lo, a.part_up, a.row_mx, a.row_inv, n, nb, p_v,
+                           a.tile_sums);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        hipLaunchKernelGGL(finalize_kernel, dim3((nb + 255) / 256, hq), dim3(256), 0, stream,
+                           a.tile_sums, p_v, nb, a.tau, route_here, p_s, c_struct, pattern);
+    }
     if ((e = hipGetLastError()) != hipSuccess || route_here) return e;
     hipLaunchKernelGGL(jsd_pool_kernel, dim3(nb, hkv + hq), dim3(256), 0, stream, q, k, n, nb, hkv,
                        a.jsd_kbar, a.jsd_qbar);

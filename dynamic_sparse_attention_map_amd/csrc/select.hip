@@ -118,8 +118,8 @@ vs_select_kernel(const uint8_t* __restrict__ pattern, const float* __restrict__ 
 {
     __shared__ int wsum[16];
     __shared__ double wsum_d[16];
-    __shared__ float best_v[16];
-    __shared__ int best_i[16];
+    __shared__ float best_v[2][16];
+    __shared__ int best_i[2][16];
     __shared__ int s_kk;
     __shared__ uint8_t flag[kMaxBlocks];
     __shared__ unsigned long long keys[kMaxBlocks];
@@ -210,6 +210,10 @@ vs_select_kernel(const uint8_t* __restrict__ pattern, const float* __restrict__ 
             const int kk = min(vr.kmin_blocks, nb);
             for (int e = 0; e < 4; ++e) flag[4 * tid + e] = 0;
             __syncthreads();
+            // one round per pick: each wavefront's best candidate, then every
+            // thread finds the overall best and its owner flags it (flags
+            // are only read by their owner); the per-wave slots alternate
+            // between rounds, so one barrier per round suffices
             for (int round = 0; round < kk; ++round) {
                 float bv = -INFINITY;
                 int bi = 0x7fffffff;
@@ -222,17 +226,19 @@ vs_select_kernel(const uint8_t* __restrict__ pattern, const float* __restrict__ 
                     const int oi = __shfl_xor(bi, o);
                     if (ov > bv || (ov == bv && oi < bi)) { bv = ov; bi = oi; }
                 }
-                if (lane == 0) { best_v[w] = bv; best_i[w] = bi; }
+                const int slot = round & 1;
+                if (lane == 0) { best_v[slot][w] = bv; best_i[slot][w] = bi; }
                 __syncthreads();
-                if (tid == 0) {
-                    float v = best_v[0];
-                    int i = best_i[0];
-                    for (int x = 1; x < 16; ++x)
-                        if (best_v[x] > v || (best_v[x] == v && best_i[x] < i)) { v = best_v[x]; i = best_i[x]; }
-                    flag[i] = 1;
-                }
-                __syncthreads();
+                float v = best_v[slot][0];
+                int i = best_i[slot][0];
+                for (int x = 1; x < 16; ++x)
+                    if (best_v[slot][x] > v || (best_v[slot][x] == v && best_i[slot][x] < i)) {
+                        v = best_v[slot][x];
+                        i = best_i[slot][x];
+                    }
+                if ((i >> 2) == tid) flag[i] = 1;
             }
+            __syncthreads();
             cnt = 0;
             for (int e = 0; e < 4; ++e) cnt += flag[4 * tid + e];
         }
@@ -448,98 +454,50 @@ __device__ T block_scan_256(T v, T* wsum, T* total)
     return before + x - v;
 }
 
-// grid (ceil(tri(Nb) / kRadixChunk), hq), 256 threads
-__global__ void __launch_bounds__(256)
-pe_radix_kernel(int nb, int pass,
-                const float* __restrict__ abar, PeState* __restrict__ state,
-                unsigned long long* __restrict__ hist_mass, uint32_t* __restrict__ hist_count,
-                uint32_t* __restrict__ pass_ctr)
+// One map entry's contribution to pass `pass`'s LDS histogram: entry e
+// (flat position in the head's triangular map) with value v.
+__device__ __forceinline__ void radix_add(int pass, int nb, const PeState& st, size_t e, float v,
+                                          uint32_t* cnt, unsigned long long* mass)
 {
-    __shared__ uint32_t cnt[kFlatBins];
-    __shared__ unsigned long long mass[kValBins];
-    __shared__ unsigned long long wsum_m[4];
-    __shared__ uint32_t wsum_c[4];
-    __shared__ int s_last;
-    const int h = blockIdx.y, tid = threadIdx.x;
-    const PeState st = state[h];
-    if (st.done) return;                // VS heads start done (pe_init_kernel)
-    const bool val = pass < kValPasses;
     const int shift = pass_shift(pass), bits = pass_bits(pass);
-    const int bins = 1 << bits;
-    for (int i = tid; i < bins; i += 256) {
-        cnt[i] = 0u;
-        if (val) mass[i] = 0ull;
+    const uint32_t mask = (1u << bits) - 1u;
+    const uint32_t key = ~__float_as_uint(v);
+    if (pass < kValPasses) {
+        if (pass > 0 && (key >> (shift + bits)) != st.key_prefix) return;
+        const uint32_t d = (key >> shift) & mask;
+        atomicAdd(&cnt[d], 1u);
+        atomicAdd(&mass[d], to_fix(v));
+    } else {
+        if (key != st.key_star) return;
+        // row of entry e: the largest qb with qb (qb + 1) / 2 <= e
+        int qb = (int)((sqrt(8.0 * (double)e + 1.0) - 1.0) * 0.5);
+        while (tri(qb + 1) <= e) ++qb;
+        while (tri(qb) > e) --qb;
+        const uint32_t flat = (uint32_t)qb * (uint32_t)nb + (uint32_t)(e - tri(qb));
+        if (pass > kValPasses && (flat >> (shift + bits)) != st.flat_prefix) return;
+        atomicAdd(&cnt[(flat >> shift) & mask], 1u);
     }
-    __syncthreads();
-    const size_t total = tri(nb);
-    const float* base = abar + (size_t)h * total;
-    const size_t e0 = (size_t)blockIdx.x * kRadixChunk;
-    const size_t e1 = min(total, e0 + kRadixChunk);
-    // all of this thread's entries in flight at once
-    constexpr int kPer = kRadixChunk / 256;
-    float vals[kPer];
-#pragma unroll
-    for (int j = 0; j < kPer; ++j) {
-        const size_t e = e0 + tid + 256 * j;
-        vals[j] = (e < e1) ? base[e] : 0.f;
-    }
-#pragma unroll
-    for (int j = 0; j < kPer; ++j) {
-        const size_t e = e0 + tid + 256 * j;
-        if (e >= e1) break;
-        const float v = vals[j];
-        const uint32_t key = ~__float_as_uint(v);
-        if (val) {
-            if (pass > 0 && (key >> (shift + bits)) != st.key_prefix) continue;
-            const int d = (key >> shift) & (bins - 1);
-            atomicAdd(&cnt[d], 1u);
-            atomicAdd(&mass[d], to_fix(v));
-        } else {
-            if (key != st.key_star) continue;
-            // row of entry e: the largest qb with qb (qb + 1) / 2 <= e
-            int qb = (int)((sqrt(8.0 * (double)e + 1.0) - 1.0) * 0.5);
-            while (tri(qb + 1) <= e) ++qb;
-            while (tri(qb) > e) --qb;
-            const uint32_t flat = (uint32_t)qb * (uint32_t)nb + (uint32_t)(e - tri(qb));
-            if (pass > kValPasses && (flat >> (shift + bits)) != st.flat_prefix) continue;
-            atomicAdd(&cnt[(flat >> shift) & (bins - 1)], 1u);
-        }
-    }
-    __syncthreads();
-    uint32_t* gc = hist_count + ((size_t)h * kRadixPasses + pass) * kFlatBins;
-    unsigned long long* gm = hist_mass + ((size_t)h * kValPasses + (val ? pass : 0)) * kValBins;
-    for (int i = tid; i < bins; i += 256) {
-        if (cnt[i]) {
-            atomicAdd(&gc[i], cnt[i]);
-            if (val) atomicAdd(&gm[i], mass[i]);
-        }
-    }
-    // The histogram atomics are performed at the device's coherence point;
-    // waiting for them to complete (vmcnt) before the counter increment
-    // orders them without a cache write-back (a __threadfence() writes back
-    // and invalidates the XCD's L2, which costs more than the pass itself).
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    if (tid == 0) {
-        const uint32_t nwg = gridDim.x;
-        s_last = atomicAdd(&pass_ctr[h * kRadixPasses + pass], 1u) == nwg - 1;
-    }
-    __syncthreads();
-    if (!s_last) return;
-    // every other work-group's atomics are complete: read them coherently
+}
 
-    // ---- resolve: this work-group saw every other one finish the pass ----
-    const int per = bins / 256;                       // consecutive bins per thread
+// Resolve pass `pass` of a PE head from its complete histogram (cnt, and
+// mass for the value passes; LDS, 1 << pass_bits(pass) digits), 256
+// threads: the digit at which the kept mass (value passes) or the tie count
+// (index passes) is reached.  The thread that finds it writes the head's
+// next state to *out; every thread must call this (it holds barriers).
+__device__ void radix_resolve(int pass, size_t total, const PeState& st, const uint32_t* cnt,
+                              const unsigned long long* mass, uint32_t* wsum_c,
+                              unsigned long long* wsum_m, PeState* out)
+{
+    const int tid = threadIdx.x;
+    const bool val = pass < kValPasses;
+    const int bits = pass_bits(pass);
+    const int per = (1 << bits) / 256;                // consecutive digits per thread
     uint32_t c_loc = 0;
     unsigned long long m_loc = 0;
     for (int j = 0; j < per; ++j) {
         const int i = tid * per + j;
-        cnt[i] = __hip_atomic_load(&gc[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         c_loc += cnt[i];
-        if (val) {
-            mass[i] = __hip_atomic_load(&gm[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            m_loc += mass[i];
-        }
+        if (val) m_loc += mass[i];
     }
     uint32_t c_all;
     unsigned long long m_all;
@@ -555,7 +513,7 @@ pe_radix_kernel(int nb, int pass,
                 nx.flat_star = 0xffffffffu;
                 nx.kstar = (uint32_t)total;
                 nx.done = 1u;
-                state[h] = nx;
+                *out = nx;
             }
             return;
         }
@@ -582,7 +540,7 @@ pe_radix_kernel(int nb, int pass,
                         nx.kstar = nx.before + (uint32_t)ties;
                     }
                 }
-                state[h] = nx;
+                *out = nx;
             }
             m_before = incl;
             c_before += cnt[i];
@@ -600,11 +558,127 @@ pe_radix_kernel(int nb, int pass,
                     nx.flat_star = nx.flat_prefix;
                     nx.done = 1u;
                 }
-                state[h] = nx;
+                *out = nx;
             }
             c_before = incl;
         }
     }
+}
+
+// grid hq, 256 threads: the whole cut-off of one head in one work-group,
+// for maps of at most kRadixSmall entries.  The same five passes, digits
+// and fixed-point masses as pe_radix_kernel (so the same result), with the
+// histograms in LDS only; it also seeds the state as pe_init_kernel does,
+// which it replaces.
+constexpr size_t kRadixSmall = (size_t)256 * 257 / 2;
+
+__global__ void __launch_bounds__(256)
+pe_radix_small_kernel(const uint8_t* __restrict__ pattern, int nb, float gamma,
+                      const float* __restrict__ abar, PeState* __restrict__ state)
+{
+    __shared__ uint32_t cnt[kFlatBins];
+    __shared__ unsigned long long mass[kValBins];
+    __shared__ unsigned long long wsum_m[4];
+    __shared__ uint32_t wsum_c[4];
+    __shared__ PeState s_st;
+    const int h = blockIdx.x, tid = threadIdx.x;
+    if (tid == 0) {
+        PeState st = {};
+        st.need = (unsigned long long)((double)gamma * kFix);
+        st.done = pattern[h] ? 1u : 0u;
+        s_st = st;
+    }
+    __syncthreads();
+    const size_t total = tri(nb);
+    const float* base = abar + (size_t)h * total;
+    for (int pass = 0; pass < kRadixPasses; ++pass) {
+        const PeState st = s_st;
+        if (st.done) break;
+        const int bins = 1 << pass_bits(pass);
+        for (int i = tid; i < bins; i += 256) {
+            cnt[i] = 0u;
+            if (pass < kValPasses) mass[i] = 0ull;
+        }
+        __syncthreads();
+        for (size_t e = tid; e < total; e += 256) radix_add(pass, nb, st, e, base[e], cnt, mass);
+        __syncthreads();
+        radix_resolve(pass, total, st, cnt, mass, wsum_c, wsum_m, &s_st);
+        __syncthreads();
+    }
+    if (tid == 0) state[h] = s_st;
+}
+
+// grid (ceil(tri(Nb) / kRadixChunk), hq), 256 threads
+__global__ void __launch_bounds__(256)
+pe_radix_kernel(int nb, int pass,
+                const float* __restrict__ abar, PeState* __restrict__ state,
+                unsigned long long* __restrict__ hist_mass, uint32_t* __restrict__ hist_count,
+                uint32_t* __restrict__ pass_ctr)
+{
+    __shared__ uint32_t cnt[kFlatBins];
+    __shared__ unsigned long long mass[kValBins];
+    __shared__ unsigned long long wsum_m[4];
+    __shared__ uint32_t wsum_c[4];
+    __shared__ int s_last;
+    const int h = blockIdx.y, tid = threadIdx.x;
+    const PeState st = state[h];
+    if (st.done) return;                // VS heads start done (pe_init_kernel)
+    const bool val = pass < kValPasses;
+    const int bins = 1 << pass_bits(pass);
+    for (int i = tid; i < bins; i += 256) {
+        cnt[i] = 0u;
+        if (val) mass[i] = 0ull;
+    }
+    __syncthreads();
+    const size_t total = tri(nb);
+    const float* base = abar + (size_t)h * total;
+    const size_t e0 = (size_t)blockIdx.x * kRadixChunk;
+    const size_t e1 = min(total, e0 + kRadixChunk);
+    // all of this thread's entries in flight at once
+    constexpr int kPer = kRadixChunk / 256;
+    float vals[kPer];
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+        const size_t e = e0 + tid + 256 * j;
+        vals[j] = (e < e1) ? base[e] : 0.f;
+    }
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+        const size_t e = e0 + tid + 256 * j;
+        if (e >= e1) break;
+        radix_add(pass, nb, st, e, vals[j], cnt, mass);
+    }
+    __syncthreads();
+    uint32_t* gc = hist_count + ((size_t)h * kRadixPasses + pass) * kFlatBins;
+    unsigned long long* gm = hist_mass + ((size_t)h * kValPasses + (val ? pass : 0)) * kValBins;
+    for (int i = tid; i < bins; i += 256) {
+        if (cnt[i]) {
+            atomicAdd(&gc[i], cnt[i]);
+            if (val) atomicAdd(&gm[i], mass[i]);
+        }
+    }
+    // The histogram atomics are performed at the device's coherence point;
+    // waiting for them to complete (vmcnt) before the counter increment
+    // orders them without a cache write-back (a __threadfence() writes back
+    // and invalidates the XCD's L2, which costs more than the pass itself).
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (tid == 0) {
+        const uint32_t nwg = gridDim.x;
+        s_last = atomicAdd(&pass_ctr[h * kRadixPasses + pass], 1u) == nwg - 1;
+    }
+    __syncthreads();
+    if (!s_last) return;
+    // every other work-group's atomics are complete: read them coherently
+
+    // ---- resolve: this work-group saw every other one finish the pass ----
+    const int per = bins / 256;                       // consecutive bins per thread
+    for (int j = 0; j < per; ++j) {
+        const int i = tid * per + j;
+        cnt[i] = __hip_atomic_load(&gc[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (val) mass[i] = __hip_atomic_load(&gm[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    radix_resolve(pass, total, st, cnt, mass, wsum_c, wsum_m, &state[h]);
 }
 
 // Block-list membership of (qb, kb) for one head: VS rows from the two
@@ -726,6 +800,64 @@ expand_fill_kernel(const uint8_t* __restrict__ pattern, int nb, const uint8_t* _
     }
 }
 
+
+// grid hq, 1024 threads: expand_count, expand_scan and expand_fill for one
+// head in one work-group (N_b <= kExpandSmall), the row lengths kept in LDS.
+// The same rows, offsets and K* as the three kernels.
+constexpr int kExpandSmall = 256;
+
+__global__ void __launch_bounds__(1024)
+expand_small_kernel(const uint8_t* __restrict__ pattern, int nb, const uint8_t* __restrict__ bitmap,
+                    const float* __restrict__ abar, const PeState* __restrict__ state,
+                    int32_t* __restrict__ row_ptr, int32_t* __restrict__ col_idx,
+                    int32_t* __restrict__ counts)
+{
+    __shared__ uint8_t bmv[kExpandSmall];
+    __shared__ uint8_t bms[kExpandSmall];
+    __shared__ int start[kExpandSmall];
+    __shared__ int wsum[16];
+    const int h = blockIdx.x, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const RowRule rule = load_rule(pattern, nb, h, bitmap, abar, state, bmv, bms);
+    for (int qb = w; qb < nb; qb += 16) {
+        int c = 0;
+        for (int kb0 = 0; kb0 <= qb; kb0 += 64) c += __popcll(__ballot(rule.member(qb, kb0 + lane)));
+        if (lane == 0) start[qb] = c;
+    }
+    __syncthreads();
+    const size_t base = (size_t)h * tri(nb);
+    int32_t* rp = row_ptr + (size_t)h * (nb + 1);
+    int len[4], mine = 0;
+    for (int e = 0; e < 4; ++e) {
+        const int j = 4 * tid + e;
+        len[e] = (j < nb) ? start[j] : 0;
+        mine += len[e];
+    }
+    int total;
+    int at = block_scan_1024(mine, wsum, &total);    // ends with a barrier
+    for (int e = 0; e < 4; ++e) {
+        const int j = 4 * tid + e;
+        if (j >= nb) break;
+        start[j] = (int)base + at;
+        rp[j] = (int32_t)(base + at);
+        at += len[e];
+    }
+    if (tid == 0) {
+        rp[nb] = (int32_t)(base + total);
+        counts[h * 3 + 2] = pattern[h] ? 0 : (int32_t)state[h].kstar;
+    }
+    __syncthreads();
+    const unsigned long long below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    for (int qb = w; qb < nb; qb += 16) {
+        size_t pos = (size_t)start[qb];
+        for (int kb0 = 0; kb0 <= qb; kb0 += 64) {
+            const bool mbr = rule.member(qb, kb0 + lane);
+            const unsigned long long bal = __ballot(mbr);
+            if (mbr) col_idx[pos + __popcll(bal & below)] = kb0 + lane;
+            pos += __popcll(bal);
+        }
+    }
+}
+
 }  // namespace
 
 hipError_t launch_select(Rows q, Rows k, const uint8_t* pattern,
@@ -741,9 +873,13 @@ hipError_t launch_select(Rows q, Rows k, const uint8_t* pattern,
     hipLaunchKernelGGL(vs_select_kernel, dim3(hq, 2), dim3(1024), 0, stream, pattern, p_v, p_s, nb,
                        vs, sel_v, sel_s, sel_counts, s.bitmap);
     CRISP_CHECK_LAUNCH();
-    hipLaunchKernelGGL(pe_init_kernel, dim3(hq), dim3(1024), 0, stream, pattern, gamma, s.hist_mass,
-                       s.hist_count, s.pass_ctr, s.state);
-    CRISP_CHECK_LAUNCH();
+    const long long tri_nb = (long long)nb * (nb + 1) / 2;
+    const bool small_map = (size_t)tri_nb <= kRadixSmall;
+    if (!small_map) {
+        hipLaunchKernelGGL(pe_init_kernel, dim3(hq), dim3(1024), 0, stream, pattern, gamma,
+                           s.hist_mass, s.hist_count, s.pass_ctr, s.state);
+        CRISP_CHECK_LAUNCH();
+    }
     hipLaunchKernelGGL(pe_pool_kernel, dim3(nb, hq + hkv), dim3(256), 0, stream, q, k, pattern, n,
                        hq, G, s.qbar, s.kbar);
     CRISP_CHECK_LAUNCH();
@@ -755,12 +891,23 @@ hipError_t launch_select(Rows q, Rows k, const uint8_t* pattern,
     hipLaunchKernelGGL(pe_softmax_kernel, dim3((nb + 3) / 4, hq), dim3(256), 0, stream, pattern, nb,
                        s.abar);
     CRISP_CHECK_LAUNCH();
-    const long long tri_nb = (long long)nb * (nb + 1) / 2;
-    const dim3 radix_grid((unsigned)((tri_nb + kRadixChunk - 1) / kRadixChunk), hq);
-    for (int pass = 0; pass < kRadixPasses; ++pass) {
-        hipLaunchKernelGGL(pe_radix_kernel, radix_grid, dim3(256), 0, stream, nb, pass,
-                           s.abar, s.state, s.hist_mass, s.hist_count, s.pass_ctr);
+    if (small_map) {
+        hipLaunchKernelGGL(pe_radix_small_kernel, dim3(hq), dim3(256), 0, stream, pattern, nb, gamma,
+                           s.abar, s.state);
         CRISP_CHECK_LAUNCH();
+    } else {
+        const dim3 radix_grid((unsigned)((tri_nb + kRadixChunk - 1) / kRadixChunk), hq);
+        for (int pass = 0; pass < kRadixPasses; ++pass) {
+            hipLaunchKernelGGL(pe_radix_kernel, radix_grid, dim3(256), 0, stream, nb, pass,
+                               s.abar, s.state, s.hist_mass, s.hist_count, s.pass_ctr);
+            CRISP_CHECK_LAUNCH();
+        }
+    }
+    if (nb <= kExpandSmall) {
+        hipLaunchKernelGGL(expand_small_kernel, dim3(hq), dim3(1024), 0, stream, pattern, nb,
+                           s.bitmap, s.abar, s.state, row_ptr, col_idx, sel_counts);
+        CRISP_CHECK_LAUNCH();
+        return hipSuccess;
     }
     const dim3 rows_grid((nb + kRowsPerGroup - 1) / kRowsPerGroup, hq);
     hipLaunchKernelGGL(expand_count_kernel, rows_grid, dim3(1024), 0, stream, pattern, nb, s.bitmap,
