@@ -399,34 +399,51 @@ route_small_kernel(const float* __restrict__ part_m, const float* __restrict__ p
         }
         __syncthreads();
     }
-    // tile masses: tile_mass_kernel, one wavefront per tile
+    // tile masses: tile_mass_kernel, one wavefront per tile; a wavefront
+    // loads four of its tiles (t, t + 16, ..) at a time
     const int lane = tid & 63;
-    for (int t = tid >> 6; t < nb; t += 16) {
-        double sv = 0.0, slo0 = 0.0, sup0 = 0.0, slo1 = 0.0, sup1 = 0.0;
-        for (int i = lane; i < R; i += 64) {
-            const size_t o = ((size_t)h * nb + t) * kB + i;
-            const float mt = part_m[o];
-            if (mt == -INFINITY) continue;
-            const float wt = exp2f(mt - mx[i]) * inv[i];
-            const float lo = part_lo[o] * wt, up = part_up[o] * wt;
-            sv += (double)lo + (double)up;
-            const int ei = nb - 1 - (q0 + i) / kB;
-            if (ei == 0) { slo0 += lo; sup0 += up; }
-            else { slo1 += lo; sup1 += up; }
-        }
-        sv = wave_sum(sv);
-        slo0 = wave_sum(slo0);
-        sup0 = wave_sum(sup0);
-        slo1 = wave_sum(slo1);
-        sup1 = wave_sum(sup1);
-        if (lane == 0) {
-            const float v = (float)(sv / R);
-            p_v[(size_t)h * nb + t] = v;
-            pv_l[t] = v;
-            ts[t] = (float)(slo0 / R);
-            ts[nb + t] = (float)(sup0 / R);
-            ts[2 * nb + t] = (float)(slo1 / R);
-            ts[3 * nb + t] = (float)(sup1 / R);
+    for (int t4 = tid >> 6; t4 < nb; t4 += 64) {
+        float vm[4][2], vlo[4][2], vup[4][2];
+        for (int b = 0; b < 4; ++b)
+            for (int x = 0; x < 2; ++x) {
+                const int t = t4 + 16 * b, i = lane + 64 * x;
+                vm[b][x] = -INFINITY;
+                if (t < nb && i < R) {
+                    const size_t o = ((size_t)h * nb + t) * kB + i;
+                    vm[b][x] = part_m[o];
+                    vlo[b][x] = part_lo[o];
+                    vup[b][x] = part_up[o];
+                }
+            }
+        for (int b = 0; b < 4; ++b) {
+            const int t = t4 + 16 * b;
+            if (t >= nb) break;
+            double sv = 0.0, slo0 = 0.0, sup0 = 0.0, slo1 = 0.0, sup1 = 0.0;
+            for (int x = 0; x < 2; ++x) {
+                const int i = lane + 64 * x;
+                const float mt = vm[b][x];
+                if (i >= R || mt == -INFINITY) continue;
+                const float wt = exp2f(mt - mx[i]) * inv[i];
+                const float lo = vlo[b][x] * wt, up = vup[b][x] * wt;
+                sv += (double)lo + (double)up;
+                const int ei = nb - 1 - (q0 + i) / kB;
+                if (ei == 0) { slo0 += lo; sup0 += up; }
+                else { slo1 += lo; sup1 += up; }
+            }
+            sv = wave_sum(sv);
+            slo0 = wave_sum(slo0);
+            sup0 = wave_sum(sup0);
+            slo1 = wave_sum(slo1);
+            sup1 = wave_sum(sup1);
+            if (lane == 0) {
+                const float v = (float)(sv / R);
+                p_v[(size_t)h * nb + t] = v;
+                pv_l[t] = v;
+                ts[t] = (float)(slo0 / R);
+                ts[nb + t] = (float)(sup0 / R);
+                ts[2 * nb + t] = (float)(slo1 / R);
+                ts[3 * nb + t] = (float)(sup1 / R);
+            }
         }
     }
     __syncthreads();

@@ -102,6 +102,8 @@ __device__ void bitonic_sort(unsigned long long* keys, int np2)
         }
 }
 
+constexpr int kRankClip = 256;      // largest N_b whose k_min clip ranks all entries
+
 // grid (hq, 2): direction 0 = vertical (p_v), 1 = slash (p_s).  Budget rule:
 //   0  p_j > alpha * r / (N_b - 2), r = max(1 - p_0 - p_{N_b-1}, 0)   (Eq. 3-4)
 //   1  p_j > alpha * median(p_1 .. p_{N_b-2})                          (App. H)
@@ -210,33 +212,51 @@ vs_select_kernel(const uint8_t* __restrict__ pattern, const float* __restrict__ 
             const int kk = min(vr.kmin_blocks, nb);
             for (int e = 0; e < 4; ++e) flag[4 * tid + e] = 0;
             __syncthreads();
-            // one round per pick: each wavefront's best candidate, then every
-            // thread finds the overall best and its owner flags it (flags
-            // are only read by their owner); the per-wave slots alternate
-            // between rounds, so one barrier per round suffices
-            for (int round = 0; round < kk; ++round) {
-                float bv = -INFINITY;
-                int bi = 0x7fffffff;
-                for (int e = 0; e < 4; ++e) {
-                    const int j = 4 * tid + e;
-                    if (j < nb && !flag[j] && (pv[e] > bv || (pv[e] == bv && j < bi))) { bv = pv[e]; bi = j; }
-                }
-                for (int o = 32; o > 0; o >>= 1) {
-                    const float ov = __shfl_xor(bv, o);
-                    const int oi = __shfl_xor(bi, o);
-                    if (ov > bv || (ov == bv && oi < bi)) { bv = ov; bi = oi; }
-                }
-                const int slot = round & 1;
-                if (lane == 0) { best_v[slot][w] = bv; best_i[slot][w] = bi; }
+            if (nb <= kRankClip) {
+                // small N_b: entry j is kept iff fewer than kk entries precede it
+                // in the order (p desc, j asc); the same kk entries as the picks
+                float* pl = reinterpret_cast<float*>(keys);     // free under rules 0 and 1
+                for (int i = tid; i < nb; i += 1024) pl[i] = p[i];
                 __syncthreads();
-                float v = best_v[slot][0];
-                int i = best_i[slot][0];
-                for (int x = 1; x < 16; ++x)
-                    if (best_v[slot][x] > v || (best_v[slot][x] == v && best_i[slot][x] < i)) {
-                        v = best_v[slot][x];
-                        i = best_i[slot][x];
+                if (4 * tid < nb) {
+                    int rank[4] = {0, 0, 0, 0};
+                    for (int i = 0; i < nb; ++i) {
+                        const float x = pl[i];
+                        for (int e = 0; e < 4; ++e)
+                            rank[e] += (x > pv[e] || (x == pv[e] && i < 4 * tid + e)) ? 1 : 0;
                     }
-                if ((i >> 2) == tid) flag[i] = 1;
+                    for (int e = 0; e < 4; ++e)
+                        if (4 * tid + e < nb) flag[4 * tid + e] = rank[e] < kk;
+                }
+            } else {
+                // one round per pick: each wavefront's best candidate, then every
+                // thread finds the overall best and its owner flags it (flags
+                // are only read by their owner); the per-wave slots alternate
+                // between rounds, so one barrier per round suffices
+                for (int round = 0; round < kk; ++round) {
+                    float bv = -INFINITY;
+                    int bi = 0x7fffffff;
+                    for (int e = 0; e < 4; ++e) {
+                        const int j = 4 * tid + e;
+                        if (j < nb && !flag[j] && (pv[e] > bv || (pv[e] == bv && j < bi))) { bv = pv[e]; bi = j; }
+                    }
+                    for (int o = 32; o > 0; o >>= 1) {
+                        const float ov = __shfl_xor(bv, o);
+                        const int oi = __shfl_xor(bi, o);
+                        if (ov > bv || (ov == bv && oi < bi)) { bv = ov; bi = oi; }
+                    }
+                    const int slot = round & 1;
+                    if (lane == 0) { best_v[slot][w] = bv; best_i[slot][w] = bi; }
+                    __syncthreads();
+                    float v = best_v[slot][0];
+                    int i = best_i[slot][0];
+                    for (int x = 1; x < 16; ++x)
+                        if (best_v[slot][x] > v || (best_v[slot][x] == v && best_i[slot][x] < i)) {
+                            v = best_v[slot][x];
+                            i = best_i[slot][x];
+                        }
+                    if ((i >> 2) == tid) flag[i] = 1;
+                }
             }
             __syncthreads();
             cnt = 0;
@@ -336,7 +356,7 @@ pe_pool_kernel(Rows q, Rows k,
 __global__ void __launch_bounds__(256)
 pe_logits_kernel(const float* __restrict__ qbar, const float* __restrict__ kbar,
                  const uint8_t* __restrict__ pattern, int nb, int G, float scale_log2,
-                 float* __restrict__ abar)
+                 int fuse_softmax, float* __restrict__ abar)
 {
     constexpr int kP = kD + 1;                   // LDS pitch (floats)
     __shared__ float qs[32 * kP];
@@ -374,23 +394,51 @@ pe_logits_kernel(const float* __restrict__ qbar, const float* __restrict__ kbar,
     __syncthreads();
     const int w = tid >> 6, lane = tid & 63, l32 = lane & 31, hi = lane >> 5;
     const int kt = kt0 + w;
-    if (kt > qt) return;
+    const bool live = kt <= qt;
+    if (!live && !fuse_softmax) return;
     // D[m][n] = sum_d Q̄[32 qt + m][d] K̄[32 kt + n][d]; step s covers d = 2s, 2s+1
     // (A: lane l holds row l % 32, d = 2s + l / 32; B likewise for keys)
     // (two independent accumulation chains over alternate steps)
     f32x16 acc = f32x16{}, acc1 = f32x16{};
-    const float* qa = qs + l32 * kP + hi;
-    const float* kb_ = kst + (32 * w + l32) * kP + hi;
-    for (int s = 0; s < kD / 2; s += 2) {
-        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(qa[2 * s], kb_[2 * s], acc, 0, 0, 0);
-        acc1 = __builtin_amdgcn_mfma_f32_32x32x2f32(qa[2 * s + 2], kb_[2 * s + 2], acc1, 0, 0, 0);
+    if (live) {
+        const float* qa = qs + l32 * kP + hi;
+        const float* kb_ = kst + (32 * w + l32) * kP + hi;
+        for (int s = 0; s < kD / 2; s += 2) {
+            acc = __builtin_amdgcn_mfma_f32_32x32x2f32(qa[2 * s], kb_[2 * s], acc, 0, 0, 0);
+            acc1 = __builtin_amdgcn_mfma_f32_32x32x2f32(qa[2 * s + 2], kb_[2 * s + 2], acc1, 0, 0, 0);
+        }
+        acc += acc1;
     }
-    acc += acc1;
     const size_t base = (size_t)h * tri(nb);
     const int kb = 32 * kt + l32;
-    for (int r = 0; r < 16; ++r) {
-        const int qb = 32 * qt + 8 * (r >> 2) + 4 * hi + (r & 3);
-        if (qb < nb && kb <= qb) abar[base + tri(qb) + kb] = acc[r] * scale_log2;
+    if (!fuse_softmax) {
+        for (int r = 0; r < 16; ++r) {
+            const int qb = 32 * qt + 8 * (r >> 2) + 4 * hi + (r & 3);
+            if (qb < nb && kb <= qb) abar[base + tri(qb) + kb] = acc[r] * scale_log2;
+        }
+        return;
+    }
+    // N_b <= 128: this work-group holds whole rows (every key tile of query
+    // blocks 32 qt .. 32 qt + 31), so it also runs pe_softmax_kernel's row
+    // normalisation on them, in the same order, from an LDS copy
+    __syncthreads();                              // kst is free
+    float* rows = kst;                            // [32][kP]
+    if (live)
+        for (int r = 0; r < 16; ++r) rows[(8 * (r >> 2) + 4 * hi + (r & 3)) * kP + kb] = acc[r] * scale_log2;
+    __syncthreads();
+    for (int rl = w; rl < 32; rl += 4) {
+        const int qb = 32 * qt + rl;
+        if (qb >= nb) break;
+        const float* row = rows + rl * kP;
+        float m = -INFINITY;
+        for (int k2 = lane; k2 <= qb; k2 += 64) m = fmaxf(m, row[k2]);
+        m = wave_max(m);
+        double l = 0.0;
+        for (int k2 = lane; k2 <= qb; k2 += 64) l += (double)exp2f(row[k2] - m);
+        l = wave_sum(l);
+        const double inv = 1.0 / (l * (double)nb);
+        float* out = abar + base + tri(qb);
+        for (int k2 = lane; k2 <= qb; k2 += 64) out[k2] = (float)((double)exp2f(row[k2] - m) * inv);
     }
 }
 
@@ -571,6 +619,7 @@ __device__ void radix_resolve(int pass, size_t total, const PeState& st, const u
 // histograms in LDS only; it also seeds the state as pe_init_kernel does,
 // which it replaces.
 constexpr size_t kRadixSmall = (size_t)256 * 257 / 2;
+constexpr int kRadixCached = 128 * 129 / 2;   // maps this small are read once, into LDS
 
 __global__ void __launch_bounds__(256)
 pe_radix_small_kernel(const uint8_t* __restrict__ pattern, int nb, float gamma,
@@ -581,6 +630,7 @@ pe_radix_small_kernel(const uint8_t* __restrict__ pattern, int nb, float gamma,
     __shared__ unsigned long long wsum_m[4];
     __shared__ uint32_t wsum_c[4];
     __shared__ PeState s_st;
+    __shared__ float vals[kRadixCached];
     const int h = blockIdx.x, tid = threadIdx.x;
     if (tid == 0) {
         PeState st = {};
@@ -588,9 +638,12 @@ pe_radix_small_kernel(const uint8_t* __restrict__ pattern, int nb, float gamma,
         st.done = pattern[h] ? 1u : 0u;
         s_st = st;
     }
-    __syncthreads();
     const size_t total = tri(nb);
+    const bool cached = total <= (size_t)kRadixCached;
     const float* base = abar + (size_t)h * total;
+    if (cached && !pattern[h])
+        for (size_t e = tid; e < total; e += 256) vals[e] = base[e];
+    __syncthreads();
     for (int pass = 0; pass < kRadixPasses; ++pass) {
         const PeState st = s_st;
         if (st.done) break;
@@ -600,7 +653,8 @@ pe_radix_small_kernel(const uint8_t* __restrict__ pattern, int nb, float gamma,
             if (pass < kValPasses) mass[i] = 0ull;
         }
         __syncthreads();
-        for (size_t e = tid; e < total; e += 256) radix_add(pass, nb, st, e, base[e], cnt, mass);
+        for (size_t e = tid; e < total; e += 256)
+            radix_add(pass, nb, st, e, cached ? vals[e] : base[e], cnt, mass);
         __syncthreads();
         radix_resolve(pass, total, st, cnt, mass, wsum_c, wsum_m, &s_st);
         __syncthreads();
@@ -884,13 +938,15 @@ hipError_t launch_select(Rows q, Rows k, const uint8_t* pattern,
                        hq, G, s.qbar, s.kbar);
     CRISP_CHECK_LAUNCH();
     const float scale_log2 = kLog2e / sqrtf((float)kD);
+    const int fuse_softmax = nb <= 128;          // one work-group per 32 whole rows
     hipLaunchKernelGGL(pe_logits_kernel, dim3((nb + 31) / 32, (nb + 127) / 128, hq), dim3(256), 0,
-                       stream, s.qbar,
-                       s.kbar, pattern, nb, G, scale_log2, s.abar);
+                       stream, s.qbar, s.kbar, pattern, nb, G, scale_log2, fuse_softmax, s.abar);
     CRISP_CHECK_LAUNCH();
-    hipLaunchKernelGGL(pe_softmax_kernel, dim3((nb + 3) / 4, hq), dim3(256), 0, stream, pattern, nb,
-                       s.abar);
-    CRISP_CHECK_LAUNCH();
+    if (!fuse_softmax) {
+        hipLaunchKernelGGL(pe_softmax_kernel, dim3((nb + 3) / 4, hq), dim3(256), 0, stream, pattern,
+                           nb, s.abar);
+        CRISP_CHECK_LAUNCH();
+    }
     if (small_map) {
         hipLaunchKernelGGL(pe_radix_small_kernel, dim3(hq), dim3(256), 0, stream, pattern, nb, gamma,
                            s.abar, s.state);
