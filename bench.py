@@ -143,10 +143,16 @@ def main():
     ap.add_argument("--no-dense", action="store_true", help="skip the dense timing")
     ap.add_argument("--no-flexprefill", action="store_true",
                     help="skip the FlexPrefill-baseline timing")
+    ap.add_argument("--no-head-types", action="store_true",
+                    help="skip the attention-per-head-type breakdown (profiled runs: it adds "
+                         "attention calls on partial lists)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="end with a 1 GiB device-to-device copy (reference for counter runs)")
     ap.add_argument("--workload", default=WORKLOAD,
                     help="configuration to time (h128, the headline, by default; c1-c4 for context)")
+    ap.add_argument("--seq-len", type=int, default=None,
+                    help="the workload's head mix at another sequence length (context runs; "
+                         "no traffic figure or CPU baseline)")
     ap.add_argument("--crossover", action="store_true",
                     help="only sweep n for the sparse/dense crossover and print it")
     args = ap.parse_args()
@@ -164,7 +170,8 @@ def main():
         crossover(args)
         return
     workload = args.workload
-    spec = synth.config_spec(workload)
+    spec = synth.config_spec(workload, n=args.seq_len) if args.seq_len else synth.config_spec(workload)
+    full_size = workload == WORKLOAD and args.seq_len is None
     n, hq, hkv = spec.n, spec.hq, spec.hkv
     nb = -(-n // B)
     log(f"generating {workload}: n={n} hq={hq} hkv={hkv}")
@@ -313,9 +320,9 @@ def main():
         torch.cuda.synchronize()
         return float(np.median([e[3].elapsed_time(e[4]) for e in t_ev]))
 
-    empty_ms = attend_ms_on(np.zeros(hq, dtype=bool))
+    empty_ms = None if args.no_head_types else attend_ms_on(np.zeros(hq, dtype=bool))
     for name, sel in (("vertical_slash", pattern_h == 1), ("pooled_estimation", pattern_h == 0)):
-        if not sel.any():
+        if args.no_head_types or not sel.any():
             continue
         t_ms = attend_ms_on(sel)
         net_ms = t_ms - empty_ms * float((~sel).sum()) / hq
@@ -325,11 +332,12 @@ def main():
                          "attend_ms": round(t_ms, 3), "attend_ms_net": round(net_ms, 3),
                          "attend_tflops_net": round(t_pairs * PAIR_FLOP / (net_ms * 1e-3) / 1e12, 1)}
         log(f"attention on {name} heads only: {t_ms:.3f} ms ({net_ms:.3f} net), {t_pairs} pairs")
-    by_type["all_rows_empty_ms"] = round(empty_ms, 3)
+    if empty_ms is not None:
+        by_type["all_rows_empty_ms"] = round(empty_ms, 3)
     del out_t, col_idx
 
     achieved = pairs * PAIR_FLOP / (attend_ms * 1e-3) / 1e12
-    traffic = measured_traffic() if workload == WORKLOAD else None
+    traffic = measured_traffic() if full_size else None
     roofline = {
         "bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS,
         "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
@@ -374,7 +382,7 @@ def main():
         dst.copy_(src)             # reads and writes exactly 1 GiB
         torch.cuda.synchronize()
         del src, dst
-    if not args.no_cpu and workload == WORKLOAD:
+    if not args.no_cpu and full_size:
         log("timing the CPU oracle on a bounded sample ...")
         res["cpu_baseline"] = cpu_baseline(inp, pairs, nb, hq, hkv, n)
     print(json.dumps(res), flush=True)
