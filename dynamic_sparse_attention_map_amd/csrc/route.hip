@@ -324,11 +324,12 @@ finalize_kernel(const float* __restrict__ tile_sums, const float* __restrict__ p
 }
 
 // grid hq, 1024 threads, N_b <= kRouteSmall: the four kernels above for one
-// head in one work-group.  Every sum runs in the same order as there (thread
+// head in one work-group (beyond that, one work-group per head is slower
+// than the four launches).  Every sum runs in the same order as there (thread
 // (row i, part p) walks segments p, p+8, .. and, within each, tiles
 // seg, seg+64, ..; wave w takes tiles w, w+16, ..), so p_v, p_s, C_struct
 // and the routing bit are the same bits.
-constexpr int kRouteSmall = 256;
+constexpr int kRouteSmall = 64;
 
 __global__ void __launch_bounds__(1024)
 route_small_kernel(const float* __restrict__ part_m, const float* __restrict__ part_lo,

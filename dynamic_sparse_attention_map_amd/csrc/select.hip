@@ -614,12 +614,13 @@ __device__ void radix_resolve(int pass, size_t total, const PeState& st, const u
 }
 
 // grid hq, 256 threads: the whole cut-off of one head in one work-group,
-// for maps of at most kRadixSmall entries.  The same five passes, digits
-// and fixed-point masses as pe_radix_kernel (so the same result), with the
-// histograms in LDS only; it also seeds the state as pe_init_kernel does,
-// which it replaces.
-constexpr size_t kRadixSmall = (size_t)256 * 257 / 2;
-constexpr int kRadixCached = 128 * 129 / 2;   // maps this small are read once, into LDS
+// for maps of at most kRadixSmall entries (N_b <= 128), read once into LDS.
+// The same five passes, digits and fixed-point masses as pe_radix_kernel
+// (so the same result), with the histograms in LDS only; it also seeds the
+// state as pe_init_kernel does, which it replaces.  (Beyond this size the
+// passes over one work-group per head take longer than the multi-launch
+// path.)
+constexpr int kRadixSmall = 128 * 129 / 2;
 
 __global__ void __launch_bounds__(256)
 pe_radix_small_kernel(const uint8_t* __restrict__ pattern, int nb, float gamma,
@@ -630,7 +631,7 @@ pe_radix_small_kernel(const uint8_t* __restrict__ pattern, int nb, float gamma,
     __shared__ unsigned long long wsum_m[4];
     __shared__ uint32_t wsum_c[4];
     __shared__ PeState s_st;
-    __shared__ float vals[kRadixCached];
+    __shared__ float vals[kRadixSmall];
     const int h = blockIdx.x, tid = threadIdx.x;
     if (tid == 0) {
         PeState st = {};
@@ -639,9 +640,8 @@ pe_radix_small_kernel(const uint8_t* __restrict__ pattern, int nb, float gamma,
         s_st = st;
     }
     const size_t total = tri(nb);
-    const bool cached = total <= (size_t)kRadixCached;
     const float* base = abar + (size_t)h * total;
-    if (cached && !pattern[h])
+    if (!pattern[h])
         for (size_t e = tid; e < total; e += 256) vals[e] = base[e];
     __syncthreads();
     for (int pass = 0; pass < kRadixPasses; ++pass) {
@@ -654,7 +654,7 @@ pe_radix_small_kernel(const uint8_t* __restrict__ pattern, int nb, float gamma,
         }
         __syncthreads();
         for (size_t e = tid; e < total; e += 256)
-            radix_add(pass, nb, st, e, cached ? vals[e] : base[e], cnt, mass);
+            radix_add(pass, nb, st, e, vals[e], cnt, mass);
         __syncthreads();
         radix_resolve(pass, total, st, cnt, mass, wsum_c, wsum_m, &s_st);
         __syncthreads();
@@ -858,7 +858,7 @@ expand_fill_kernel(const uint8_t* __restrict__ pattern, int nb, const uint8_t* _
 // grid hq, 1024 threads: expand_count, expand_scan and expand_fill for one
 // head in one work-group (N_b <= kExpandSmall), the row lengths kept in LDS.
 // The same rows, offsets and K* as the three kernels.
-constexpr int kExpandSmall = 256;
+constexpr int kExpandSmall = 128;
 
 __global__ void __launch_bounds__(1024)
 expand_small_kernel(const uint8_t* __restrict__ pattern, int nb, const uint8_t* __restrict__ bitmap,
@@ -928,7 +928,7 @@ hipError_t launch_select(Rows q, Rows k, const uint8_t* pattern,
                        vs, sel_v, sel_s, sel_counts, s.bitmap);
     CRISP_CHECK_LAUNCH();
     const long long tri_nb = (long long)nb * (nb + 1) / 2;
-    const bool small_map = (size_t)tri_nb <= kRadixSmall;
+    const bool small_map = tri_nb <= kRadixSmall;
     if (!small_map) {
         hipLaunchKernelGGL(pe_init_kernel, dim3(hq), dim3(1024), 0, stream, pattern, gamma,
                            s.hist_mass, s.hist_count, s.pass_ctr, s.state);

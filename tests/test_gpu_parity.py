@@ -177,6 +177,18 @@ def test_tau_sweep_values(tau):
     P.log(P.check_select(inp, grh, gs, 1.0, orc).line() + f" tau={tau}")
 
 
+@pytest.mark.parametrize("n", [64 * B, 64 * B + 1, 128 * B, 128 * B + 1])
+def test_one_workgroup_path_boundaries(n):
+    """Either side of the lengths where the route reductions (N_b <= 64),
+    the list expansion and the PE cut-off (N_b <= 128) switch from one
+    work-group per head to several launches: routing, sets and CSR against
+    the oracle, outputs on sampled rows."""
+    sp = synth.custom_spec(n, 4, 2, [synth.VS, synth.DIFFUSE, synth.VS, synth.DIFFUSE],
+                           seed_id=140 + n % 7)
+    nb = -(-n // B)
+    case(synth.generate(sp), rows=P.sample_rows(nb, 4, 8, seed=n % 11), tag=f" n={n}")
+
+
 def test_c2_parity_sampled_rows():
     inp = synth.generate(synth.config_spec("c2"))
     nb = 32768 // B
