@@ -71,7 +71,12 @@ __device__ __forceinline__ void wait_copies()
 // an XCD start one head's adjacent pairs close together in time: their lists
 // are alike, they walk them in step, and all but the first find most K/V
 // tiles in L2.  (Interleaving the heads instead, pair by pair, leaves almost
-// no reuse: the long rows of diffuse heads start far apart in time.)
+// no reuse: the long rows of diffuse heads start far apart in time.)  XCD x
+// starts its chunks' heads at head x % G: vertical-slash heads, with short,
+// scattered lists, miss L2 far more often than diffuse heads, and this keeps
+// the XCDs from all running them at the same time.  (Runs inside a chunk are
+// rotated, never reordered across chunks, so the walk from the longest rows
+// down is kept.)
 __device__ __forceinline__ void
 attend_pair(int b, uint16_t* lds, uint32_t* list, Rows q, Rows k,
             const uint16_t* __restrict__ vt, const int32_t* __restrict__ row_ptr,
@@ -86,7 +91,7 @@ attend_pair(int b, uint16_t* lds, uint32_t* list, Rows q, Rows k,
     const int pair = (chunk / hkv) * run + r % run;
     if (pair >= npairs) return;
     const int g = chunk % hkv;
-    const int h = g * G + r / run;
+    const int h = g * G + (r / run + (b & 7)) % G;
     const int qb_hi = nb - 1 - 2 * pair;
     const int qb_lo = qb_hi - 1;                   // -1: no second block
 
