@@ -1,6 +1,6 @@
-// Routing kernels: proxy map (Alg. 2, lines 3-5) and the block-mass
-// reduction that yields the vertical / slash scores (Alg. 3, lines 3-5),
-// C_struct (Eq. 2) and the routing bit (Alg. 2, lines 9-13).
+// Routing kernels: proxy map (Alg. 2) and the block-mass
+// reduction that yields the vertical / slash scores (Alg. 3),
+// C_struct (Eq. 2) and the routing bit (Alg. 2).
 //
 // The proxy map A^ = Softmax(Q^ K^T / sqrt(d)) over the last R = min(B, n)
 // query rows is never stored.  proxy_map_kernel splits the keys into 128-key

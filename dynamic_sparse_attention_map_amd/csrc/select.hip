@@ -1,7 +1,7 @@
 // Index selection and block-list expansion kernels.
 //
 //   vs_select_kernel   VS budget per direction: the sink-aware noise floor
-//                      (Alg. 3, lines 7-12; Eq. 3-4), the median floor
+//                      (Alg. 3; Eq. 3-4), the median floor
 //                      (Appendix H) or FlexPrefill's cumulative rule (Alg. 6),
 //                      with stream compaction
 //   pe_*_kernel        pooled estimation for PE heads (Alg. 4): block-mean

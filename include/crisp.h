@@ -126,7 +126,7 @@ int crisp_workspace_size(int seq_len, int n_heads, int n_kv_heads, int head_dim,
  * the last R = min(block_size, seq_len) rows; A^ = Softmax(Q^ K^T / sqrt(d))
  * with the causal mask.  Outputs (device):
  *   p_v, p_s   float [n_heads][N_b]  block-pooled column / diagonal means of
- *              A^ over its R rows (Alg. 3 lines 3-5); each row sums to 1.
+ *              A^ over its R rows (Alg. 3); each row sums to 1.
  *              Entry (i, k) lies on the diagonal at offset o = q_i - k from
  *              its query q_i; diagonal (slash) block j collects the offsets
  *              (N_b-1-j)*B .. (N_b-j)*B - 1, so block N_b-1 is the recency

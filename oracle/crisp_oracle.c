@@ -55,7 +55,7 @@ static double dot(const float *a, const float *b, int d)
 }
 
 /*
- * Proxy attention of one query head (Alg. 2, lines 3-5): the representative
+ * Proxy attention of one query head (Alg. 2): the representative
  * query block Q^ is the last R = min(b, n) query rows (b = B); A^ =
  * Softmax(Q^ K^T / sqrt(d)).  Causal reading: row i sits at position
  * q_i = n - R + i and sees keys k <= q_i; entries with k > q_i are exactly 0.
@@ -86,7 +86,7 @@ static void proxy_rows(const float *qh, const float *kg, int n, int d, int R, do
 }
 
 /*
- * Directional block scores (Alg. 3, lines 3 and 5) and C_struct (Eq. 2).
+ * Directional block scores (Alg. 3) and C_struct (Eq. 2).
  * Blocks partition the n tokens into N_b = ceil(n / B) blocks (Section 4.3);
  * the last one holds n - (N_b - 1) B tokens.
  *   a_v = colmean(A^): a_v[k] = (1/R) sum_i A^[i,k]
@@ -156,7 +156,7 @@ int orc_block_scores(const double *ahat, int n, int B, int w_sink, int w_local,
 /*
  * PatSearch (Alg. 2) for every query head: proxy map, block scores,
  * C_struct (Eq. 2) and the routing rule "VS iff C_struct >= tau_proxy"
- * (Alg. 2, lines 9-13), the comparison taken in float.
+ * (Alg. 2), the comparison taken in float.
  * pattern: 1 = VS, 0 = PE.  p_v and p_s are [hq][N_b].
  */
 int orc_route(const uint16_t *q, const uint16_t *k, int n, int hq, int hkv, int d, int B,
@@ -258,7 +258,7 @@ static int cmp_int(const void *a, const void *b)
 }
 
 /*
- * Budget and top-k shared by both noise floors (Alg. 3, lines 10-12; Eq. 4):
+ * Budget and top-k shared by both noise floors (Alg. 3; Eq. 4):
  *   k = #{j : p[j] > theta}, counted over all Nb blocks
  *   k = clip(k, k_min, Nb);  S = top-k(p), ties to the lower block index.
  * pf holds p rounded to float.  Writes S ascending to sel, returns |S|.
@@ -282,7 +282,7 @@ static int floor_topk(const float *pf, int nb, float theta, int kmin, int32_t *s
 }
 
 /*
- * Sink-aware selection in one direction (Alg. 3, lines 7-12; Eq. 3 and 4):
+ * Sink-aware selection in one direction (Alg. 3; Eq. 3 and 4):
  *   r = max(1 - p[0] - p[Nb-1], 0);  mu = r / (Nb - 2);  theta = alpha * mu
  *   then floor_topk.  All in float, in that order.  theta_out receives
  *   theta and kth_out the k-th largest value (the decisive value when the
@@ -344,7 +344,7 @@ int orc_vs_select_median(const double *p, int nb, float alpha, int kmin, int32_t
 
 /*
  * Cumulative-gamma selection in one direction, the FlexPrefill rule the
- * paper compares against (Alg. 6, lines 2-5): p already sums to one, order
+ * paper compares against (Alg. 6): p already sums to one, order
  * it (desc, ties to the lower index), keep the shortest prefix whose
  * running sum reaches gamma.  kmin > 0 additionally clips the size to at
  * least kmin (FlexPrefill as configured in Section 5, "Setup").
@@ -368,7 +368,7 @@ int orc_gamma_select(const double *p, int nb, float gamma, int kmin, int32_t *se
 }
 
 /*
- * Pooled map of one query head for the PE path (Alg. 4, lines 3-6):
+ * Pooled map of one query head for the PE path (Alg. 4):
  *   Qbar[qb] = mean of Q over the tokens of query block qb (all queries; the
  *              last block may hold fewer than B),
  *   Kbar[kb] = mean of K over key block kb,
@@ -426,7 +426,7 @@ int orc_pe_map(const uint16_t *q, const uint16_t *k, int n, int hq, int hkv, int
 }
 
 /*
- * gamma-cumsum over the flattened pooled map (Alg. 4, lines 8-10):
+ * gamma-cumsum over the flattened pooled map (Alg. 4):
  * order the causal entries by (value desc, flat index qb*Nb+kb asc) on the
  * float-rounded values, K* = min{k : running sum >= gamma}, S = first K*.
  * selmask[qb*Nb+kb] = 1 for the selected entries.  Returns K*; vstar gets
@@ -462,7 +462,7 @@ int64_t orc_pe_select(const double *abar, int nb, float gamma, uint8_t *selmask,
 
 /*
  * Block index lists of one head: the mask M_S of Eq. 1 at block level.
- * VS (Alg. 3, line 14): S_v holds key-block columns; S_s holds slash blocks,
+ * VS (Alg. 3): S_v holds key-block columns; S_s holds slash blocks,
  *   slash block j being the diagonal band of offset block Nb-1-j, which for
  *   query block qb lands on key block qb-(Nb-1-j); {0, Nb-1} are the sink
  *   column and the recency diagonal (key block qb).

@@ -95,7 +95,7 @@ def nblocks(n: int, B: int = 128) -> int:
 
 
 def proxy_map(q, k, n, hq, hkv, d, h, B=128) -> np.ndarray:
-    """A^ of one query head, [min(B, n), n] float64 (Alg. 2, lines 3-5)."""
+    """A^ of one query head, [min(B, n), n] float64 (Alg. 2)."""
     out = np.zeros((min(B, n), n), dtype=np.float64)
     rc = lib().orc_proxy_map(_p(_u16(q)), _p(_u16(k)), n, hq, hkv, d, B, h, _p(out))
     assert rc == 0, rc
@@ -103,7 +103,7 @@ def proxy_map(q, k, n, hq, hkv, d, h, B=128) -> np.ndarray:
 
 
 def block_scores(ahat: np.ndarray, B=128, w_sink=W_SINK, w_local=W_LOCAL):
-    """(p_v, p_s, C_struct) of one head from its A^ (Alg. 3 lines 3-5, Eq. 2)."""
+    """(p_v, p_s, C_struct) of one head from its A^ (Alg. 3, Eq. 2)."""
     ahat = np.ascontiguousarray(ahat, dtype=np.float64)
     n = ahat.shape[1]
     assert ahat.shape[0] == min(B, n)
@@ -179,7 +179,7 @@ def vs_select(p: np.ndarray, alpha: float, kmin_blocks: int = K_MIN_TOKENS // 12
 
 
 def gamma_select(p: np.ndarray, gamma: float = GAMMA, kmin_blocks: int = 0) -> np.ndarray:
-    """Cumulative-gamma selection in one direction (Alg. 6, lines 2-5)."""
+    """Cumulative-gamma selection in one direction (Alg. 6)."""
     p = np.ascontiguousarray(p, dtype=np.float64)
     nb = p.shape[0]
     sel = np.zeros(nb, dtype=np.int32)
@@ -188,7 +188,7 @@ def gamma_select(p: np.ndarray, gamma: float = GAMMA, kmin_blocks: int = 0) -> n
 
 
 def pe_map(q, k, n, hq, hkv, d, h, B=128) -> np.ndarray:
-    """Normalised pooled map A-bar of one query head, [Nb, Nb] (Alg. 4, lines 3-6)."""
+    """Normalised pooled map A-bar of one query head, [Nb, Nb] (Alg. 4)."""
     nb = nblocks(n, B)
     out = np.zeros((nb, nb), dtype=np.float64)
     rc = lib().orc_pe_map(_p(_u16(q)), _p(_u16(k)), n, hq, hkv, d, B, h, _p(out))
@@ -205,7 +205,7 @@ class PESel:
 
 
 def pe_select(abar: np.ndarray, gamma: float = GAMMA) -> PESel:
-    """gamma-cumsum over the flattened pooled map (Alg. 4, lines 8-10)."""
+    """gamma-cumsum over the flattened pooled map (Alg. 4)."""
     abar = np.ascontiguousarray(abar, dtype=np.float64)
     nb = abar.shape[0]
     mask = np.zeros((nb, nb), dtype=np.uint8)
@@ -217,7 +217,7 @@ def pe_select(abar: np.ndarray, gamma: float = GAMMA) -> PESel:
 
 def expand(nb: int, vs: bool, sv=None, ss=None, pe_mask=None, base: int = 0,
            col_idx: np.ndarray | None = None):
-    """Block index lists of one head (Alg. 3 line 14 / Alg. 4 + {0, qb}).
+    """Block index lists of one head (Alg. 3 / Alg. 4 + {0, qb}).
 
     Returns (row_ptr[Nb+1] int32 absolute offsets, col_idx, count)."""
     sv = np.ascontiguousarray(sv if sv is not None else np.zeros(0), dtype=np.int32)

@@ -133,7 +133,7 @@ def test_uniform_logits_closed_form():
     assert r.p_v[0][-1] == pytest.approx(pvl, rel=1e-12)
     assert r.c_struct[0] == pytest.approx(pv0 + pvl, rel=1e-12)
     assert r.c_struct[0] == pytest.approx(0.047, abs=0.001)
-    assert r.pattern[0] == 0                  # diffuse: PE (Alg. 2 lines 9-13)
+    assert r.pattern[0] == 0                  # diffuse: PE (Alg. 2)
 
 
 def test_one_hot_sink_routes_vs():
@@ -574,7 +574,7 @@ def test_ragged_plan_small_nb_is_dense():
 
 # ------------------------------------------- FlexPrefill baseline (App. A)
 def brute_abar(q, k, h, G, B):
-    """Alg. 5 line 3 by numpy: softmax over blocks of the pooled query and
+    """Alg. 5 by numpy: softmax over blocks of the pooled query and
     the per-block key means."""
     n, d = q.shape[1], q.shape[2]
     R = min(B, n)
