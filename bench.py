@@ -157,8 +157,9 @@ def main():
                     help="only sweep n for the sparse/dense crossover and print it")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only: every step is per query head and this build runs "
-              f"on a single MI355X (asked for --gpus {args.gpus})", file=sys.stderr)
+        print(f"bench.py measures one GPU only: every step is per query head and runs on a single "
+              f"MI355X; the head-sharded multi-GPU layout is a design, not code "
+              f"(asked for --gpus {args.gpus})", file=sys.stderr)
         sys.exit(2)
 
     import torch
