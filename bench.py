@@ -133,6 +133,40 @@ def crossover(args):
                       "first_n_sparse_faster": faster[0] if faster else None}), flush=True)
 
 
+def gemm_ceiling():
+    """The practical bf16 matrix-core rate of this part, for scale: the
+    vendor library's GEMM (torch.matmul on rocBLAS / hipBLASLt) on random and
+    on all-zero inputs (the part is power-limited, so data toggling moves the
+    clock).  Prints one JSON line."""
+    import torch
+    g = torch.Generator(device="cuda").manual_seed(0)
+    rows = []
+    for (m, n, k) in ((8192, 8192, 8192), (16384, 16384, 8192)):
+        for kind in ("random", "zeros"):
+            a = torch.randn(m, k, device="cuda", dtype=torch.bfloat16, generator=g)
+            b = torch.randn(k, n, device="cuda", dtype=torch.bfloat16, generator=g)
+            if kind == "zeros":
+                a.zero_()
+                b.zero_()
+            c = a @ b
+            torch.cuda.synchronize()
+            reps = 30
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(reps):
+                c = a @ b
+            e1.record()
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1) / reps
+            rows.append({"m": m, "n": n, "k": k, "inputs": kind, "ms": round(ms, 3),
+                         "tflops": round(2.0 * m * n * k / (ms * 1e-3) / 1e12, 1)})
+            log(f"gemm {m}x{n}x{k} {kind}: {ms:.3f} ms, {rows[-1]['tflops']} TFLOP/s")
+            del a, b, c
+    print(json.dumps({"metric": "bf16_gemm_ceiling", "library": "torch.matmul", "rows": rows,
+                      "peak_tflops": PEAK_BF16_TFLOPS}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -153,6 +187,8 @@ def main():
     ap.add_argument("--seq-len", type=int, default=None,
                     help="the workload's head mix at another sequence length (context runs; "
                          "no traffic figure or CPU baseline)")
+    ap.add_argument("--gemm-ceiling", action="store_true",
+                    help="only time the vendor bf16 GEMM (the practical matrix-core rate)")
     ap.add_argument("--crossover", action="store_true",
                     help="only sweep n for the sparse/dense crossover and print it")
     args = ap.parse_args()
@@ -169,6 +205,9 @@ def main():
     crisp.lib()
     if args.crossover:
         crossover(args)
+        return
+    if args.gemm_ceiling:
+        gemm_ceiling()
         return
     workload = args.workload
     spec = synth.config_spec(workload, n=args.seq_len) if args.seq_len else synth.config_spec(workload)
