@@ -83,8 +83,16 @@ def cpu_baseline(inp, plan_pairs, nb, hq, hkv, n, rows_per_head=2):
     O.attend(inp.q, inp.k, inp.v, n, hq, hkv, 128, plan.row_ptr, plan.col_idx, rows)
     t_att = time.perf_counter() - t0
     est_s = t_rs + t_att * total_pairs / max(sampled_pairs, 1)
+    cpu_model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            cpu_model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")),
+                             None)
+    except OSError:
+        pass
     return {
         "value": round(est_s * 1e3, 1), "unit": "ms", "cores": O.threads(), "kind": "oracle",
+        "cpu_model": cpu_model,
         "sample": (f"route+select of all {hq} heads in full ({t_rs:.1f} s); attention of "
                    f"{len(rows)} query blocks ({rows_per_head} per head, {sampled_pairs} of "
                    f"{total_pairs} block pairs, {t_att:.1f} s) extrapolated by block pairs"),
@@ -170,7 +178,7 @@ def gemm_ceiling():
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--alpha", type=float, default=1.0)
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
