@@ -352,8 +352,13 @@ attend_pair(int b, uint16_t* lds, uint32_t* list, Rows q, Rows k,
                 update_max();
                 probs();
             }
+            // the wavefront in its matrix phase issues first, so the matrix
+            // core stays fed and the other wavefront's vector work fills the
+            // gaps (raising the vector phase instead was 2% slower)
+            __builtin_amdgcn_s_setprio(1);
             if (t >= 1 && prev.act) pv_mfma((t - 1) & 3);   // M_t
             if (cur.act) qk(t & 3);
+            __builtin_amdgcn_s_setprio(0);
             if (half == 0 && cur.act) {                     // V_t
                 if (cur.diag) mask(cur.sub);
                 update_max();
