@@ -16,8 +16,9 @@
 // the diagonal key block; sub-tiles that lie entirely in a wavefront's
 // future are skipped.  Fragment reads are issued several products ahead
 // of the matrix cores (scheduling-group hints), and the two wavefronts on
-// each SIMD run the matrix and vector phases of a tile in opposite order
-// (schedule below).
+// each SIMD run the matrix and vector phases of a tile in opposite order,
+// the one in its matrix phase with the higher issue priority (schedule
+// below).
 #include "crisp_common.h"
 #include "crisp_kernels.h"
 
