@@ -430,7 +430,7 @@ def main():
         dst.copy_(src)             # reads and writes exactly 1 GiB
         torch.cuda.synchronize()
         del src, dst
-    if not args.no_cpu and full_size:
+    if not args.no_cpu and args.seq_len is None:
         log("timing the CPU oracle on a bounded sample ...")
         res["cpu_baseline"] = cpu_baseline(inp, pairs, nb, hq, hkv, n)
     print(json.dumps(res), flush=True)
