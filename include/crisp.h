@@ -28,7 +28,10 @@
  *   pointer after a call returns and never allocates device memory.
  * Streams: stream is a hipStream_t (NULL = the default stream).  Every call
  *   is asynchronous on it; results are valid once the stream has reached
- *   them.  Calls on different streams need distinct workspaces.
+ *   them.  Calls on different streams need distinct workspaces.  No call
+ *   synchronises, allocates, copies through the host or records a memset,
+ *   so a call (or a whole prefill) can be captured into a HIP graph and
+ *   replayed; the workspace and the pointers are then fixed by the graph.
  * Errors: every call returns CRISP_OK (0) or a positive CRISP_ERR_* code.
  *   Arguments are validated on the host before anything is launched; on a
  *   validation error nothing is launched and no output is touched.
