@@ -9,6 +9,7 @@ configuration), Llama shape at 524288 tokens (c4), and the mass-cliff sweep
 """
 import json
 import os
+import tempfile
 
 import numpy as np
 import pytest
@@ -21,7 +22,8 @@ from oracle import oracle as O
 pytestmark = pytest.mark.gpu
 
 B = 128
-OUT_DIR = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "gpurun_out")
+# where the mass-cliff block counts are written (one JSON file per length)
+OUT_DIR = os.environ.get("CRISP_TEST_OUT_DIR") or os.path.join(tempfile.gettempdir(), "crisp_test_out")
 
 
 @pytest.fixture(scope="module", autouse=True)
