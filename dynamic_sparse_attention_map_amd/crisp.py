@@ -128,10 +128,62 @@ def _opts(opts):
     return None if opts is None else C.byref(opts)
 
 
-def _shape(q, k):
+def _tensor(t, name, dtype=None, ndim=None, numel=None, min_numel=None):
+    """A contiguous device tensor of the given dtype (bfloat16 by default)."""
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    want = torch.bfloat16 if dtype is None else dtype
+    if t.dtype != want:
+        raise ValueError(f"{name} must be {want}, got {t.dtype}")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dimensions, got shape {tuple(t.shape)}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if numel is not None and t.numel() != numel:
+        raise ValueError(f"{name} must have {numel} elements, got {t.numel()}")
+    if min_numel is not None and t.numel() < min_numel:
+        raise ValueError(f"{name} must have at least {min_numel} elements, got {t.numel()}")
+    return t
+
+
+def _shape(q, k, v=None, out=None):
+    """(seq_len, n_heads, n_kv_heads, head_dim) of q [H, n, d], k [H_kv, n, d],
+    after checking that v / out match k / q, then dtypes, devices and
+    contiguity.  head_dim and the block size are checked by the library."""
+    import torch
+    for t, name in ((q, "q"), (k, "k"), (v, "v"), (out, "out")):
+        if t is None:
+            continue
+        if not isinstance(t, torch.Tensor):
+            raise TypeError(f"{name} must be a torch.Tensor")
+        if t.dim() != 3:
+            raise ValueError(f"{name} must have 3 dimensions, got shape {tuple(t.shape)}")
     hq, n, d = q.shape
     hkv = k.shape[0]
+    if k.shape[1] != n or k.shape[2] != d:
+        raise ValueError(f"k {tuple(k.shape)} does not match q {tuple(q.shape)} in length or head_dim")
+    if v is not None and v.shape != k.shape:
+        raise ValueError(f"v {tuple(v.shape)} must have k's shape {tuple(k.shape)}")
+    if out is not None and out.shape != q.shape:
+        raise ValueError(f"out {tuple(out.shape)} must have q's shape {tuple(q.shape)}")
+    for t, name in ((q, "q"), (k, "k"), (v, "v"), (out, "out")):
+        if t is not None:
+            _tensor(t, name)
+            if t.device != q.device:
+                raise ValueError(f"{name} must be on q's device")
     return n, hq, hkv, d
+
+
+def _workspace(ws):
+    import torch
+    return _tensor(ws, "ws", dtype=torch.uint8)
+
+
+def _nblocks(n, block_size):
+    return -(-n // block_size) if block_size > 0 else 0
 
 
 def crisp_workspace_size(seq_len, n_heads, n_kv_heads, head_dim=128, block_size=128):
@@ -150,7 +202,14 @@ def alloc_workspace(seq_len, n_heads, n_kv_heads, device="cuda"):
 
 
 def crisp_route(q, k, ws, pattern, c_struct, p_v, p_s, opts=None, block_size=128, stream=None):
+    import torch
     n, hq, hkv, d = _shape(q, k)
+    _workspace(ws)
+    nb = _nblocks(n, block_size)
+    _tensor(pattern, "pattern", dtype=torch.uint8, numel=hq)
+    _tensor(c_struct, "c_struct", dtype=torch.float32, numel=hq)
+    _tensor(p_v, "p_v", dtype=torch.float32, numel=hq * nb)
+    _tensor(p_s, "p_s", dtype=torch.float32, numel=hq * nb)
     _check(lib().crisp_route(_ptr(q), _ptr(k), n, hq, hkv, d, block_size, _opts(opts), _ptr(ws),
                              ws.numel(), _ptr(pattern), _ptr(c_struct), _ptr(p_v), _ptr(p_s),
                              _stream(stream)), "crisp_route")
@@ -158,28 +217,56 @@ def crisp_route(q, k, ws, pattern, c_struct, p_v, p_s, opts=None, block_size=128
 
 def crisp_select(q, k, pattern, p_v, p_s, alpha, ws, sel_v, sel_s, sel_counts, row_ptr, col_idx,
                  opts=None, block_size=128, stream=None):
+    import torch
     n, hq, hkv, d = _shape(q, k)
+    _workspace(ws)
+    nb = _nblocks(n, block_size)
+    _tensor(pattern, "pattern", dtype=torch.uint8, numel=hq)
+    _tensor(p_v, "p_v", dtype=torch.float32, numel=hq * nb)
+    _tensor(p_s, "p_s", dtype=torch.float32, numel=hq * nb)
+    _tensor(sel_v, "sel_v", dtype=torch.int32, numel=hq * nb)
+    _tensor(sel_s, "sel_s", dtype=torch.int32, numel=hq * nb)
+    _tensor(sel_counts, "sel_counts", dtype=torch.int32, numel=hq * 3)
+    _tensor(row_ptr, "row_ptr", dtype=torch.int32, numel=hq * (nb + 1))
+    _tensor(col_idx, "col_idx", dtype=torch.int32)
     _check(lib().crisp_select(_ptr(q), _ptr(k), _ptr(pattern), _ptr(p_v), _ptr(p_s), n, hq, hkv, d,
                               block_size, float(alpha), _opts(opts), _ptr(ws), ws.numel(),
                               _ptr(sel_v), _ptr(sel_s), _ptr(sel_counts), _ptr(row_ptr),
                               _ptr(col_idx), col_idx.numel(), _stream(stream)), "crisp_select")
 
 
-def crisp_attend(q, k, v, row_ptr, col_idx, ws, out, block_size=128, stream=None):
-    n, hq, hkv, d = _shape(q, k)
+def crisp_attend(q, k, v, row_ptr, col_idx, ws, out, block_size=128, stream=None,
+                 check_lists=True):
+    """Eq. 1 on given lists.  row_ptr int32 [hq, N_b + 1] of absolute offsets
+    into col_idx (int32); every offset must lie inside col_idx.  With
+    check_lists (and outside graph capture) that is checked on a host copy of
+    row_ptr, which synchronises with the device; timing loops pass False."""
+    import torch
+    n, hq, hkv, d = _shape(q, k, v, out)
+    _workspace(ws)
+    nb = _nblocks(n, block_size)
+    _tensor(row_ptr, "row_ptr", dtype=torch.int32, numel=hq * (nb + 1))
+    _tensor(col_idx, "col_idx", dtype=torch.int32)
+    if n > 0 and check_lists and not torch.cuda.is_current_stream_capturing():
+        rp = row_ptr.detach().to("cpu").view(hq, nb + 1)
+        lo, hi = int(rp.min()), int(rp.max())
+        if lo < 0 or hi > col_idx.numel() or bool((rp[:, 1:] < rp[:, :-1]).any()):
+            raise ValueError("row_ptr must be non-decreasing per head and stay inside col_idx")
     _check(lib().crisp_attend(_ptr(q), _ptr(k), _ptr(v), _ptr(row_ptr), _ptr(col_idx), n, hq, hkv, d,
                               block_size, _ptr(ws), ws.numel(), _ptr(out), _stream(stream)),
            "crisp_attend")
 
 
 def crisp_attend_dense(q, k, v, ws, out, block_size=128, stream=None):
-    n, hq, hkv, d = _shape(q, k)
+    n, hq, hkv, d = _shape(q, k, v, out)
+    _workspace(ws)
     _check(lib().crisp_attend_dense(_ptr(q), _ptr(k), _ptr(v), n, hq, hkv, d, block_size, _ptr(ws),
                                     ws.numel(), _ptr(out), _stream(stream)), "crisp_attend_dense")
 
 
 def crisp_prefill(q, k, v, alpha, ws, out, opts=None, block_size=128, stream=None):
-    n, hq, hkv, d = _shape(q, k)
+    n, hq, hkv, d = _shape(q, k, v, out)
+    _workspace(ws)
     _check(lib().crisp_prefill(_ptr(q), _ptr(k), _ptr(v), n, hq, hkv, d, block_size, float(alpha),
                                _opts(opts), _ptr(ws), ws.numel(), _ptr(out), _stream(stream)),
            "crisp_prefill")

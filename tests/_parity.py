@@ -9,7 +9,10 @@ Contract (from the hot path's definition):
 """
 from __future__ import annotations
 
+import json
+import os
 import sys
+import tempfile
 
 import numpy as np
 import torch
@@ -21,6 +24,8 @@ B = 128
 BAND = 1e-4
 REL_L2 = 1e-2
 MAX_ABS = 2e-2
+# where per-case parity records (set counts, attention comparisons) go
+OUT_DIR = os.environ.get("CRISP_TEST_OUT_DIR") or os.path.join(tempfile.gettempdir(), "crisp_test_out")
 
 
 def log(*a):
@@ -175,6 +180,44 @@ class Report:
     def line(self):
         return (f"[{self.name}] compared={self.compared} mismatches={self.mismatch} "
                 f"exempt={self.exempt} non_exempt={self.mismatch - self.exempt}")
+
+    def as_dict(self):
+        return {"compared": self.compared, "mismatches": self.mismatch, "exempt": self.exempt,
+                "non_exempt": self.mismatch - self.exempt}
+
+
+def record(case: str, key: str, value) -> None:
+    """Merge `value` under `key` into OUT_DIR/parity_<case>.json, so the
+    counts a run produced survive beyond its log."""
+    os.makedirs(OUT_DIR, exist_ok=True)
+    path = os.path.join(OUT_DIR, f"parity_{case}.json")
+    data = {}
+    if os.path.exists(path):
+        with open(path) as f:
+            data = json.load(f)
+    data[key] = value
+    with open(path, "w") as f:
+        json.dump(data, f, indent=1, sort_keys=True)
+
+
+def attention_record(got: np.ndarray, want: np.ndarray, heads: np.ndarray) -> dict:
+    """Comparison summary of got/want [m, rows, d]: query rows compared,
+    overall rel-L2 / max-abs and the worst per-head values (heads[i] is the
+    head of entry i)."""
+    g = got.astype(np.float64)
+    w = want.astype(np.float64)
+    per = []
+    for h in np.unique(heads):
+        m = heads == h
+        e = g[m] - w[m]
+        per.append((float(np.linalg.norm(e) / max(np.linalg.norm(w[m]), 1e-30)),
+                    float(np.abs(e).max())))
+    e = g - w
+    return {"queries": int(got.shape[0] * (got.shape[1] if got.ndim == 3 else 1)),
+            "rel_l2": float(np.linalg.norm(e) / max(np.linalg.norm(w), 1e-30)),
+            "max_abs": float(np.abs(e).max()) if e.size else 0.0,
+            "worst_head_rel_l2": max(r for r, _ in per) if per else 0.0,
+            "worst_head_max_abs": max(m for _, m in per) if per else 0.0}
 
 
 def check_select(inp, gr, gs, alpha, orc_route: O.Route, heads=None, rep=None, gamma=O.GAMMA,

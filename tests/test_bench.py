@@ -70,3 +70,15 @@ def test_bench_json_line():
     assert set(st) == {"route", "select", "v_relayout", "attend"}
     assert sum(st.values()) <= d["value"] * 1.05
     assert d["step_ms"]["p10"] <= d["step_ms"]["median"] <= d["step_ms"]["p90"]
+
+
+def test_stratified_blocks():
+    for nb, per in ((1024, 64), (4096, 64), (64, 64), (10, 64)):
+        b = bench.stratified_blocks(nb, per, seed=3)
+        assert len(b) == min(nb, per) and len(set(b.tolist())) == len(b)
+        assert b[0] == 0 and b[-1] == nb - 1 and list(b) == sorted(b)
+
+
+def test_diagonal_pairs_count_three_quarters():
+    assert bench.pair_flop(10, 0) == 10 * bench.PAIR_FLOP
+    assert bench.pair_flop(10, 4) == 6 * bench.PAIR_FLOP + 3 * bench.PAIR_FLOP

@@ -200,3 +200,26 @@ def test_batch_binding_rejects_mismatched_views():
         qt = torch.zeros(4, 128, 10, dtype=torch.bfloat16).transpose(1, 2)
         crisp.crisp_prefill_batch([qt], [k.transpose(1, 2).contiguous().transpose(1, 2)], [k], [q],
                                   1.0, ws)
+
+
+def test_binding_rejects_bad_tensors():
+    """The binding's own checks: dtype, device, contiguity, matching shapes
+    and index array sizes are refused before any call reaches the library."""
+    import torch
+    q = torch.zeros(4, 10, 128, dtype=torch.bfloat16)
+    k = torch.zeros(1, 10, 128, dtype=torch.bfloat16)
+    ws = torch.zeros(256, dtype=torch.uint8)
+    with pytest.raises(ValueError, match="device"):          # host tensors
+        crisp.crisp_prefill(q, k, k, 1.0, ws, q)
+    with pytest.raises(ValueError, match="bfloat16"):
+        crisp.crisp_prefill(q.float(), k, k, 1.0, ws, q)
+    with pytest.raises(ValueError, match="dimensions"):
+        crisp.crisp_attend_dense(q[0], k, k, ws, q)
+    with pytest.raises(ValueError, match="match"):            # k length differs from q
+        crisp.crisp_prefill(q, k[:, :5], k, 1.0, ws, q)
+    with pytest.raises(ValueError, match="k's shape"):
+        crisp.crisp_prefill(q, k, q, 1.0, ws, q)
+    with pytest.raises(ValueError, match="q's shape"):
+        crisp.crisp_prefill(q, k, k, 1.0, ws, q[:2])
+    with pytest.raises(TypeError):
+        crisp.crisp_attend(q, k, [0, 1], None, None, ws, q)

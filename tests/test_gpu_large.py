@@ -9,7 +9,6 @@ configuration), Llama shape at 524288 tokens (c4), and the mass-cliff sweep
 """
 import json
 import os
-import tempfile
 
 import numpy as np
 import pytest
@@ -23,7 +22,7 @@ pytestmark = pytest.mark.gpu
 
 B = 128
 # where the mass-cliff block counts are written (one JSON file per length)
-OUT_DIR = os.environ.get("CRISP_TEST_OUT_DIR") or os.path.join(tempfile.gettempdir(), "crisp_test_out")
+OUT_DIR = P.OUT_DIR
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -47,7 +46,13 @@ def sample_queries(nb, hq, blocks_per_head, queries_per_block, seed):
     return np.array(sel, dtype=np.int32)
 
 
-def full_case(name, n=None, blocks_per_head=64, queries_per_block=2, prefill_check=True):
+def full_case(name, n=None, blocks_per_head=64, queries_per_block=2, whole_blocks_per_head=16,
+              prefill_check=True):
+    """Routing and sets of every head against the oracle; attention on the
+    oracle's lists compared on `whole_blocks_per_head` stratified query blocks
+    per head (all 128 rows each: qb = 0, N_b - 1 and uniform others) and on
+    `queries_per_block` queries in each of `blocks_per_head` stratified
+    blocks per head."""
     spec = synth.config_spec(name, n)
     n, hq, hkv = spec.n, spec.hq, spec.hkv
     nb = -(-n // B)
@@ -61,11 +66,29 @@ def full_case(name, n=None, blocks_per_head=64, queries_per_block=2, prefill_che
     P.log(f"case {name}: oracle routing + selection")
     orc_r = O.route(inp.q, inp.k, n, hq, hkv)
     P.check_route(grh, orc_r, margin=0.05)
+    P.record(name, "routing", {"heads": hq, "mismatches": 0,
+                               "min_margin": float(np.min(np.abs(orc_r.c_struct - O.TAU_PROXY)))})
     rep = P.check_select(inp, grh, gs, 1.0, orc_r)
     P.log(rep.line())
+    P.record(name, "selection", rep.as_dict())
     plan = O.plan(inp.q, inp.k, n, hq, hkv, alpha=1.0, routed=orc_r)
-    P.log(f"case {name}: attention on the oracle's lists, sampled queries")
+    P.log(f"case {name}: attention on the oracle's lists")
     out = P.gpu_attend(q, k, v, plan.row_ptr, plan.col_idx, ws)
+    # whole query blocks: every row of the diagonal (masked) block and of
+    # the blocks before it
+    rows = P.sample_rows(nb, hq, whole_blocks_per_head, seed=7 * n + hq)
+    want_b = O.attend(inp.q, inp.k, inp.v, n, hq, hkv, 128, plan.row_ptr, plan.col_idx, rows)
+    full = out.view(hq * nb, B, 128) if n % B == 0 else None
+    assert full is not None, "whole-block sampling assumes n is a multiple of the block size"
+    got_b = full[torch.as_tensor(rows, dtype=torch.long, device=out.device)].float().cpu().numpy()
+    P.check_outputs(got_b, want_b, f"{name} attend ({len(rows)} whole blocks)")
+    for h in range(hq):
+        m = rows // nb == h
+        P.check_outputs(got_b[m], want_b[m], f"{name} blocks head {h}")
+    rec = P.attention_record(got_b, want_b, rows // nb)
+    rec["blocks_per_head"] = int(len(rows) // hq)
+    P.record(name, "attention_whole_blocks", rec)
+    # single queries in many more blocks
     sel = sample_queries(nb, hq, blocks_per_head, queries_per_block, seed=n + hq)
     want = O.attend_queries(inp.q, inp.k, inp.v, n, hq, hkv, 128, plan.row_ptr, plan.col_idx, sel)
     hs = torch.as_tensor(sel[:, 0], dtype=torch.long, device=out.device)
@@ -75,6 +98,9 @@ def full_case(name, n=None, blocks_per_head=64, queries_per_block=2, prefill_che
     for h in range(hq):
         m = sel[:, 0] == h
         P.check_outputs(got[m][:, None, :], want[m][:, None, :], f"{name} head {h}")
+    rec = P.attention_record(got[:, None, :], want[:, None, :], sel[:, 0])
+    rec["blocks_per_head"] = blocks_per_head
+    P.record(name, "attention_sampled_queries", rec)
     if prefill_check:
         # the end-to-end prefill on the GPU's own lists equals the staged calls
         out2 = torch.empty_like(q)
@@ -87,6 +113,7 @@ def full_case(name, n=None, blocks_per_head=64, queries_per_block=2, prefill_che
                 and np.array_equal(gs["col_idx"][gs["row_ptr"][h][0]:gs["row_ptr"][h][-1]],
                                    plan.col_idx[plan.row_ptr[h][0]:plan.row_ptr[h][-1]])]
         P.log(f"case {name}: heads with identical lists: {len(same)}/{hq}")
+        P.record(name, "heads_with_identical_lists", len(same))
         m = np.isin(sel[:, 0], same)
         got2 = out2[hs[torch.as_tensor(m, device=out.device)], ps[torch.as_tensor(m, device=out.device)]].float().cpu().numpy()
         P.check_outputs(got2[:, None, :], want[m][:, None, :], f"{name} prefill")
@@ -102,7 +129,7 @@ def test_h128_llama_131072():
 
 
 def test_c4_llama_524288():
-    full_case("c4", blocks_per_head=64, queries_per_block=1)
+    full_case("c4", blocks_per_head=64, queries_per_block=2, whole_blocks_per_head=8)
 
 
 @pytest.mark.parametrize("n", synth.MASS_CLIFF_NS)
@@ -126,6 +153,7 @@ def test_c5_mass_cliff_sweep(n):
         gs = P.host(P.gpu_select(q, k, gr, alpha, ws))
         rep = P.check_select(inp, grh, gs, alpha, orc_r)
         P.log(rep.line() + f" alpha={alpha}")
+        P.record(f"c5_n{n}", f"selection_alpha{alpha}", rep.as_dict())
         pairs = int((gs["row_ptr"][:, nb] - gs["row_ptr"][:, 0]).sum())
         crisp_sel = [int(gs["counts"][h][0] + gs["counts"][h][1]) for h in range(hq)]
         record["alpha"][str(alpha)] = {"crisp_blocks_per_head": crisp_sel, "pairs": pairs}

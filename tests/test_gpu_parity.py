@@ -22,10 +22,14 @@ def _gpu():
 
 
 def case(inp, alpha=1.0, rows=None, tag=""):
-    """Route, select and attend on the GPU; check all three against the oracle."""
+    """Route, select and attend on the GPU; check all three against the oracle
+    (attention on the oracle's lists, on the query blocks `rows`: all of
+    them by default, none for an empty array).  The counts and errors are
+    also written to the parity record of the case."""
     sp = inp.spec
     n, hq, hkv = sp.n, sp.hq, sp.hkv
     nb = -(-n // B)
+    name = f"{sp.name}{tag}".replace(" ", "_").replace("=", "")
     P.log(f"case {sp.name}{tag}: n={n} hq={hq} hkv={hkv} alpha={alpha}")
     q, k, v = P.to_dev(inp)
     ws = crisp.alloc_workspace(n, hq, hkv)
@@ -36,20 +40,23 @@ def case(inp, alpha=1.0, rows=None, tag=""):
     gs = P.host(P.gpu_select(q, k, gr, alpha, ws))
     rep = P.check_select(inp, grh, gs, alpha, orc_r)
     P.log(rep.line())
+    P.record(name, "selection", rep.as_dict())
     plan = O.plan(inp.q, inp.k, n, hq, hkv, alpha=alpha)
     out = P.gpu_attend(q, k, v, plan.row_ptr, plan.col_idx, ws)
     if rows is None:
         rows = np.arange(hq * nb, dtype=np.int32)
-    want = O.attend(inp.q, inp.k, inp.v, n, hq, hkv, 128, plan.row_ptr, plan.col_idx, rows)
-    full = torch.zeros(hq, nb * B, 128)          # rows past n (a partial last block) are 0
-    full[:, :n] = out.float().cpu()
-    got = full.numpy().reshape(hq * nb, B, 128)[rows]
-    P.check_outputs(got, want, f"{sp.name}{tag} attend")
-    for h in range(hq):
-        sel = rows // nb == h
-        if sel.any():
-            P.check_outputs(got[sel], want[sel], f"{sp.name}{tag} head {h}")
-    return dict(q=q, k=k, v=v, ws=ws, gr=gr, gs=gs, plan=plan)
+    if len(rows):
+        want = O.attend(inp.q, inp.k, inp.v, n, hq, hkv, 128, plan.row_ptr, plan.col_idx, rows)
+        full = torch.zeros(hq, nb * B, 128)          # rows past n (a partial last block) are 0
+        full[:, :n] = out.float().cpu()
+        got = full.numpy().reshape(hq * nb, B, 128)[rows]
+        P.check_outputs(got, want, f"{sp.name}{tag} attend")
+        for h in range(hq):
+            sel = rows // nb == h
+            if sel.any():
+                P.check_outputs(got[sel], want[sel], f"{sp.name}{tag} head {h}")
+        P.record(name, "attention_whole_blocks", P.attention_record(got, want, rows // nb))
+    return dict(q=q, k=k, v=v, ws=ws, gr=gr, gs=gs, plan=plan, out=out, inp=inp)
 
 
 def test_c1_full_parity():
@@ -189,11 +196,34 @@ def test_one_workgroup_path_boundaries(n):
     case(synth.generate(sp), rows=P.sample_rows(nb, 4, 8, seed=n % 11), tag=f" n={n}")
 
 
-def test_c2_parity_sampled_rows():
-    inp = synth.generate(synth.config_spec("c2"))
-    nb = 32768 // B
-    rows = P.sample_rows(nb, 32, 6, seed=2)
-    case(inp, rows=rows)
+_C2 = {}
+
+
+def c2_state():
+    """c2 (32768 tokens, 32/8 heads) routed, selected and attended once per
+    module: routing and sets checked against the oracle for every head."""
+    if not _C2:
+        _C2.update(case(synth.generate(synth.config_spec("c2")), rows=np.zeros(0, np.int32)))
+    return _C2
+
+
+@pytest.mark.parametrize("part", range(4))
+def test_c2_full_parity(part):
+    """Every query block of every head of c2 (all 256 per head, in four
+    groups of 8 heads): attention on the oracle's lists against the oracle."""
+    st = c2_state()
+    nb, hq = 32768 // B, 32
+    heads = np.arange(8 * part, 8 * part + 8)
+    rows = (heads[:, None] * nb + np.arange(nb)[None, :]).reshape(-1).astype(np.int32)
+    inp, plan, out = st["inp"], st["plan"], st["out"]
+    want = O.attend(inp.q, inp.k, inp.v, 32768, hq, 8, 128, plan.row_ptr, plan.col_idx, rows)
+    got = out.view(hq * nb, B, 128)[torch.as_tensor(rows, dtype=torch.long, device=out.device)]
+    got = got.float().cpu().numpy()
+    P.check_outputs(got, want, f"c2 heads {heads[0]}-{heads[-1]} attend")
+    for h in heads:
+        m = rows // nb == h
+        P.check_outputs(got[m], want[m], f"c2 head {h}")
+    P.record("c2", f"attention_heads_{heads[0]}_{heads[-1]}", P.attention_record(got, want, rows // nb))
 
 
 def test_select_is_deterministic():
