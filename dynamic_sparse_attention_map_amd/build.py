@@ -14,7 +14,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OUT_DIR = os.path.join(PKG, "_lib")
 LIB = os.path.join(OUT_DIR, "libcrisp.so")
-SOURCES = ["route.hip", "select.hip", "attend.hip", "crisp_api.cpp"]
+SOURCES = ["route.hip", "select.hip", "attend.hip", "crisp_api.cpp", "noalloc.hip"]
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -46,6 +46,9 @@ class crisp_strides(C.Structure):
                                          "v_token", "out_head", "out_token")]
 
 
+# crisp_prefill_noalloc's static scratch (CRISP_NOALLOC_SCRATCH_BYTES)
+NOALLOC_SCRATCH_BYTES = 64 << 20
+
 ROUTER_CSTRUCT, ROUTER_JSD = 0, 1
 VS_NOISE_MEAN, VS_NOISE_MEDIAN, VS_GAMMA = 0, 1, 2
 
@@ -85,12 +88,13 @@ def lib():
         L.crisp_attend_dense.argtypes = [P, P, P, i, i, i, i, i, P, sz, P, P]
         L.crisp_prefill.argtypes = [P, P, P, i, i, i, i, i, f, P, P, sz, P, P]
         L.crisp_prefill_batch.argtypes = [P, i, P, i, i, i, i, f, P, P, sz, P]
+        L.crisp_prefill_noalloc.argtypes = [P, P, P, i, i, i, i, i, f, P, P, P]
         L.crisp_set_stage_events.argtypes = [P, i]
         L.crisp_default_opts.argtypes = [P]
         L.crisp_default_opts.restype = None
         for name in ("crisp_workspace_size", "crisp_route", "crisp_select", "crisp_attend",
                      "crisp_attend_dense", "crisp_prefill", "crisp_prefill_batch",
-                     "crisp_set_stage_events"):
+                     "crisp_prefill_noalloc", "crisp_set_stage_events"):
             getattr(L, name).restype = i
         _lib = L
     return _lib
@@ -270,6 +274,16 @@ def crisp_prefill(q, k, v, alpha, ws, out, opts=None, block_size=128, stream=Non
     _check(lib().crisp_prefill(_ptr(q), _ptr(k), _ptr(v), n, hq, hkv, d, block_size, float(alpha),
                                _opts(opts), _ptr(ws), ws.numel(), _ptr(out), _stream(stream)),
            "crisp_prefill")
+
+
+def crisp_prefill_noalloc(q, k, v, alpha, out, opts=None, block_size=128, stream=None):
+    """crisp_prefill on the library's static per-device scratch (no
+    workspace argument; layers needing more than NOALLOC_SCRATCH_BYTES are
+    refused with CRISP_ERR_WORKSPACE).  Calls overlapping on one device race."""
+    n, hq, hkv, d = _shape(q, k, v, out)
+    _check(lib().crisp_prefill_noalloc(_ptr(q), _ptr(k), _ptr(v), n, hq, hkv, d, block_size,
+                                       float(alpha), _opts(opts), _ptr(out), _stream(stream)),
+           "crisp_prefill_noalloc")
 
 
 def crisp_prefill_batch(qs, ks, vs, outs, alpha, ws, opts=None, block_size=128, stream=None):

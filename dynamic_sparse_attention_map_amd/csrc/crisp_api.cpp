@@ -264,6 +264,27 @@ bool bad_strides(long long sh, long long st)
 
 }  // namespace
 
+namespace crisp {
+
+int validate_prefill(const void* q, const void* k, const void* v, int seq_len, int n_heads,
+                     int n_kv_heads, int head_dim, int block_size, float alpha,
+                     const crisp_opts* opts, const void* out, size_t* ws_need)
+{
+    Shape s;
+    int rc = check_shape(seq_len, n_heads, n_kv_heads, head_dim, block_size, &s);
+    if (rc) return rc;
+    Opts op;
+    if ((rc = check_opts(opts, &op))) return rc;
+    if (!std::isfinite(alpha) || alpha < 0.0f) return CRISP_ERR_INVALID_ARG;
+    *ws_need = 0;
+    if (s.n == 0) return CRISP_OK;
+    if (bad_ptr(q) || bad_ptr(k) || bad_ptr(v) || bad_ptr(out)) return CRISP_ERR_INVALID_ARG;
+    *ws_need = make_layout(s).total;
+    return CRISP_OK;
+}
+
+}  // namespace crisp
+
 extern "C" {
 
 void crisp_default_opts(crisp_opts* opts)
@@ -278,7 +299,7 @@ const char* crisp_status_string(int code)
     case CRISP_ERR_INVALID_ARG: return "invalid argument (null or misaligned pointer, or bad option)";
     case CRISP_ERR_SHAPE: return "bad shape (negative seq_len, n_heads % n_kv_heads != 0, or non-positive head count)";
     case CRISP_ERR_UNSUPPORTED: return "unsupported (head_dim, block_size and anchor windows must be 128; N_b <= 4096)";
-    case CRISP_ERR_WORKSPACE: return "workspace or CSR capacity too small";
+    case CRISP_ERR_WORKSPACE: return "workspace or CSR capacity too small (crisp_prefill_noalloc: the layer needs more than its CRISP_NOALLOC_SCRATCH_BYTES)";
     case CRISP_ERR_HIP: return "HIP launch error";
     default: return "unknown status";
     }

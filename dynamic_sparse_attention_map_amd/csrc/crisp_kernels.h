@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+struct crisp_opts;   // include/crisp.h
+
 namespace crisp {
 
 constexpr int kD = 128;            // head_dim
@@ -101,5 +103,12 @@ hipError_t launch_v_transpose(Rows v, int n, int hkv, uint16_t* vt, int* queue,
 hipError_t launch_attend(Rows q, Rows k, const uint16_t* vt,
                          const int32_t* row_ptr, const int32_t* col_idx, int n, int hq, int hkv,
                          int* counters, OutRows out, hipStream_t stream);
+
+// crisp_prefill's argument checks without a workspace: shape, options,
+// alpha and the q/k/v/out pointers.  On CRISP_OK, *ws_need is the workspace
+// the call needs (0 for an empty call, which then needs nothing else).
+int validate_prefill(const void* q, const void* k, const void* v, int seq_len, int n_heads,
+                     int n_kv_heads, int head_dim, int block_size, float alpha,
+                     const ::crisp_opts* opts, const void* out, size_t* ws_need);
 
 }  // namespace crisp

@@ -199,6 +199,30 @@ int crisp_prefill(const void *q, const void *k, const void *v, int seq_len, int 
                   int n_kv_heads, int head_dim, int block_size, float alpha,
                   const crisp_opts *opts, void *ws, size_t ws_bytes, void *out, void *stream);
 
+/*
+ * crisp_prefill without a caller workspace, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc.  The caller still passes q, k, v
+ * and out (as for crisp_prefill); the workspace is a static device array of
+ * CRISP_NOALLOC_SCRATCH_BYTES held by the library, one per device it runs
+ * on, for the life of the process.  The call uses the array of the device
+ * current on the calling thread (stream must belong to that device); its
+ * address is looked up on the first call on each device, after which no
+ * call allocates, frees or synchronises.
+ * Limit: a layer whose crisp_workspace_size exceeds the array returns
+ * CRISP_ERR_WORKSPACE before anything is launched.  The 64 MiB hold, e.g.,
+ * 32 query / 8 KV heads up to 30848 tokens, or 4 / 1 heads up to 191488.
+ * Every call on one device shares its array: the kernels clear what must
+ * start at zero, so results do not depend on earlier calls, but calls that
+ * overlap in time on one device (other streams, unordered threads) race.
+ * CRISP_ERR_HIP if the array's address cannot be obtained.
+ */
+#define CRISP_NOALLOC_SCRATCH_BYTES (64u << 20)
+
+int crisp_prefill_noalloc(const void *q, const void *k, const void *v, int seq_len, int n_heads,
+                          int n_kv_heads, int head_dim, int block_size, float alpha,
+                          const crisp_opts *opts, void *out, void *stream);
+
 /* One sequence of a batch: device pointers to token 0 of head 0 of its q, k,
  * v and out, and its length (>= 0; 0 skips the sequence). */
 typedef struct crisp_seq {

@@ -202,6 +202,34 @@ def test_batch_binding_rejects_mismatched_views():
                                   1.0, ws)
 
 
+def test_noalloc_validation_before_device(L):
+    """crisp_prefill_noalloc checks everything, including its scratch limit,
+    before the device is touched (this host has none)."""
+    N = L.crisp_prefill_noalloc
+    assert N(None, None, None, 0, 4, 1, 128, 128, 1.0, None, None, None) == OK
+    assert N(None, None, None, 0, 4, 3, 128, 128, 1.0, None, None, None) == SHAPE
+    assert N(FAKE, FAKE, FAKE, 256, 4, 1, 64, 128, 1.0, None, FAKE, None) == UNSUPPORTED
+    assert N(FAKE, FAKE, FAKE, 256, 4, 1, 128, 128, -1.0, None, FAKE, None) == INVALID
+    assert N(FAKE, FAKE, FAKE, 256, 4, 1, 128, 128, 1.0, _opts(gamma=0.0), FAKE, None) == INVALID
+    assert N(None, FAKE, FAKE, 256, 4, 1, 128, 128, 1.0, None, FAKE, None) == INVALID
+    assert N(FAKE, FAKE, FAKE, 256, 4, 1, 128, 128, 1.0, None, C.c_void_p((1 << 20) + 8),
+             None) == INVALID
+    # layers beyond the static scratch are refused with WORKSPACE
+    limit = crisp.NOALLOC_SCRATCH_BYTES
+    for n, hq, hkv in ((65536, 32, 8), (30848 + 128, 32, 8), (191488 + 128, 4, 1)):
+        assert ws_size(n, hq, hkv)[1] > limit
+        assert N(FAKE, FAKE, FAKE, n, hq, hkv, 128, 128, 1.0, None, FAKE, None) == WORKSPACE
+    # the largest layers the header names still fit
+    assert ws_size(30848, 32, 8)[1] <= limit and ws_size(191488, 4, 1)[1] <= limit
+
+
+def test_noalloc_limit_matches_header():
+    import re
+    text = open(crisp.HEADER).read()
+    m = re.search(r"#define CRISP_NOALLOC_SCRATCH_BYTES \((\d+)u << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == crisp.NOALLOC_SCRATCH_BYTES
+
+
 def test_binding_rejects_bad_tensors():
     """The binding's own checks: dtype, device, contiguity, matching shapes
     and index array sizes are refused before any call reaches the library."""
@@ -220,6 +248,6 @@ def test_binding_rejects_bad_tensors():
     with pytest.raises(ValueError, match="k's shape"):
         crisp.crisp_prefill(q, k, q, 1.0, ws, q)
     with pytest.raises(ValueError, match="q's shape"):
-        crisp.crisp_prefill(q, k, k, 1.0, ws, q[:2])
+        crisp.crisp_prefill_noalloc(q, k, k, 1.0, q[:2])
     with pytest.raises(TypeError):
         crisp.crisp_attend(q, k, [0, 1], None, None, ws, q)
