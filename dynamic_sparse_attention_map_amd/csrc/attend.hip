@@ -42,32 +42,6 @@ constexpr int kListWords = kMaxBlocks / 32;   // bitmap words per row
 constexpr int kPairRun = 256;
 constexpr int kWholeHeadPairs = 512;
 
-// 16 bytes per lane from global memory straight into LDS: lane l's bytes
-// land at lds_addr + 16 l (lds_addr wave-uniform).  Written as inline asm so
-// that the compiler, which cannot tell the ring's stages apart, does not put
-// a full vmcnt(0) before every LDS read; completion is awaited explicitly
-// (wait_copies) before the barrier that publishes a tile.  M0 is set here
-// and declared clobbered; the s_nop covers the M0 -> LDS-DMA hazard.
-// (M0 is otherwise unused by this code, so its clobber is harmless.)
-#pragma clang diagnostic push
-#pragma clang diagnostic ignored "-Winline-asm"
-__device__ __forceinline__ void copy16_to_lds(const void* gptr, uint32_t lds_addr)
-{
-    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
-                 :
-                 : "v"(gptr), "s"(__builtin_amdgcn_readfirstlane(lds_addr))
-                 : "memory", "m0");
-}
-#pragma clang diagnostic pop
-
-// s_waitcnt vmcnt(N) with the other counters left alone (gfx9 encoding)
-template <int N>
-__device__ __forceinline__ void wait_copies()
-{
-    static_assert(N >= 0 && N < 16, "vmcnt field");
-    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8));
-}
-
 // Work items.  Pair p is query blocks Nb-1-2p and Nb-2-2p.  A chunk is `run`
 // consecutive pairs of the G query heads of one KV head: chunk c covers KV
 // head c % hkv and pairs run * (c / hkv) onward, and holds its G x run items
@@ -108,6 +82,19 @@ attend_pair(int b, uint16_t* lds, uint32_t* list, Rows q, Rows k,
     const int l32 = lane & 31, hi = lane >> 5;
     const int myqb = half ? qb_lo : qb_hi;
     const bool active = myqb >= 0;
+
+    // this wavefront's queries, loaded first so that their latency overlaps
+    // the list build below (a partial last block has rows past the end:
+    // they load the last row and their results are never stored)
+    const int qc = 32 * wq + l32;                         // query within its block
+    const int qpos = (active ? myqb : 0) * kB + qc;
+    const bool q_valid = active && qpos < n;
+    bf16x8 qf[8];
+    {
+        const uint16_t* qrow = q.row(h, min(qpos, n - 1));
+        for (int s = 0; s < 8; ++s)
+            qf[s] = *reinterpret_cast<const bf16x8*>(qrow + 16 * s + 8 * hi);
+    }
 
     // ---- the merged key-block list of the two rows, built in LDS ----
     // bits[r][kb / 32] bit kb % 32: row r (0 = qb_hi, 1 = qb_lo) lists key
@@ -164,15 +151,6 @@ attend_pair(int b, uint16_t* lds, uint32_t* list, Rows q, Rows k,
     __syncthreads();
     const int n_entries = __builtin_amdgcn_readfirstlane((int)desc[kMaxBlocks]);
 
-    const int qc = 32 * wq + l32;                         // query within its block
-    // a partial last block has rows past the end: they load the last row
-    // (their results are never stored)
-    const int qpos = (active ? myqb : 0) * kB + qc;
-    const bool q_valid = active && qpos < n;
-    const uint16_t* qrow = q.row(h, min(qpos, n - 1));
-    bf16x8 qf[8];
-    for (int s = 0; s < 8; ++s)
-        qf[s] = *reinterpret_cast<const bf16x8*>(qrow + 16 * s + 8 * hi);
 
     f32x16 o[4];
     for (int dt = 0; dt < 4; ++dt) o[dt] = f32x16{};
@@ -191,31 +169,38 @@ attend_pair(int b, uint16_t* lds, uint32_t* list, Rows q, Rows k,
     //   V^T  [128 d][8 chunks]:     chunk c of row d at slot c ^ ((d >> 1) & 7)
     // K is swizzled by the per-lane source address; V^T is stored in HBM as
     // these images already (v_transpose_kernel), so its copy is contiguous.
-    int k_row[2], k_col[2];
-    long long k_src[2];
+    // Copies take a wave-uniform base (scalar registers) and a 32-bit byte
+    // offset per lane.  K: lane l of copy j holds key 4 (2w + j) + l / 16 of
+    // the sub-tile, chunk (l % 16) ^ (key & 15).
+    uint32_t k_off[2];
     for (int j = 0; j < 2; ++j) {
-        const int ci = 2 * w + j;                       // 1 KiB chunk of the image
-        k_row[j] = 4 * ci + (lane >> 4);
-        k_col[j] = 8 * ((lane & 15) ^ (k_row[j] & 15));
-        k_src[j] = k_row[j] * k.st + k_col[j];
+        const int row = 4 * (2 * w + j) + (lane >> 4);
+        k_off[j] = (uint32_t)(row * k.st + 8 * ((lane & 15) ^ (row & 15))) * 2u;
     }
-    const uint32_t lds_base = (uint32_t)(uintptr_t)(
-        (__attribute__((address_space(3))) uint16_t*)lds);
+    const uint32_t v_off = (uint32_t)(1024 * w + 8 * lane) * 2u;
+    const uint32_t lds_base = lds_address(lds);
     auto issue_tile = [&](int t, uint32_t dsc) {        // tile t into stage t % 4
         const int kb = (int)(dsc & 0xffffu), sub = t & 1;
         const int key0 = kb * kB + sub * kKT;
         const uint32_t sb = lds_base + (uint32_t)((t & 3) * kStageBytes) + 2048u * w;
-        const uint16_t* kt = kg + key0 * k.st;
         const bool full = key0 + kKT <= n;
+        // keys past the end of a partial last block repeat the last key
+        // (every query that exists masks them: they lie in its future); the
+        // base then sits at the sub-tile's first existing key, or at the last
+        // key when none exists, so every offset stays non-negative
+        const int kfirst = min(key0, n - 1);
+        const uint16_t* kt = kg + (long long)kfirst * k.st;
         for (int j = 0; j < 2; ++j) {
-            // keys past the end of a partial last block repeat the last key
-            // (every query that exists masks them: they lie in its future)
-            const uint16_t* src = full ? kt + k_src[j]
-                                       : kg + min(key0 + k_row[j], n - 1) * k.st + k_col[j];
-            copy16_to_lds(src, sb + 1024u * j);
+            uint32_t off = k_off[j];
+            if (!full) {
+                const int r = 4 * (2 * w + j) + (lane >> 4);
+                const int row = min(key0 + r, n - 1) - kfirst;
+                off = (uint32_t)(row * k.st + 8 * ((lane & 15) ^ (r & 15))) * 2u;
+            }
+            copy16_to_lds(kt, off, sb + 1024u * j);
         }
-        const uint16_t* vimg = vg + (size_t)(2 * kb + sub) * kImg + 1024 * w + 8 * lane;
-        for (int j = 0; j < 2; ++j) copy16_to_lds(vimg + 512 * j, sb + 2 * kImg + 1024u * j);
+        const uint16_t* vimg = vg + (size_t)(2 * kb + sub) * kImg;
+        for (int j = 0; j < 2; ++j) copy16_to_lds(vimg, v_off + 1024u * j, sb + 2 * kImg + 1024u * j);
     };
 
     // ---- tile stream: two 64-key sub-tiles per merged list entry ----
@@ -420,7 +405,7 @@ attend_kernel(Rows q, Rows k,
             s_item = item;
         }
         __syncthreads();
-        const int item = s_item;
+        const int item = __builtin_amdgcn_readfirstlane(s_item);
         __syncthreads();
         if (item < 0) break;
         attend_pair(item, lds, list, q, k, vt, row_ptr, col_idx, n, nb, hkv, G, run, scale_log2,

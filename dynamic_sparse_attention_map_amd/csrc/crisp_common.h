@@ -59,10 +59,65 @@ __device__ __forceinline__ double wave_sum(double x)
     return x;
 }
 
+// N independent wave sums with the butterfly of wave_sum (the same additions
+// in the same order, so the same bits), their shuffles interleaved so that
+// their latencies overlap.
+template <int N>
+__device__ __forceinline__ void wave_sum_n(double (&x)[N])
+{
+    for (int o = 32; o > 0; o >>= 1) {
+        double y[N];
+        for (int j = 0; j < N; ++j) y[j] = __shfl_xor(x[j], o);
+        for (int j = 0; j < N; ++j) x[j] += y[j];
+    }
+}
+
 __device__ __forceinline__ int wave_sum(int x)
 {
     for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
     return x;
+}
+
+// 16 bytes per lane from global memory straight into LDS: lane l's bytes
+// land at lds_addr + 16 l (lds_addr wave-uniform).  Written as inline asm so
+// that the compiler, which cannot tell a ring's stages apart, does not put a
+// full vmcnt(0) before every LDS read; completion is awaited explicitly
+// (wait_copies) before the barrier that publishes the data.  M0 is set here
+// and declared clobbered; the s_nop covers the M0 -> LDS-DMA hazard.  (M0 is
+// otherwise unused by the kernels that call this.)
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void copy16_to_lds(const void* gptr, uint32_t lds_addr)
+{
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+                 :
+                 : "v"(gptr), "s"(__builtin_amdgcn_readfirstlane(lds_addr))
+                 : "memory", "m0");
+}
+// The same with a wave-uniform 64-bit base (held in scalar registers) and a
+// per-lane 32-bit byte offset, which costs one vector register instead of two.
+__device__ __forceinline__ void copy16_to_lds(const void* sbase, uint32_t voff, uint32_t lds_addr)
+{
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+                 :
+                 : "v"(voff), "s"(sbase), "s"(__builtin_amdgcn_readfirstlane(lds_addr))
+                 : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+// s_waitcnt vmcnt(N) with the other counters left alone (gfx9 encoding)
+template <int N>
+__device__ __forceinline__ void wait_copies()
+{
+    static_assert(N >= 0 && N < 16, "vmcnt field");
+    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8));
+}
+
+// LDS byte address of a shared-memory pointer
+template <typename T>
+__device__ __forceinline__ uint32_t lds_address(T* p)
+{
+    return (uint32_t)(uintptr_t)((__attribute__((address_space(3))) T*)p);
 }
 
 }  // namespace crisp

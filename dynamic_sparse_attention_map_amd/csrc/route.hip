@@ -26,12 +26,19 @@ namespace crisp {
 namespace {
 
 constexpr int kTileKeys = 128;
-constexpr int kKRow = kD + 8;   // LDS row pitch of a K tile (bf16): 272 bytes
 
 // grid: (ceil(Nb / tiles_per_wg), n_kv_heads * ceil(G / 4)); block: 16
-// wavefronts sharing one staged K tile (double-buffered in LDS).  Wave w
-// handles proxy rows 32 (w % 4) .. +31 of query head kv*G + 4*sub + w / 4
-// (idle when that head is >= G; it still helps stage K).
+// wavefronts sharing one K tile, double-buffered in LDS.  Wave w handles proxy
+// rows 32 (w % 4) .. +31 of query head kv*G + 4*sub + w / 4 (idle when that
+// head is >= G; it still copies its share of K).
+// Each K tile (128 keys x 256 bytes) is copied from HBM straight into LDS
+// (two 1 KiB copies per wavefront), one tile ahead: the copies of tile t+1
+// are issued when tile t's products start and awaited at the barrier that
+// opens iteration t+1, so their latency hides behind a whole tile of work.
+// The 16-byte chunk c of key r sits at slot c ^ (r & 15) of the key's row, so
+// the fragment reads below are free of bank conflicts without padding.  The
+// per-(row, tile) partials of a tile are stored one iteration later, so that
+// the wait for the copies never waits on fresh stores.
 // Aligned (B divides n): row i sits at column i of the last tile, so the
 // split column and the causal cut are compile-time per (chunk, key group).
 template <bool Aligned>
@@ -41,7 +48,7 @@ proxy_map_kernel(Rows q, Rows k, int n, int nb,
                  float* __restrict__ part_m, float* __restrict__ part_lo,
                  float* __restrict__ part_up)
 {
-    __shared__ __attribute__((aligned(16))) uint16_t ks[2][kTileKeys * kKRow];
+    __shared__ __attribute__((aligned(1024))) uint16_t ks[2][kTileKeys * kD];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -57,6 +64,27 @@ proxy_map_kernel(Rows q, Rows k, int n, int nb,
     const int R = min(kB, n);                       // proxy rows
     const int q0 = n - R;                           // position of proxy row 0
 
+    const uint16_t* kg = k.row(kv, 0);
+    const int t0 = blockIdx.x * tiles_per_wg;
+    const int t1 = min(nb, t0 + tiles_per_wg);
+    // copy j of this wavefront fills LDS bytes 1024 (2w + j) .. +1023 of the
+    // tile: keys 4 (2w + j) .. +3, lane l at key 4 (2w + j) + l / 16, slot
+    // l % 16, which holds chunk (l % 16) ^ (key & 15).  Keys past the end of
+    // the sequence repeat the last key (masked below: they lie after every
+    // proxy row).
+    const uint32_t lds0 = lds_address(&ks[0][0]) + 2048u * w;
+    auto issue = [&](int t, int buf) {
+        const long long key0 = (long long)t * kTileKeys;
+        const uint16_t* base = kg + key0 * k.st;                 // wave-uniform
+        for (int j = 0; j < 2; ++j) {
+            const int r = 4 * (2 * w + j) + (lane >> 4);          // key in the tile
+            const int rr = (int)min((long long)r, (long long)n - 1 - key0);
+            const uint32_t off = (uint32_t)(rr * k.st + 8 * ((lane & 15) ^ (r & 15))) * 2u;
+            copy16_to_lds(base, off, lds0 + (uint32_t)buf * (kTileKeys * kD * 2) + 1024u * j);
+        }
+    };
+    if (t0 < t1) issue(t0, 0);
+
     // rows 32c .. 32c+31 of the representative block Q^ as MFMA B-operands,
     // step s holding d = 16s .. 16s+15 (rows past R, which exist only when
     // n < B, repeat the last row)
@@ -66,26 +94,27 @@ proxy_map_kernel(Rows q, Rows k, int n, int nb,
         for (int s = 0; s < 8; ++s) qf[s] = *reinterpret_cast<const bf16x8*>(qr + 16 * s + 8 * hi);
     }
 
-    const uint16_t* kg = k.row(kv, 0);
-    const int t0 = blockIdx.x * tiles_per_wg;
-    const int t1 = min(nb, t0 + tiles_per_wg);
-    // stage K tile t into buffer `buf`: 128 rows x 256 bytes as 2048 16-byte
-    // chunks, two per thread; rows past the end of the sequence are zero
-    // (and masked below)
-    auto stage = [&](int t, int buf) {
-        for (int e = tid; e < kTileKeys * (kD / 8); e += 1024) {
-            const int row = e >> 4, ch = e & 15;
-            const long long key = (long long)t * kTileKeys + row;
-            u32x4 val = {0u, 0u, 0u, 0u};
-            if (key < n) val = *reinterpret_cast<const u32x4*>(kg + key * k.st + 8 * ch);
-            *reinterpret_cast<u32x4*>(&ks[buf][row * kKRow + 8 * ch]) = val;
-        }
+    const int i = 32 * c + l32;
+    const int qi = q0 + i;
+    const int kx = l32 & 15;                        // this lane's key swizzle
+    // partials of the previous tile, stored one iteration late
+    bool pend = false;
+    float pms = 0.f, plo = 0.f, pup = 0.f;
+    auto store_prev = [&](int tp) {
+        const size_t o = ((size_t)h * nb + tp) * kB + i;
+        part_m[o] = pms;
+        part_lo[o] = plo;
+        part_up[o] = pup;
     };
-    if (t0 < t1) stage(t0, 0);
     for (int t = t0; t < t1; ++t) {
         const int buf = (t - t0) & 1;
-        __syncthreads();                            // tile t staged, buffer buf ^ 1 free
-        if (t + 1 < t1) stage(t + 1, buf ^ 1);
+        wait_copies<0>();
+        __syncthreads();                            // tile t landed, buffer buf ^ 1 free
+        if (t + 1 < t1) issue(t + 1, buf ^ 1);
+        if (pend) {
+            store_prev(t - 1);
+            pend = false;
+        }
         if (!active) continue;
 
         // S^T of this wave's rows against key group (a + c) % 4 of the tile
@@ -93,10 +122,11 @@ proxy_map_kernel(Rows q, Rows k, int n, int nb,
         // wave's own rows' columns
         f32x16 acc[4];
         for (int a = 0; a < 4; ++a) acc[a] = f32x16{};
+        const uint16_t* kb = &ks[buf][l32 * kD];
         for (int s = 0; s < 8; ++s)
             for (int a = 0; a < 4; ++a) {
                 const int g = (a + c) & 3;
-                const bf16x8 kf = *reinterpret_cast<const bf16x8*>(&ks[buf][(32 * g + l32) * kKRow + 16 * s + 8 * hi]);
+                const bf16x8 kf = *reinterpret_cast<const bf16x8*>(kb + 32 * g * kD + 8 * ((2 * s + hi) ^ kx));
                 acc[a] = mfma32(kf, qf[s], acc[a]);
             }
 
@@ -106,8 +136,6 @@ proxy_map_kernel(Rows q, Rows k, int n, int nb,
         // (g = c) needs a per-element test at offset l32, and acc[a], a > 0,
         // lies wholly after column i when a + c < 4 (g > c) and wholly
         // before it otherwise.
-        const int i = 32 * c + l32;
-        const int qi = q0 + i;
         float m;
         if (Aligned) {
             if (t == nb - 1) {                                // causal cut
@@ -149,11 +177,12 @@ proxy_map_kernel(Rows q, Rows k, int n, int nb,
                 else up += e;
             }
             for (int a = 1; a < 4; ++a) {
-                float e[16];
+                // exponentials in place (the accumulator is dead after this)
                 for (int r = 0; r < 16; ++r)
-                    e[r] = __builtin_amdgcn_exp2f(fmaf(acc[a][r], scale_log2, nref));
+                    acc[a][r] = __builtin_amdgcn_exp2f(fmaf(acc[a][r], scale_log2, nref));
                 float s4[4];
-                for (int j = 0; j < 4; ++j) s4[j] = (e[j] + e[4 + j]) + (e[8 + j] + e[12 + j]);
+                for (int j = 0; j < 4; ++j)
+                    s4[j] = (acc[a][j] + acc[a][4 + j]) + (acc[a][8 + j] + acc[a][12 + j]);
                 const float sa = (s4[0] + s4[1]) + (s4[2] + s4[3]);
                 if (a + c < 4) up += sa;
                 else lo += sa;
@@ -170,12 +199,13 @@ proxy_map_kernel(Rows q, Rows k, int n, int nb,
         lo += swap_half(lo);
         up += swap_half(up);
         if (hi == 0 && i < R) {
-            const size_t o = ((size_t)h * nb + t) * kB + i;
-            part_m[o] = ms;
-            part_lo[o] = lo;
-            part_up[o] = up;
+            pend = true;
+            pms = ms;
+            plo = lo;
+            pup = up;
         }
     }
+    if (pend) store_prev(t1 - 1);
 }
 
 // The block-mass reduction runs in four small kernels so that it spreads over
@@ -282,18 +312,15 @@ tile_mass_kernel(const float* __restrict__ part_m, const float* __restrict__ par
         if (ei == 0) { slo0 += lo; sup0 += up; }
         else { slo1 += lo; sup1 += up; }
     }
-    sv = wave_sum(sv);
-    slo0 = wave_sum(slo0);
-    sup0 = wave_sum(sup0);
-    slo1 = wave_sum(slo1);
-    sup1 = wave_sum(sup1);
+    double r5[5] = {sv, slo0, sup0, slo1, sup1};
+    wave_sum_n(r5);
     if (lane == 0) {
-        p_v[(size_t)h * nb + t] = (float)(sv / R);
+        p_v[(size_t)h * nb + t] = (float)(r5[0] / R);
         float* ts = tile_sums + (size_t)h * 4 * nb;
-        ts[t] = (float)(slo0 / R);
-        ts[nb + t] = (float)(sup0 / R);
-        ts[2 * nb + t] = (float)(slo1 / R);
-        ts[3 * nb + t] = (float)(sup1 / R);
+        ts[t] = (float)(r5[1] / R);
+        ts[nb + t] = (float)(r5[2] / R);
+        ts[2 * nb + t] = (float)(r5[3] / R);
+        ts[3 * nb + t] = (float)(r5[4] / R);
     }
 }
 
@@ -416,9 +443,9 @@ route_small_kernel(const float* __restrict__ part_m, const float* __restrict__ p
                     vup[b][x] = part_up[o];
                 }
             }
+        // the five sums of each of the four tiles, reduced together
+        double r[20];
         for (int b = 0; b < 4; ++b) {
-            const int t = t4 + 16 * b;
-            if (t >= nb) break;
             double sv = 0.0, slo0 = 0.0, sup0 = 0.0, slo1 = 0.0, sup1 = 0.0;
             for (int x = 0; x < 2; ++x) {
                 const int i = lane + 64 * x;
@@ -431,19 +458,24 @@ route_small_kernel(const float* __restrict__ part_m, const float* __restrict__ p
                 if (ei == 0) { slo0 += lo; sup0 += up; }
                 else { slo1 += lo; sup1 += up; }
             }
-            sv = wave_sum(sv);
-            slo0 = wave_sum(slo0);
-            sup0 = wave_sum(sup0);
-            slo1 = wave_sum(slo1);
-            sup1 = wave_sum(sup1);
+            r[5 * b] = sv;
+            r[5 * b + 1] = slo0;
+            r[5 * b + 2] = sup0;
+            r[5 * b + 3] = slo1;
+            r[5 * b + 4] = sup1;
+        }
+        wave_sum_n(r);
+        for (int b = 0; b < 4; ++b) {
+            const int t = t4 + 16 * b;
+            if (t >= nb) break;
             if (lane == 0) {
-                const float v = (float)(sv / R);
+                const float v = (float)(r[5 * b] / R);
                 p_v[(size_t)h * nb + t] = v;
                 pv_l[t] = v;
-                ts[t] = (float)(slo0 / R);
-                ts[nb + t] = (float)(sup0 / R);
-                ts[2 * nb + t] = (float)(slo1 / R);
-                ts[3 * nb + t] = (float)(sup1 / R);
+                ts[t] = (float)(r[5 * b + 1] / R);
+                ts[nb + t] = (float)(r[5 * b + 2] / R);
+                ts[2 * nb + t] = (float)(r[5 * b + 3] / R);
+                ts[3 * nb + t] = (float)(r[5 * b + 4] / R);
             }
         }
     }
