@@ -170,6 +170,57 @@ def crossover(args):
                       "first_n_sparse_faster": faster[0] if faster else None}), flush=True)
 
 
+def batch_bench(args):
+    """Many short sequences: crisp_prefill_batch with a workspace for one
+    attention launch over the whole batch ("fused") against the same call
+    sequence by sequence ("serial") and against separate crisp_prefill calls,
+    on the headline head mix.  Prints one JSON line."""
+    import torch
+    from dynamic_sparse_attention_map_amd import crisp, synth
+
+    count, n = args.batch
+    spec0 = synth.config_spec(WORKLOAD, n=n)
+    hq, hkv = spec0.hq, spec0.hkv
+    log(f"batch of {count} x {n} tokens, {hq}/{hkv} heads")
+    qs, ks, vs = [], [], []
+    for i in range(count):
+        sp = synth.custom_spec(n, hq, hkv, [hp.kind for hp in spec0.heads], seed_id=900 + i)
+        inp = synth.generate(sp, threads=16)
+        qs.append(inp.q.cuda())
+        ks.append(inp.k.cuda())
+        vs.append(inp.v.cuda())
+    outs = [torch.empty_like(x) for x in qs]
+    ws_f = crisp.alloc_batch_workspace([n] * count, hq, hkv)
+    ws_s = crisp.alloc_workspace(n, hq, hkv)
+
+    def timed(fn, reps):
+        for _ in range(2):
+            fn()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    reps = max(3, args.steps // 4)
+    fused = timed(lambda: crisp.crisp_prefill_batch(qs, ks, vs, outs, args.alpha, ws_f), reps)
+    serial = timed(lambda: crisp.crisp_prefill_batch(qs, ks, vs, outs, args.alpha, ws_s), reps)
+
+    def singles():
+        for q, k, v, o in zip(qs, ks, vs, outs):
+            crisp.crisp_prefill(q, k, v, args.alpha, ws_s, o)
+    single = timed(singles, reps)
+    log(f"batch fused {fused:.3f} ms, serial {serial:.3f} ms, separate calls {single:.3f} ms")
+    print(json.dumps({"metric": "varlen_batch_prefill_ms", "sequences": count, "seq_len": n,
+                      "n_heads": hq, "n_kv_heads": hkv, "fused_ms": round(fused, 3),
+                      "serial_ms": round(serial, 3), "separate_calls_ms": round(single, 3),
+                      "fused_speedup_vs_separate": round(single / fused, 3)}), flush=True)
+
+
 def gemm_ceiling():
     """The practical bf16 matrix-core rate of this part, for scale: the
     vendor library's GEMM (torch.matmul on rocBLAS / hipBLASLt) on random and
@@ -228,6 +279,9 @@ def main():
                     help="only time the vendor bf16 GEMM (the practical matrix-core rate)")
     ap.add_argument("--crossover", action="store_true",
                     help="only sweep n for the sparse/dense crossover and print it")
+    ap.add_argument("--batch", type=int, nargs=2, metavar=("COUNT", "SEQ_LEN"), default=None,
+                    help="only time a batch of COUNT sequences of SEQ_LEN tokens (one attention "
+                         "launch for the batch against sequence by sequence)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: every step is per query head and runs on a single "
@@ -242,6 +296,9 @@ def main():
     crisp.lib()
     if args.crossover:
         crossover(args)
+        return
+    if args.batch:
+        batch_bench(args)
         return
     if args.gemm_ceiling:
         gemm_ceiling()

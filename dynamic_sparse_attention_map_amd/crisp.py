@@ -82,6 +82,7 @@ def lib():
         L.crisp_status_string.argtypes = [i]
         L.crisp_status_string.restype = C.c_char_p
         L.crisp_workspace_size.argtypes = [i, i, i, i, i, C.POINTER(sz), C.POINTER(i64)]
+        L.crisp_workspace_size_batch.argtypes = [P, i, i, i, i, i, C.POINTER(sz)]
         L.crisp_route.argtypes = [P, P, i, i, i, i, i, P, P, sz, P, P, P, P, P]
         L.crisp_select.argtypes = [P, P, P, P, P, i, i, i, i, i, f, P, P, sz, P, P, P, P, P, i64, P]
         L.crisp_attend.argtypes = [P, P, P, P, P, i, i, i, i, i, P, sz, P, P]
@@ -92,7 +93,7 @@ def lib():
         L.crisp_set_stage_events.argtypes = [P, i]
         L.crisp_default_opts.argtypes = [P]
         L.crisp_default_opts.restype = None
-        for name in ("crisp_workspace_size", "crisp_route", "crisp_select", "crisp_attend",
+        for name in ("crisp_workspace_size", "crisp_workspace_size_batch", "crisp_route", "crisp_select", "crisp_attend",
                      "crisp_attend_dense", "crisp_prefill", "crisp_prefill_batch",
                      "crisp_prefill_noalloc", "crisp_set_stage_events"):
             getattr(L, name).restype = i
@@ -196,6 +197,22 @@ def crisp_workspace_size(seq_len, n_heads, n_kv_heads, head_dim=128, block_size=
     _check(lib().crisp_workspace_size(seq_len, n_heads, n_kv_heads, head_dim, block_size,
                                       C.byref(ws), C.byref(cap)), "crisp_workspace_size")
     return int(ws.value), int(cap.value)
+
+
+def crisp_workspace_size_batch(seq_lens, n_heads, n_kv_heads, head_dim=128, block_size=128):
+    """Workspace with which crisp_prefill_batch attends the whole batch in one launch."""
+    lens = (C.c_int * max(len(seq_lens), 1))(*[int(x) for x in seq_lens])
+    ws = C.c_size_t(0)
+    _check(lib().crisp_workspace_size_batch(lens, len(seq_lens), n_heads, n_kv_heads, head_dim,
+                                            block_size, C.byref(ws)), "crisp_workspace_size_batch")
+    return int(ws.value)
+
+
+def alloc_batch_workspace(seq_lens, n_heads, n_kv_heads, device="cuda"):
+    """A caller-owned workspace for the single-launch batch path."""
+    import torch
+    return torch.empty(crisp_workspace_size_batch(seq_lens, n_heads, n_kv_heads), dtype=torch.uint8,
+                       device=device)
 
 
 def alloc_workspace(seq_len, n_heads, n_kv_heads, device="cuda"):

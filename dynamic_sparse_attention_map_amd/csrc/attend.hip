@@ -413,6 +413,61 @@ attend_kernel(Rows q, Rows k,
     }
 }
 
+// The same for several sequences in one launch: queue slot j (every queue
+// has the same layout) belongs to sequence slot_seq[j], whose items occupy
+// slots slot0 .. slot0 + per_xcd - 1; within it the item is decoded exactly
+// as in a launch of that sequence alone, so each sequence's output is the
+// same bits.
+__global__ void __launch_bounds__(kThreads)
+attend_batch_kernel(const SeqDesc* __restrict__ seqs, const int* __restrict__ slot_seq, int hkv,
+                    int G, float scale_log2, int per_xcd, int* __restrict__ ctr)
+{
+    __shared__ __attribute__((aligned(1024))) uint16_t lds[kStages * kStageBytes / 2];
+    __shared__ uint32_t list[2 * kListWords + kMaxBlocks + 1];
+    __shared__ int s_item;
+    const int home = blockIdx.x & 7;
+    int next_q = 0;   // queues home+0 .. home+7 in turn; only thread 0 uses it
+    for (;;) {
+        if (threadIdx.x == 0) {
+            int item = -1;
+            while (next_q < 8) {
+                const int x = (home + next_q) & 7;
+                const int j = atomicAdd(&ctr[x], 1);
+                if (j < per_xcd) { item = 8 * j + x; break; }
+                ++next_q;
+            }
+            s_item = item;
+        }
+        __syncthreads();
+        const int item = __builtin_amdgcn_readfirstlane(s_item);
+        __syncthreads();
+        if (item < 0) break;
+        const int j = item >> 3;
+        const SeqDesc& d = seqs[__builtin_amdgcn_readfirstlane(slot_seq[j])];
+        const int n = d.n;
+        attend_pair(8 * (j - d.slot0) + (item & 7), lds, list, Rows{d.q, d.q_sh, d.q_st},
+                    Rows{d.k, d.k_sh, d.k_st}, d.vt, d.row_ptr, d.col_idx, n, (n + kB - 1) / kB, hkv,
+                    G, d.run, scale_log2, OutRows{d.out, d.o_sh, d.o_st});
+    }
+}
+
+// Up to 16 descriptors per launch, passed by value.
+struct SeqChunk {
+    SeqDesc d[16];
+    int first, count;
+};
+
+// grid (ceil(max per_xcd / 256), count), 256 threads
+__global__ void __launch_bounds__(256)
+seq_table_kernel(SeqChunk c, SeqDesc* __restrict__ table, int* __restrict__ slot_seq)
+{
+    const int i = blockIdx.y;
+    const SeqDesc& d = c.d[i];
+    if (blockIdx.x == 0 && threadIdx.x == 0) table[c.first + i] = d;
+    const int j = blockIdx.x * 256 + threadIdx.x;
+    if (j < d.per_xcd) slot_seq[d.slot0 + j] = c.first + i;
+}
+
 // V^T as LDS-ready images, one per 64-key sub-tile: image i of KV head g
 // (keys 64 i .. 64 i + 63) holds row d (the 64 keys' values
 // of head dimension d) as 8 chunks of 8 keys, chunk c at slot c ^ ((d >> 1) & 7), and inside
@@ -462,9 +517,7 @@ hipError_t launch_v_transpose(Rows v, int n, int hkv, uint16_t* vt, int* queue,
     return hipGetLastError();
 }
 
-hipError_t launch_attend(Rows q, Rows k, const uint16_t* vt,
-                         const int32_t* row_ptr, const int32_t* col_idx, int n, int hq, int hkv,
-                         int* counters, OutRows out, hipStream_t stream)
+void attend_plan(int n, int hq, int hkv, int* run_out, int* per_xcd_out)
 {
     const int nb = (n + kB - 1) / kB, G = hq / hkv;
     const int npairs = (nb + 1) / 2;
@@ -473,14 +526,59 @@ hipError_t launch_attend(Rows q, Rows k, const uint16_t* vt,
     if (run < 1) run = 1;
     const long long chunks = (long long)((npairs + run - 1) / run) * hkv;
     const long long items = ((chunks + 7) / 8) * 8 * G * run;
-    const int per_xcd = (int)(items / 8);
+    *run_out = run;
+    *per_xcd_out = (int)(items / 8);
+}
+
+namespace {
+int resident_groups()
+{
     int dev = 0, cus = 256;
     if (hipGetDevice(&dev) == hipSuccess)
         (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-    const int groups = cus;   // one resident work-group of 8 wavefronts per CU
+    return cus;   // one resident work-group of 8 wavefronts per CU
+}
+}  // namespace
+
+hipError_t launch_attend(Rows q, Rows k, const uint16_t* vt,
+                         const int32_t* row_ptr, const int32_t* col_idx, int n, int hq, int hkv,
+                         int* counters, OutRows out, hipStream_t stream)
+{
+    const int nb = (n + kB - 1) / kB, G = hq / hkv;
+    int run, per_xcd;
+    attend_plan(n, hq, hkv, &run, &per_xcd);
     const float scale_log2 = kLog2e / sqrtf((float)kD);
-    hipLaunchKernelGGL(attend_kernel, dim3(groups), dim3(kThreads), 0, stream, q, k, vt, row_ptr, col_idx,
-                       n, nb, hkv, G, run, scale_log2, per_xcd, counters, out);
+    hipLaunchKernelGGL(attend_kernel, dim3(resident_groups()), dim3(kThreads), 0, stream, q, k, vt,
+                       row_ptr, col_idx, n, nb, hkv, G, run, scale_log2, per_xcd, counters, out);
+    return hipGetLastError();
+}
+
+hipError_t launch_seq_table(const SeqDesc* descs, int first, int count, SeqDesc* table,
+                            int* slot_seq, hipStream_t stream)
+{
+    for (int at = 0; at < count; at += 16) {
+        SeqChunk c{};
+        c.first = first + at;
+        c.count = count - at < 16 ? count - at : 16;
+        int most = 1;
+        for (int i = 0; i < c.count; ++i) {
+            c.d[i] = descs[at + i];
+            if (c.d[i].per_xcd > most) most = c.d[i].per_xcd;
+        }
+        hipLaunchKernelGGL(seq_table_kernel, dim3((most + 255) / 256, c.count), dim3(256), 0, stream,
+                           c, table, slot_seq);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
+hipError_t launch_attend_batch(const SeqDesc* table, const int* slot_seq, int total_per_xcd,
+                               int hq, int hkv, int* counters, hipStream_t stream)
+{
+    const float scale_log2 = kLog2e / sqrtf((float)kD);
+    hipLaunchKernelGGL(attend_batch_kernel, dim3(resident_groups()), dim3(kThreads), 0, stream, table,
+                       slot_seq, hkv, hq / hkv, scale_log2, total_per_xcd, counters);
     return hipGetLastError();
 }
 

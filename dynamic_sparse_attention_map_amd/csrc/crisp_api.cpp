@@ -5,6 +5,7 @@
 #include <cmath>
 #include <cstdint>
 #include <cstring>
+#include <vector>
 
 #include "crisp.h"
 #include "crisp_kernels.h"
@@ -262,6 +263,151 @@ bool bad_strides(long long sh, long long st)
     return sh <= 0 || st <= 0 || sh % 8 != 0 || st % 8 != 0;
 }
 
+// Workspace of crisp_prefill_batch's single-launch path: the shared scratch
+// region S at offset 0 (routing and selection, one sequence at a time), then
+// per sequence its crisp_prefill intermediates (region P of its own layout)
+// and its V^T images, then the sequence table, the queue-slot map and the
+// queue counters.
+struct BatchLayout {
+    std::vector<size_t> p_base, vt_base;
+    std::vector<int> run, per_xcd, slot0;
+    size_t table = 0, slot_seq = 0, counters = 0, total = 0;
+    int total_per_xcd = 0;
+};
+
+// seq_len of entry b (validated shapes)
+template <typename LenOf>
+BatchLayout make_batch_layout(int batch, LenOf len_of, int hq, int hkv)
+{
+    BatchLayout B;
+    size_t S = 0;
+    for (int b = 0; b < batch; ++b) {
+        const int n = len_of(b);
+        if (n == 0) continue;
+        Shape s;
+        (void)check_shape(n, hq, hkv, kD, kB, &s);
+        const Layout L = make_layout(s);
+        S = std::max(S, std::max(L.route_end, L.select_end));
+    }
+    size_t o = align_up(S);
+    auto take = [&](size_t bytes) {
+        const size_t at = o;
+        o = align_up(o + bytes);
+        return at;
+    };
+    B.p_base.assign(batch, 0);
+    B.vt_base.assign(batch, 0);
+    B.run.assign(batch, 0);
+    B.per_xcd.assign(batch, 0);
+    B.slot0.assign(batch, 0);
+    for (int b = 0; b < batch; ++b) {
+        const int n = len_of(b);
+        if (n == 0) continue;
+        Shape s;
+        (void)check_shape(n, hq, hkv, kD, kB, &s);
+        const Layout L = make_layout(s);
+        B.p_base[b] = take(L.total - L.pattern);
+        B.vt_base[b] = take((size_t)hkv * kD * s.nb * kB * sizeof(uint16_t));
+        attend_plan(n, hq, hkv, &B.run[b], &B.per_xcd[b]);
+        B.slot0[b] = B.total_per_xcd;
+        B.total_per_xcd += B.per_xcd[b];
+    }
+    B.table = take((size_t)batch * sizeof(SeqDesc));
+    B.slot_seq = take((size_t)B.total_per_xcd * sizeof(int));
+    B.counters = take(8 * sizeof(int));
+    B.total = o;
+    return B;
+}
+
+// Alg. 1 over every sequence of a batch with one attention launch: route all
+// (stage 0 -> 1), select all (1 -> 2), lay out V and build the sequence
+// table (2 -> 3), attend (3 -> 4).  Sequences below the gating length keep
+// dense lists.
+int run_prefill_batch_fused(const crisp_seq* seqs, int batch, const crisp_strides* strides,
+                            int hq, int hkv, const Opts& op, float alpha, void* ws,
+                            const BatchLayout& B, hipStream_t st)
+{
+    std::vector<SeqDesc> descs;
+    std::vector<Operands> xs(batch);
+    std::vector<Shape> shapes(batch);
+    std::vector<Layout> lays(batch);
+    for (int b = 0; b < batch; ++b) {
+        (void)check_shape(seqs[b].seq_len, hq, hkv, kD, kB, &shapes[b]);
+        if (shapes[b].n == 0) continue;
+        lays[b] = make_layout(shapes[b]);
+        if (strides) {
+            xs[b].q = Rows{static_cast<const uint16_t*>(seqs[b].q), strides->q_head, strides->q_token};
+            xs[b].k = Rows{static_cast<const uint16_t*>(seqs[b].k), strides->k_head, strides->k_token};
+            xs[b].v = Rows{static_cast<const uint16_t*>(seqs[b].v), strides->v_head, strides->v_token};
+            xs[b].out = OutRows{static_cast<uint16_t*>(seqs[b].out), strides->out_head, strides->out_token};
+        } else {
+            const int n = shapes[b].n;
+            xs[b] = Operands{packed(seqs[b].q, n), packed(seqs[b].k, n), packed(seqs[b].v, n),
+                             packed_out(seqs[b].out, n)};
+        }
+    }
+    // P-region pointer of sequence b for a field at layout offset `off`
+    auto pp = [&](int b, size_t off) { return B.p_base[b] + (off - lays[b].pattern); };
+    auto sparse = [&](int b) { return shapes[b].n > 0 && shapes[b].n >= op.dense_below; };
+    int rc;
+    mark(0, st);
+    for (int b = 0; b < batch; ++b) {
+        if (!sparse(b)) continue;
+        const Layout& L = lays[b];
+        if ((rc = do_route(shapes[b], op, xs[b].q, xs[b].k, ws, L, at<uint8_t>(ws, pp(b, L.pattern)),
+                           at<float>(ws, pp(b, L.c_struct)), at<float>(ws, pp(b, L.p_v)),
+                           at<float>(ws, pp(b, L.p_s)), st)))
+            return rc;
+    }
+    mark(1, st);
+    for (int b = 0; b < batch; ++b) {
+        if (!sparse(b)) continue;
+        const Layout& L = lays[b];
+        if ((rc = do_select(shapes[b], op, alpha, xs[b].q, xs[b].k, at<uint8_t>(ws, pp(b, L.pattern)),
+                            at<float>(ws, pp(b, L.p_v)), at<float>(ws, pp(b, L.p_s)), ws, L,
+                            at<int32_t>(ws, pp(b, L.sel_v)), at<int32_t>(ws, pp(b, L.sel_s)),
+                            at<int32_t>(ws, pp(b, L.counts)), at<int32_t>(ws, pp(b, L.row_ptr)),
+                            at<int32_t>(ws, pp(b, L.col_idx)), st)))
+            return rc;
+    }
+    mark(2, st);
+    int* counters = at<int>(ws, B.counters);
+    for (int b = 0; b < batch; ++b) {
+        if (shapes[b].n == 0) continue;
+        uint16_t* vt = at<uint16_t>(ws, B.vt_base[b]);
+        if (launch_v_transpose(xs[b].v, shapes[b].n, hkv, vt, counters, st) != hipSuccess)
+            return CRISP_ERR_HIP;
+        SeqDesc d{};
+        d.q = xs[b].q.p;
+        d.k = xs[b].k.p;
+        d.out = xs[b].out.p;
+        d.vt = vt;
+        const bool sp = sparse(b);
+        d.row_ptr = sp ? at<int32_t>(ws, pp(b, lays[b].row_ptr)) : nullptr;
+        d.col_idx = sp ? at<int32_t>(ws, pp(b, lays[b].col_idx)) : nullptr;
+        d.q_sh = xs[b].q.sh;
+        d.q_st = xs[b].q.st;
+        d.k_sh = xs[b].k.sh;
+        d.k_st = xs[b].k.st;
+        d.o_sh = xs[b].out.sh;
+        d.o_st = xs[b].out.st;
+        d.n = shapes[b].n;
+        d.run = B.run[b];
+        d.slot0 = B.slot0[b];
+        d.per_xcd = B.per_xcd[b];
+        descs.push_back(d);
+    }
+    if (descs.empty()) return CRISP_OK;
+    SeqDesc* table = at<SeqDesc>(ws, B.table);
+    int* slot_seq = at<int>(ws, B.slot_seq);
+    if (launch_seq_table(descs.data(), 0, (int)descs.size(), table, slot_seq, st) != hipSuccess)
+        return CRISP_ERR_HIP;
+    mark(3, st);
+    const hipError_t e = launch_attend_batch(table, slot_seq, B.total_per_xcd, hq, hkv, counters, st);
+    mark(4, st);
+    return hip_status(e);
+}
+
 }  // namespace
 
 namespace crisp {
@@ -315,6 +461,25 @@ int crisp_workspace_size(int seq_len, int n_heads, int n_kv_heads, int head_dim,
     const Layout L = make_layout(s);
     *ws_bytes = L.total;
     *csr_capacity = L.csr_capacity;
+    return CRISP_OK;
+}
+
+int crisp_workspace_size_batch(const int* seq_lens, int batch, int n_heads, int n_kv_heads,
+                               int head_dim, int block_size, size_t* ws_bytes)
+{
+    if (batch < 0 || (batch > 0 && seq_lens == nullptr) || ws_bytes == nullptr)
+        return CRISP_ERR_INVALID_ARG;
+    for (int b = 0; b < batch; ++b) {
+        Shape s;
+        const int rc = check_shape(seq_lens[b], n_heads, n_kv_heads, head_dim, block_size, &s);
+        if (rc) return rc;
+    }
+    if (batch == 0) {
+        Shape s;
+        const int rc = check_shape(0, n_heads, n_kv_heads, head_dim, block_size, &s);
+        if (rc) return rc;
+    }
+    *ws_bytes = make_batch_layout(batch, [&](int b) { return seq_lens[b]; }, n_heads, n_kv_heads).total;
     return CRISP_OK;
 }
 
@@ -460,6 +625,13 @@ int crisp_prefill_batch(const crisp_seq* seqs, int batch, const crisp_strides* s
         if (ws_bytes < make_layout(s).total) return CRISP_ERR_WORKSPACE;
     }
     const hipStream_t st = static_cast<hipStream_t>(stream);
+    if (batch > 0) {
+        const BatchLayout BL = make_batch_layout(
+            batch, [&](int b) { return seqs[b].seq_len; }, n_heads, n_kv_heads);
+        if (BL.total_per_xcd > 0 && ws_bytes >= BL.total)
+            return run_prefill_batch_fused(seqs, batch, strides, n_heads, n_kv_heads, op, alpha, ws,
+                                           BL, st);
+    }
     for (int b = 0; b < batch; ++b) {
         Shape s;
         (void)check_shape(seqs[b].seq_len, n_heads, n_kv_heads, head_dim, block_size, &s);

@@ -104,6 +104,37 @@ hipError_t launch_attend(Rows q, Rows k, const uint16_t* vt,
                          const int32_t* row_ptr, const int32_t* col_idx, int n, int hq, int hkv,
                          int* counters, OutRows out, hipStream_t stream);
 
+// One sequence of a batched attention launch (an entry of a device table):
+// its operands with their strides, its V^T images and block lists, and its
+// share of the eight per-XCD work queues (slots slot0 .. slot0 + per_xcd - 1
+// of every queue).  row_ptr == nullptr: dense causal lists.
+struct SeqDesc {
+    const uint16_t* q;
+    const uint16_t* k;
+    uint16_t* out;
+    const uint16_t* vt;
+    const int32_t* row_ptr;
+    const int32_t* col_idx;
+    long long q_sh, q_st, k_sh, k_st, o_sh, o_st;
+    int n, run, slot0, per_xcd;
+};
+
+// Work-queue plan of one sequence's attention: pair-run length and slots per
+// XCD queue.
+void attend_plan(int n, int hq, int hkv, int* run, int* per_xcd);
+
+// Copies `count` host descriptors into the device table at table[first ..]
+// and marks their queue slots in slot_seq (kernel arguments only: no host
+// copy), in launches of up to 16 descriptors.
+hipError_t launch_seq_table(const SeqDesc* descs, int first, int count, SeqDesc* table,
+                            int* slot_seq, hipStream_t stream);
+
+// Attention of every sequence in `table` in one launch; total_per_xcd is the
+// sum of their per_xcd, slot_seq maps a queue slot to its sequence and
+// counters are 8 ints at zero (launch_v_transpose clears them).
+hipError_t launch_attend_batch(const SeqDesc* table, const int* slot_seq, int total_per_xcd,
+                               int hq, int hkv, int* counters, hipStream_t stream);
+
 // crisp_prefill's argument checks without a workspace: shape, options,
 // alpha and the q/k/v/out pointers.  On CRISP_OK, *ws_need is the workspace
 // the call needs (0 for an empty call, which then needs nothing else).

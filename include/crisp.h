@@ -252,15 +252,33 @@ typedef struct crisp_strides {
 /*
  * crisp_prefill over `batch` independent sequences of any lengths (variable-
  * length batches), each routed, selected and attended on its own as in
- * Alg. 1, one after another on `stream`, reusing one workspace.
+ * Alg. 1, on `stream`.
  *   seqs      host array [batch] (may be NULL when batch == 0)
  *   strides   host pointer; NULL means each sequence is contiguous
  *             [heads][seq_len][head_dim] as in crisp_prefill
- *   ws_bytes  at least crisp_workspace_size of the longest sequence
- * All sequences are validated before the first launch; an error leaves
- * every output untouched.  Sequences with seq_len < dense_below_tokens run
- * dense attention.  The stage events, when set, time the last sequence.
+ *   ws_bytes  at least crisp_workspace_size of the longest sequence: the
+ *             sequences then run one after another, reusing the workspace
+ *             (the stage events, when set, time the last sequence);
+ *             at least crisp_workspace_size_batch of the batch: every
+ *             sequence is routed and selected into a region of its own and
+ *             the attention of the whole batch runs in one launch, one work
+ *             queue over all sequences (the stage events then time the
+ *             batch: routing of all, selection of all, V re-layout of all,
+ *             the attention launch).
+ * Either way each sequence's output is the same bits as crisp_prefill on it
+ * alone.  All sequences are validated before the first launch; an error
+ * leaves every output untouched.  Sequences with seq_len <
+ * dense_below_tokens run dense attention.
  */
+/*
+ * Workspace for crisp_prefill_batch to attend a whole batch in one launch:
+ * the routing / selection scratch of the longest sequence, plus per sequence
+ * its intermediates and transposed V, plus a small table.  seq_lens: host
+ * array [batch].  Host-only and pure; errors as crisp_workspace_size.
+ */
+int crisp_workspace_size_batch(const int *seq_lens, int batch, int n_heads, int n_kv_heads,
+                               int head_dim, int block_size, size_t *ws_bytes);
+
 int crisp_prefill_batch(const crisp_seq *seqs, int batch, const crisp_strides *strides,
                         int n_heads, int n_kv_heads, int head_dim, int block_size, float alpha,
                         const crisp_opts *opts, void *ws, size_t ws_bytes, void *stream);

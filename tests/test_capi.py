@@ -251,3 +251,23 @@ def test_binding_rejects_bad_tensors():
         crisp.crisp_prefill_noalloc(q, k, k, 1.0, q[:2])
     with pytest.raises(TypeError):
         crisp.crisp_attend(q, k, [0, 1], None, None, ws, q)
+
+
+def test_batch_workspace_size(L):
+    """The single-launch batch workspace holds every sequence's lists and V^T
+    beside the largest routing / selection scratch."""
+    lens = [300, 1, 0, 1000, 129, 2048]
+    ws = crisp.crisp_workspace_size_batch(lens, 32, 8)
+    singles = [ws_size(n)[1] for n in lens]
+    assert ws >= max(singles) and ws % 256 == 0
+    # per sequence at least its CSR capacity and its padded V^T
+    need = sum(4 * ws_size(n)[2] + 8 * 128 * (-(-n // 128)) * 128 * 2 for n in lens)
+    assert ws >= need
+    assert crisp.crisp_workspace_size_batch(lens + [4096], 32, 8) > ws
+    assert crisp.crisp_workspace_size_batch([], 32, 8) > 0
+    sz = C.c_size_t(0)
+    bad = (C.c_int * 2)(128, -1)
+    assert L.crisp_workspace_size_batch(bad, 2, 32, 8, 128, 128, C.byref(sz)) == SHAPE
+    assert L.crisp_workspace_size_batch(bad, 1, 32, 8, 64, 128, C.byref(sz)) == UNSUPPORTED
+    assert L.crisp_workspace_size_batch(None, 1, 32, 8, 128, 128, C.byref(sz)) == INVALID
+    assert L.crisp_workspace_size_batch(bad, 1, 32, 8, 128, 128, None) == INVALID

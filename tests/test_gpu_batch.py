@@ -1,9 +1,11 @@
 """Several sequences per call, strided layouts and the context-length gate
 (needs an MI355X).
 
-crisp_prefill_batch runs Alg. 1 on each sequence in turn.  Each output is
-checked bit for bit against crisp_prefill on a contiguous copy of that
-sequence: the same kernels see the same values. crisp_prefill itself is
+crisp_prefill_batch runs Alg. 1 on each sequence in turn, or, with a
+workspace of crisp_workspace_size_batch, routes and selects every sequence
+and attends the whole batch in one launch ("fused").  Each output is checked
+bit for bit against crisp_prefill on a contiguous copy of that sequence: the
+same kernels see the same values. crisp_prefill itself is
 checked against the oracle (routing, selection and attention) on the same
 sequences.  The gate (Section 5.3, "Short contexts") must reproduce
 crisp_attend_dense bit for bit and the oracle's dense causal attention.
@@ -34,6 +36,17 @@ def _gpu():
 def gen(n, seed_id):
     """A seeded sequence of n >= 1 tokens (None for n == 0)."""
     return synth.generate(synth.custom_spec(n, HQ, HKV, KINDS, seed_id=seed_id)) if n else None
+
+
+def batch_ws(lens, kind, hq=HQ, hkv=HKV):
+    """The workspace that selects crisp_prefill_batch's path: the longest
+    sequence's (one sequence after another) or the batch's (one launch)."""
+    if kind == "serial":
+        return crisp.alloc_workspace(max(lens), hq, hkv)
+    return crisp.alloc_batch_workspace(lens, hq, hkv)
+
+
+PATHS = ["serial", "fused"]
 
 
 def single(q, k, v, alpha=1.0, opts=None):
@@ -70,7 +83,8 @@ def oracle_check(inp, got, alpha=1.0, tag=""):
     P.check_outputs(full.numpy().reshape(HQ * nb, B, 128), want, f"batch {tag}")
 
 
-def test_varlen_packed_tokens_major():
+@pytest.mark.parametrize("path", PATHS)
+def test_varlen_packed_tokens_major(path):
     """[total, heads, d] packed sequences with cumulative offsets (ragged,
     one of length 1, one empty), one call, one workspace."""
     lens = [300, 1, 0, 1000, 129, 2048]
@@ -88,7 +102,7 @@ def test_varlen_packed_tokens_major():
             v[cu[b]:cu[b + 1]] = inps[b].v.transpose(0, 1)
     qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
     out = torch.full_like(qd, float("nan"))
-    crisp.prefill_varlen(qd, kd, vd, cu, out, 1.0, crisp.alloc_workspace(max(lens), HQ, HKV))
+    crisp.prefill_varlen(qd, kd, vd, cu, out, 1.0, batch_ws(lens, path))
     torch.cuda.synchronize()
     for b, n in enumerate(lens):
         if n == 0:
@@ -96,10 +110,11 @@ def test_varlen_packed_tokens_major():
         ref = single(inps[b].q.cuda(), inps[b].k.cuda(), inps[b].v.cuda())
         got = out[cu[b]:cu[b + 1]].transpose(0, 1)
         assert same_bits(got, ref), f"sequence {b} (n={n}) differs from crisp_prefill"
-        oracle_check(inps[b], got, tag=f"varlen seq {b} n={n}")
+        oracle_check(inps[b], got, tag=f"varlen {path} seq {b} n={n}")
 
 
-def test_batch_seq_heads_layout():
+@pytest.mark.parametrize("path", PATHS)
+def test_batch_seq_heads_layout(path):
     """Equal lengths in a [batch, seq, heads, d] tensor."""
     n, batch = 1024, 2
     inps = [gen(n, 320 + b) for b in range(batch)]
@@ -111,13 +126,14 @@ def test_batch_seq_heads_layout():
                               [k[b].transpose(0, 1) for b in range(batch)],
                               [v[b].transpose(0, 1) for b in range(batch)],
                               [out[b].transpose(0, 1) for b in range(batch)],
-                              1.0, crisp.alloc_workspace(n, HQ, HKV))
+                              1.0, batch_ws([n] * batch, path))
     for b in range(batch):
         ref = single(inps[b].q.cuda(), inps[b].k.cuda(), inps[b].v.cuda())
         assert same_bits(out[b].transpose(0, 1), ref), f"batch element {b}"
 
 
-def test_batch_contiguous_default_strides():
+@pytest.mark.parametrize("path", PATHS)
+def test_batch_contiguous_default_strides(path):
     """strides == NULL: each sequence contiguous [heads, n, d], separate
     allocations, called through the C ABI directly."""
     lens = [640, 77, 1500]
@@ -127,7 +143,7 @@ def test_batch_contiguous_default_strides():
     arr = (crisp.crisp_seq * len(lens))()
     for b, ((q, k, v), o) in enumerate(zip(dev, outs)):
         arr[b] = crisp.crisp_seq(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lens[b])
-    ws = crisp.alloc_workspace(max(lens), HQ, HKV)
+    ws = batch_ws(lens, path)
     rc = crisp.lib().crisp_prefill_batch(arr, len(lens), None, HQ, HKV, 128, 128, 1.0, None,
                                          C.c_void_p(ws.data_ptr()), ws.numel(),
                                          C.c_void_p(torch.cuda.current_stream().cuda_stream))
@@ -157,7 +173,8 @@ def test_gate_runs_dense_below_threshold():
     assert not same_bits(gated, ungated)
 
 
-def test_gate_inside_a_batch():
+@pytest.mark.parametrize("path", PATHS)
+def test_gate_inside_a_batch(path):
     """A gate between the lengths: short sequences dense, long ones sparse."""
     lens = [3000, 5000]
     inps = [gen(n, 380 + i) for i, n in enumerate(lens)]
@@ -165,10 +182,33 @@ def test_gate_inside_a_batch():
     dev = [(i.q.cuda(), i.k.cuda(), i.v.cuda()) for i in inps]
     outs = [torch.empty_like(d[0]) for d in dev]
     crisp.crisp_prefill_batch([d[0] for d in dev], [d[1] for d in dev], [d[2] for d in dev], outs,
-                              1.0, crisp.alloc_workspace(max(lens), HQ, HKV), opts=opts)
+                              1.0, batch_ws(lens, path), opts=opts)
     q, k, v = dev[0]
     dense = torch.empty_like(q)
     crisp.crisp_attend_dense(q, k, v, crisp.alloc_workspace(lens[0], HQ, HKV), dense)
     assert same_bits(outs[0], dense)
     assert not same_bits(outs[0], single(*dev[0]))
     assert same_bits(outs[1], single(*dev[1]))
+
+
+def test_fused_batch_llama_heads():
+    """The single-launch path at the Llama-3.1-8B head shape (32 query / 8 KV
+    heads): twelve sequences of mixed lengths (short, ragged, one of 20000
+    tokens), each bit-identical to crisp_prefill on it alone; the serial path
+    on the same call agrees too."""
+    hq, hkv = 32, 8
+    lens = [20000, 2048, 2048, 77, 4096 + 5, 1, 2048, 640, 8192, 129, 3000, 2048]
+    kinds = [synth.VS if h % 4 != 3 else synth.DIFFUSE for h in range(hq)]
+    inps = [synth.generate(synth.custom_spec(n, hq, hkv, kinds, seed_id=400 + i))
+            for i, n in enumerate(lens)]
+    P.log(f"fused batch lens={lens}")
+    dev = [(i.q.cuda(), i.k.cuda(), i.v.cuda()) for i in inps]
+    for path in PATHS:
+        outs = [torch.full_like(d[0], float("nan")) for d in dev]
+        crisp.crisp_prefill_batch([d[0] for d in dev], [d[1] for d in dev], [d[2] for d in dev], outs,
+                                  1.0, batch_ws(lens, path, hq, hkv))
+        torch.cuda.synchronize()
+        for b, (q, k, v) in enumerate(dev):
+            ref = torch.empty_like(q)
+            crisp.crisp_prefill(q, k, v, 1.0, crisp.alloc_workspace(lens[b], hq, hkv), ref)
+            assert same_bits(outs[b], ref), f"{path}: sequence {b} (n={lens[b]})"
