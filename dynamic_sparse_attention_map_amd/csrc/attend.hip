@@ -457,6 +457,19 @@ struct SeqChunk {
     int first, count;
 };
 
+// Up to 64 pointers per launch, passed by value.
+struct PtrChunk {
+    const void* p[64];
+    int count;
+};
+
+// one work-group of 64 threads
+__global__ void __launch_bounds__(64)
+ptr_table_kernel(PtrChunk c, const void** __restrict__ dst)
+{
+    if ((int)threadIdx.x < c.count) dst[threadIdx.x] = c.p[threadIdx.x];
+}
+
 // grid (ceil(max per_xcd / 256), count), 256 threads
 __global__ void __launch_bounds__(256)
 seq_table_kernel(SeqChunk c, SeqDesc* __restrict__ table, int* __restrict__ slot_seq)
@@ -477,8 +490,9 @@ seq_table_kernel(SeqChunk c, SeqDesc* __restrict__ table, int* __restrict__ slot
 // then one 16-byte chunk.  Keys past n are zero.  The first work-group also
 // clears the attention kernel's eight per-XCD queue counters.
 // grid (N_b * 2, hkv), 256 threads.
+template <class R>
 __global__ void __launch_bounds__(256)
-v_transpose_kernel(Rows v, int n, int n_img, uint16_t* __restrict__ vt, int* __restrict__ queue)
+v_transpose_kernel(R v, int n, int n_img, uint16_t* __restrict__ vt, int* __restrict__ queue)
 {
     __shared__ uint16_t tile[64][kD + 8];
     const int g = blockIdx.y, key0 = blockIdx.x * 64, tid = threadIdx.x;
@@ -508,11 +522,11 @@ v_transpose_kernel(Rows v, int n, int n_img, uint16_t* __restrict__ vt, int* __r
 
 }  // namespace
 
-hipError_t launch_v_transpose(Rows v, int n, int hkv, uint16_t* vt, int* queue,
-                              hipStream_t stream)
+template <class R>
+hipError_t launch_v_transpose(R v, int n, int hkv, uint16_t* vt, int* queue, hipStream_t stream)
 {
     const int n_img = (n + kB - 1) / kB * 2;
-    hipLaunchKernelGGL(v_transpose_kernel, dim3(n_img, hkv), dim3(256), 0, stream, v, n, n_img, vt,
+    hipLaunchKernelGGL(HIP_KERNEL_NAME(v_transpose_kernel<R>), dim3(n_img, hkv), dim3(256), 0, stream, v, n, n_img, vt,
                        queue);
     return hipGetLastError();
 }
@@ -573,6 +587,20 @@ hipError_t launch_seq_table(const SeqDesc* descs, int first, int count, SeqDesc*
     return hipSuccess;
 }
 
+hipError_t launch_ptr_table(const void* const* ptrs, int count, const void** dst,
+                            hipStream_t stream)
+{
+    for (int at = 0; at < count; at += 64) {
+        PtrChunk c{};
+        c.count = count - at < 64 ? count - at : 64;
+        for (int i = 0; i < c.count; ++i) c.p[i] = ptrs[at + i];
+        hipLaunchKernelGGL(ptr_table_kernel, dim3(1), dim3(64), 0, stream, c, dst + at);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
 hipError_t launch_attend_batch(const SeqDesc* table, const int* slot_seq, int total_per_xcd,
                                int hq, int hkv, int* counters, hipStream_t stream)
 {
@@ -581,5 +609,8 @@ hipError_t launch_attend_batch(const SeqDesc* table, const int* slot_seq, int to
                        slot_seq, hkv, hq / hkv, scale_log2, total_per_xcd, counters);
     return hipGetLastError();
 }
+
+template hipError_t launch_v_transpose<Rows>(Rows, int, int, uint16_t*, int*, hipStream_t);
+template hipError_t launch_v_transpose<SeqRows>(SeqRows, int, int, uint16_t*, int*, hipStream_t);
 
 }  // namespace crisp

@@ -5,6 +5,7 @@
 #include <cmath>
 #include <cstdint>
 #include <cstring>
+#include <algorithm>
 #include <vector>
 
 #include "crisp.h"
@@ -175,7 +176,8 @@ T* at(void* ws, size_t off)
     return reinterpret_cast<T*>(static_cast<char*>(ws) + off);
 }
 
-int do_route(const Shape& s, const Opts& op, Rows q, Rows k, void* ws,
+template <class R>
+int do_route(const Shape& s, const Opts& op, R q, R k, void* ws,
              const Layout& L, uint8_t* pattern, float* c_struct, float* p_v, float* p_s,
              hipStream_t stream)
 {
@@ -195,7 +197,8 @@ int do_route(const Shape& s, const Opts& op, Rows q, Rows k, void* ws,
     return hip_status(launch_route(q, k, s.n, s.hq, s.hkv, ra, p_v, p_s, c_struct, pattern, stream));
 }
 
-int do_select(const Shape& s, const Opts& op, float alpha, Rows q, Rows k,
+template <class R>
+int do_select(const Shape& s, const Opts& op, float alpha, R q, R k,
               const uint8_t* pattern, const float* p_v, const float* p_s, void* ws,
               const Layout& L, int32_t* sel_v, int32_t* sel_s, int32_t* counts,
               int32_t* row_ptr, int32_t* col_idx, hipStream_t stream)
@@ -263,30 +266,59 @@ bool bad_strides(long long sh, long long st)
     return sh <= 0 || st <= 0 || sh % 8 != 0 || st % 8 != 0;
 }
 
-// Workspace of crisp_prefill_batch's single-launch path: the shared scratch
-// region S at offset 0 (routing and selection, one sequence at a time), then
-// per sequence its crisp_prefill intermediates (region P of its own layout)
-// and its V^T images, then the sequence table, the queue-slot map and the
-// queue counters.
+// crisp_prefill_batch's single-launch path works on groups: the sequences
+// of one length form a group, routed, selected and re-laid out as one layer
+// of count * n_heads query and count * n_kv_heads KV heads (sequence i of
+// the group owns heads i * n_heads .. and i * n_kv_heads ..), reading its
+// rows through per-sequence base pointers; then one attention launch covers
+// every sequence.  Workspace: the routing / selection scratch region S at
+// offset 0 (one group at a time), then per group its intermediates (region
+// P of the group's layout), its V^T images and three pointer tables, then
+// the sequence table, the queue-slot map and the queue counters.
+struct BatchGroup {
+    int n;
+    std::vector<int> seqs;        // indices into the batch, in batch order
+    size_t p_base, vt_base, qtab, ktab, vtab;
+};
 struct BatchLayout {
-    std::vector<size_t> p_base, vt_base;
-    std::vector<int> run, per_xcd, slot0;
+    std::vector<BatchGroup> groups;
+    std::vector<int> run, per_xcd, slot0;   // per batch entry
     size_t table = 0, slot_seq = 0, counters = 0, total = 0;
     int total_per_xcd = 0;
 };
 
-// seq_len of entry b (validated shapes)
+// the group's layer shape (validated lengths)
+Shape group_shape(const BatchGroup& g, int hq, int hkv)
+{
+    Shape s;
+    const int c = (int)g.seqs.size();
+    (void)check_shape(g.n, hq * c, hkv * c, kD, kB, &s);
+    return s;
+}
+
 template <typename LenOf>
 BatchLayout make_batch_layout(int batch, LenOf len_of, int hq, int hkv)
 {
     BatchLayout B;
-    size_t S = 0;
     for (int b = 0; b < batch; ++b) {
         const int n = len_of(b);
         if (n == 0) continue;
-        Shape s;
-        (void)check_shape(n, hq, hkv, kD, kB, &s);
-        const Layout L = make_layout(s);
+        // a group's layer must stay within the shape limits of one call
+        // (n_heads * N_b (N_b + 1) / 2 list entries below 2^31)
+        const long long nb = (n + kB - 1) / kB;
+        const long long cap = std::max(1LL, ((1LL << 31) - 1) / ((long long)hq * (nb * (nb + 1) / 2)));
+        auto it = std::find_if(B.groups.begin(), B.groups.end(), [&](const BatchGroup& g) {
+            return g.n == n && (long long)g.seqs.size() < cap;
+        });
+        if (it == B.groups.end()) {
+            B.groups.push_back(BatchGroup{n, {}, 0, 0, 0, 0, 0});
+            it = B.groups.end() - 1;
+        }
+        it->seqs.push_back(b);
+    }
+    size_t S = 0;
+    for (const BatchGroup& g : B.groups) {
+        const Layout L = make_layout(group_shape(g, hq, hkv));
         S = std::max(S, std::max(L.route_end, L.select_end));
     }
     size_t o = align_up(S);
@@ -295,19 +327,21 @@ BatchLayout make_batch_layout(int batch, LenOf len_of, int hq, int hkv)
         o = align_up(o + bytes);
         return at;
     };
-    B.p_base.assign(batch, 0);
-    B.vt_base.assign(batch, 0);
+    for (BatchGroup& g : B.groups) {
+        const Shape s = group_shape(g, hq, hkv);
+        const Layout L = make_layout(s);
+        g.p_base = take(L.total - L.pattern);
+        g.vt_base = take((size_t)s.hkv * kD * s.nb * kB * sizeof(uint16_t));
+        g.qtab = take(g.seqs.size() * sizeof(void*));
+        g.ktab = take(g.seqs.size() * sizeof(void*));
+        g.vtab = take(g.seqs.size() * sizeof(void*));
+    }
     B.run.assign(batch, 0);
     B.per_xcd.assign(batch, 0);
     B.slot0.assign(batch, 0);
     for (int b = 0; b < batch; ++b) {
         const int n = len_of(b);
         if (n == 0) continue;
-        Shape s;
-        (void)check_shape(n, hq, hkv, kD, kB, &s);
-        const Layout L = make_layout(s);
-        B.p_base[b] = take(L.total - L.pattern);
-        B.vt_base[b] = take((size_t)hkv * kD * s.nb * kB * sizeof(uint16_t));
         attend_plan(n, hq, hkv, &B.run[b], &B.per_xcd[b]);
         B.slot0[b] = B.total_per_xcd;
         B.total_per_xcd += B.per_xcd[b];
@@ -319,88 +353,116 @@ BatchLayout make_batch_layout(int batch, LenOf len_of, int hq, int hkv)
     return B;
 }
 
-// Alg. 1 over every sequence of a batch with one attention launch: route all
-// (stage 0 -> 1), select all (1 -> 2), lay out V and build the sequence
-// table (2 -> 3), attend (3 -> 4).  Sequences below the gating length keep
-// dense lists.
+// Alg. 1 over every sequence of a batch: route every group (stage 0 -> 1),
+// select every group (1 -> 2), lay out V and build the sequence table
+// (2 -> 3), attend all in one launch (3 -> 4).  Groups below the gating
+// length keep dense lists.
 int run_prefill_batch_fused(const crisp_seq* seqs, int batch, const crisp_strides* strides,
                             int hq, int hkv, const Opts& op, float alpha, void* ws,
                             const BatchLayout& B, hipStream_t st)
 {
-    std::vector<SeqDesc> descs;
-    std::vector<Operands> xs(batch);
-    std::vector<Shape> shapes(batch);
-    std::vector<Layout> lays(batch);
-    for (int b = 0; b < batch; ++b) {
-        (void)check_shape(seqs[b].seq_len, hq, hkv, kD, kB, &shapes[b]);
-        if (shapes[b].n == 0) continue;
-        lays[b] = make_layout(shapes[b]);
+    const size_t ng = B.groups.size();
+    std::vector<Shape> gs(ng);
+    std::vector<Layout> gl(ng);
+    std::vector<SeqRows> gq(ng), gk(ng), gv(ng);
+    for (size_t i = 0; i < ng; ++i) {
+        const BatchGroup& g = B.groups[i];
+        gs[i] = group_shape(g, hq, hkv);
+        gl[i] = make_layout(gs[i]);
+        // rows of every sequence of the group share their strides
+        long long qsh, qst, ksh, kst, vsh, vst;
         if (strides) {
-            xs[b].q = Rows{static_cast<const uint16_t*>(seqs[b].q), strides->q_head, strides->q_token};
-            xs[b].k = Rows{static_cast<const uint16_t*>(seqs[b].k), strides->k_head, strides->k_token};
-            xs[b].v = Rows{static_cast<const uint16_t*>(seqs[b].v), strides->v_head, strides->v_token};
-            xs[b].out = OutRows{static_cast<uint16_t*>(seqs[b].out), strides->out_head, strides->out_token};
+            qsh = strides->q_head, qst = strides->q_token;
+            ksh = strides->k_head, kst = strides->k_token;
+            vsh = strides->v_head, vst = strides->v_token;
         } else {
-            const int n = shapes[b].n;
-            xs[b] = Operands{packed(seqs[b].q, n), packed(seqs[b].k, n), packed(seqs[b].v, n),
-                             packed_out(seqs[b].out, n)};
+            qsh = ksh = vsh = (long long)g.n * kD;
+            qst = kst = vst = kD;
         }
+        gq[i] = SeqRows{at<const uint16_t*>(ws, g.qtab), hq, qsh, qst};
+        gk[i] = SeqRows{at<const uint16_t*>(ws, g.ktab), hkv, ksh, kst};
+        gv[i] = SeqRows{at<const uint16_t*>(ws, g.vtab), hkv, vsh, vst};
+        // the three pointer tables, written from kernel arguments
+        std::vector<const void*> qp, kp, vp;
+        for (int b : g.seqs) {
+            qp.push_back(seqs[b].q);
+            kp.push_back(seqs[b].k);
+            vp.push_back(seqs[b].v);
+        }
+        if (launch_ptr_table(qp.data(), (int)qp.size(), at<const void*>(ws, g.qtab), st) != hipSuccess ||
+            launch_ptr_table(kp.data(), (int)kp.size(), at<const void*>(ws, g.ktab), st) != hipSuccess ||
+            launch_ptr_table(vp.data(), (int)vp.size(), at<const void*>(ws, g.vtab), st) != hipSuccess)
+            return CRISP_ERR_HIP;
     }
-    // P-region pointer of sequence b for a field at layout offset `off`
-    auto pp = [&](int b, size_t off) { return B.p_base[b] + (off - lays[b].pattern); };
-    auto sparse = [&](int b) { return shapes[b].n > 0 && shapes[b].n >= op.dense_below; };
+    auto pp = [&](size_t i, size_t off) { return B.groups[i].p_base + (off - gl[i].pattern); };
+    auto sparse = [&](size_t i) { return B.groups[i].n >= op.dense_below; };
     int rc;
     mark(0, st);
-    for (int b = 0; b < batch; ++b) {
-        if (!sparse(b)) continue;
-        const Layout& L = lays[b];
-        if ((rc = do_route(shapes[b], op, xs[b].q, xs[b].k, ws, L, at<uint8_t>(ws, pp(b, L.pattern)),
-                           at<float>(ws, pp(b, L.c_struct)), at<float>(ws, pp(b, L.p_v)),
-                           at<float>(ws, pp(b, L.p_s)), st)))
+    for (size_t i = 0; i < ng; ++i) {
+        if (!sparse(i)) continue;
+        const Layout& L = gl[i];
+        if ((rc = do_route(gs[i], op, gq[i], gk[i], ws, L, at<uint8_t>(ws, pp(i, L.pattern)),
+                           at<float>(ws, pp(i, L.c_struct)), at<float>(ws, pp(i, L.p_v)),
+                           at<float>(ws, pp(i, L.p_s)), st)))
             return rc;
     }
     mark(1, st);
-    for (int b = 0; b < batch; ++b) {
-        if (!sparse(b)) continue;
-        const Layout& L = lays[b];
-        if ((rc = do_select(shapes[b], op, alpha, xs[b].q, xs[b].k, at<uint8_t>(ws, pp(b, L.pattern)),
-                            at<float>(ws, pp(b, L.p_v)), at<float>(ws, pp(b, L.p_s)), ws, L,
-                            at<int32_t>(ws, pp(b, L.sel_v)), at<int32_t>(ws, pp(b, L.sel_s)),
-                            at<int32_t>(ws, pp(b, L.counts)), at<int32_t>(ws, pp(b, L.row_ptr)),
-                            at<int32_t>(ws, pp(b, L.col_idx)), st)))
+    for (size_t i = 0; i < ng; ++i) {
+        if (!sparse(i)) continue;
+        const Layout& L = gl[i];
+        if ((rc = do_select(gs[i], op, alpha, gq[i], gk[i], at<uint8_t>(ws, pp(i, L.pattern)),
+                            at<float>(ws, pp(i, L.p_v)), at<float>(ws, pp(i, L.p_s)), ws, L,
+                            at<int32_t>(ws, pp(i, L.sel_v)), at<int32_t>(ws, pp(i, L.sel_s)),
+                            at<int32_t>(ws, pp(i, L.counts)), at<int32_t>(ws, pp(i, L.row_ptr)),
+                            at<int32_t>(ws, pp(i, L.col_idx)), st)))
             return rc;
     }
     mark(2, st);
     int* counters = at<int>(ws, B.counters);
-    for (int b = 0; b < batch; ++b) {
-        if (shapes[b].n == 0) continue;
-        uint16_t* vt = at<uint16_t>(ws, B.vt_base[b]);
-        if (launch_v_transpose(xs[b].v, shapes[b].n, hkv, vt, counters, st) != hipSuccess)
+    std::vector<SeqDesc> descs(batch);
+    std::vector<int> live(batch, 0);
+    for (size_t i = 0; i < ng; ++i) {
+        const BatchGroup& g = B.groups[i];
+        uint16_t* vt = at<uint16_t>(ws, g.vt_base);
+        if (launch_v_transpose(gv[i], g.n, gs[i].hkv, vt, counters, st) != hipSuccess)
             return CRISP_ERR_HIP;
-        SeqDesc d{};
-        d.q = xs[b].q.p;
-        d.k = xs[b].k.p;
-        d.out = xs[b].out.p;
-        d.vt = vt;
-        const bool sp = sparse(b);
-        d.row_ptr = sp ? at<int32_t>(ws, pp(b, lays[b].row_ptr)) : nullptr;
-        d.col_idx = sp ? at<int32_t>(ws, pp(b, lays[b].col_idx)) : nullptr;
-        d.q_sh = xs[b].q.sh;
-        d.q_st = xs[b].q.st;
-        d.k_sh = xs[b].k.sh;
-        d.k_st = xs[b].k.st;
-        d.o_sh = xs[b].out.sh;
-        d.o_st = xs[b].out.st;
-        d.n = shapes[b].n;
-        d.run = B.run[b];
-        d.slot0 = B.slot0[b];
-        d.per_xcd = B.per_xcd[b];
-        descs.push_back(d);
+        const int nb = gs[i].nb;
+        for (size_t j = 0; j < g.seqs.size(); ++j) {
+            const int b = g.seqs[j];
+            SeqDesc& d = descs[b];
+            d.q = static_cast<const uint16_t*>(seqs[b].q);
+            d.k = static_cast<const uint16_t*>(seqs[b].k);
+            d.out = static_cast<uint16_t*>(seqs[b].out);
+            d.vt = vt + j * (size_t)hkv * nb * kB * kD;     // its KV heads' images
+            const bool sp = sparse(i);
+            d.row_ptr = sp ? at<int32_t>(ws, pp(i, gl[i].row_ptr)) + j * (size_t)hq * (nb + 1) : nullptr;
+            d.col_idx = sp ? at<int32_t>(ws, pp(i, gl[i].col_idx)) : nullptr;
+            d.q_sh = gq[i].sh;
+            d.q_st = gq[i].st;
+            d.k_sh = gk[i].sh;
+            d.k_st = gk[i].st;
+            if (strides) {
+                d.o_sh = strides->out_head;
+                d.o_st = strides->out_token;
+            } else {
+                d.o_sh = (long long)g.n * kD;
+                d.o_st = kD;
+            }
+            d.n = g.n;
+            d.run = B.run[b];
+            d.slot0 = B.slot0[b];
+            d.per_xcd = B.per_xcd[b];
+            live[b] = 1;
+        }
     }
-    if (descs.empty()) return CRISP_OK;
+    std::vector<SeqDesc> packed_descs;
+    for (int b = 0; b < batch; ++b)
+        if (live[b]) packed_descs.push_back(descs[b]);
+    if (packed_descs.empty()) return CRISP_OK;
     SeqDesc* table = at<SeqDesc>(ws, B.table);
     int* slot_seq = at<int>(ws, B.slot_seq);
-    if (launch_seq_table(descs.data(), 0, (int)descs.size(), table, slot_seq, st) != hipSuccess)
+    if (launch_seq_table(packed_descs.data(), 0, (int)packed_descs.size(), table, slot_seq, st) !=
+        hipSuccess)
         return CRISP_ERR_HIP;
     mark(3, st);
     const hipError_t e = launch_attend_batch(table, slot_seq, B.total_per_xcd, hq, hkv, counters, st);

@@ -12,6 +12,12 @@ constexpr int kD = 128;            // head_dim
 constexpr int kB = 128;            // block size B (tokens per block)
 constexpr int kMaxBlocks = 4096;   // largest N_b (seq_len 524288 at B = 128)
 constexpr int kRouteSegs = 64;     // tile segments per head in the routing row reduction
+// Up to these sizes a kernel runs one work-group per head over the whole
+// head (bit-identical to the multi-launch path used beyond): the route
+// reductions up to kRouteSmall key blocks, the PE cut-off up to kRadixSmall
+// map entries (N_b <= 128).  The multi-launch scratch is not needed below.
+constexpr int kRouteSmall = 64;
+constexpr int kRadixSmall = 128 * 129 / 2;
 
 // A bf16 operand [heads][tokens][128] with arbitrary head and token strides
 // in elements; the 128 head-dimension values of one row are contiguous.
@@ -19,6 +25,18 @@ struct Rows {
     const uint16_t* p;
     long long sh, st;               // head stride, token stride
     __host__ __device__ const uint16_t* row(int h, long long i) const { return p + h * sh + i * st; }
+};
+// The same rows for a group of sequences of one length seen as one layer of
+// count * hper heads: head h is head h % hper of sequence h / hper, whose
+// rows start at base[h / hper] (a device array); the strides are shared.
+struct SeqRows {
+    const uint16_t* const* base;
+    int hper;
+    long long sh, st;
+    __device__ const uint16_t* row(int h, long long i) const
+    {
+        return base[h / hper] + (long long)(h % hper) * sh + i * st;
+    }
 };
 struct OutRows {
     uint16_t* p;
@@ -65,7 +83,8 @@ struct RouteArgs {
     float* tile_sums;               // [hq][4][Nb] slash-part sums per tile
 };
 
-hipError_t launch_route(Rows q, Rows k, int n, int hq, int hkv,
+template <class R>
+hipError_t launch_route(R q, R k, int n, int hq, int hkv,
                         const RouteArgs& a, float* p_v, float* p_s, float* c_struct,
                         uint8_t* pattern, hipStream_t stream);
 
@@ -87,14 +106,16 @@ struct SelectScratch {
     uint8_t* bitmap;                // [hq][2][Nb]
 };
 
-hipError_t launch_select(Rows q, Rows k, const uint8_t* pattern,
+template <class R>
+hipError_t launch_select(R q, R k, const uint8_t* pattern,
                          const float* p_v, const float* p_s, int n, int hq, int hkv,
                          const VsRule& vs, float gamma, const SelectScratch& s, int32_t* sel_v,
                          int32_t* sel_s, int32_t* sel_counts, int32_t* row_ptr, int32_t* col_idx,
                          hipStream_t stream);
 
 // queue: the attention kernel's 8 ints of device scratch, cleared here.
-hipError_t launch_v_transpose(Rows v, int n, int hkv, uint16_t* vt, int* queue,
+template <class R>
+hipError_t launch_v_transpose(R v, int n, int hkv, uint16_t* vt, int* queue,
                               hipStream_t stream);
 
 // row_ptr / col_idx == nullptr: dense causal lists.
@@ -128,6 +149,11 @@ void attend_plan(int n, int hq, int hkv, int* run, int* per_xcd);
 // copy), in launches of up to 16 descriptors.
 hipError_t launch_seq_table(const SeqDesc* descs, int first, int count, SeqDesc* table,
                             int* slot_seq, hipStream_t stream);
+
+// Writes `count` host pointers into the device array dst (kernel arguments
+// only), in launches of up to 64.
+hipError_t launch_ptr_table(const void* const* ptrs, int count, const void** dst,
+                            hipStream_t stream);
 
 // Attention of every sequence in `table` in one launch; total_per_xcd is the
 // sum of their per_xcd, slot_seq maps a queue slot to its sequence and

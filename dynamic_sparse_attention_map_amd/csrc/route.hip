@@ -41,9 +41,9 @@ constexpr int kTileKeys = 128;
 // the wait for the copies never waits on fresh stores.
 // Aligned (B divides n): row i sits at column i of the last tile, so the
 // split column and the causal cut are compile-time per (chunk, key group).
-template <bool Aligned>
+template <bool Aligned, class QK>
 __global__ void __launch_bounds__(1024)
-proxy_map_kernel(Rows q, Rows k, int n, int nb,
+proxy_map_kernel(QK q, QK k, int n, int nb,
                  int G, int tiles_per_wg, float scale_log2,
                  float* __restrict__ part_m, float* __restrict__ part_lo,
                  float* __restrict__ part_up)
@@ -356,7 +356,6 @@ finalize_kernel(const float* __restrict__ tile_sums, const float* __restrict__ p
 // (row i, part p) walks segments p, p+8, .. and, within each, tiles
 // seg, seg+64, ..; wave w takes tiles w, w+16, ..), so p_v, p_s, C_struct
 // and the routing bit are the same bits.
-constexpr int kRouteSmall = 64;
 
 __global__ void __launch_bounds__(1024)
 route_small_kernel(const float* __restrict__ part_m, const float* __restrict__ part_lo,
@@ -498,8 +497,9 @@ route_small_kernel(const float* __restrict__ part_m, const float* __restrict__ p
 // grid (Nb, hkv + hq), 256 threads: y < hkv: mean of key block x of KV head
 // y over the tokens it holds; y >= hkv (x == 0 only): mean of the R
 // representative query rows of head y - hkv.
+template <class QK>
 __global__ void __launch_bounds__(256)
-jsd_pool_kernel(Rows q, Rows k, int n, int nb,
+jsd_pool_kernel(QK q, QK k, int n, int nb,
                 int hkv, float* __restrict__ kbar, float* __restrict__ qbar)
 {
     __shared__ float red[16][kD];
@@ -604,7 +604,8 @@ jsd_route_kernel(const float* __restrict__ kbar, const float* __restrict__ qbar,
 
 }  // namespace
 
-hipError_t launch_route(Rows q, Rows k, int n, int hq, int hkv,
+template <class QK>
+hipError_t launch_route(QK q, QK k, int n, int hq, int hkv,
                         const RouteArgs& a, float* p_v, float* p_s, float* c_struct,
                         uint8_t* pattern, hipStream_t stream)
 {
@@ -617,10 +618,10 @@ hipError_t launch_route(Rows q, Rows k, int n, int hq, int hkv,
         tiles_per_wg *= 2;
     dim3 grid((nb + tiles_per_wg - 1) / tiles_per_wg, hkv * ((G + 3) / 4));
     if (n % kB == 0)
-        hipLaunchKernelGGL(proxy_map_kernel<true>, grid, dim3(1024), 0, stream, q, k, n, nb, G,
+        hipLaunchKernelGGL(HIP_KERNEL_NAME(proxy_map_kernel<true, QK>), grid, dim3(1024), 0, stream, q, k, n, nb, G,
                            tiles_per_wg, scale_log2, a.part_m, a.part_lo, a.part_up);
     else
-        hipLaunchKernelGGL(proxy_map_kernel<false>, grid, dim3(1024), 0, stream, q, k, n, nb, G,
+        hipLaunchKernelGGL(HIP_KERNEL_NAME(proxy_map_kernel<false, QK>), grid, dim3(1024), 0, stream, q, k, n, nb, G,
                            tiles_per_wg, scale_log2, a.part_m, a.part_lo, a.part_up);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -643,12 +644,17 @@ hipError_t launch_route(Rows q, Rows k, int n, int hq, int hkv,
                            a.tile_sums, p_v, nb, a.tau, route_here, p_s, c_struct, pattern);
     }
     if ((e = hipGetLastError()) != hipSuccess || route_here) return e;
-    hipLaunchKernelGGL(jsd_pool_kernel, dim3(nb, hkv + hq), dim3(256), 0, stream, q, k, n, nb, hkv,
+    hipLaunchKernelGGL(HIP_KERNEL_NAME(jsd_pool_kernel<QK>), dim3(nb, hkv + hq), dim3(256), 0, stream, q, k, n, nb, hkv,
                        a.jsd_kbar, a.jsd_qbar);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL(jsd_route_kernel, dim3(hq), dim3(256), 0, stream, a.jsd_kbar, a.jsd_qbar, p_v,
                        nb, G, a.tau, c_struct, pattern);
     return hipGetLastError();
 }
+
+template hipError_t launch_route<Rows>(Rows, Rows, int, int, int, const RouteArgs&, float*, float*,
+                                       float*, uint8_t*, hipStream_t);
+template hipError_t launch_route<SeqRows>(SeqRows, SeqRows, int, int, int, const RouteArgs&, float*,
+                                          float*, float*, uint8_t*, hipStream_t);
 
 }  // namespace crisp

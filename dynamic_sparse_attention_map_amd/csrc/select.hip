@@ -306,8 +306,9 @@ __device__ __forceinline__ bool group_has_pe(const uint8_t* pattern, int g, int 
 
 // grid (Nb, hq + hkv): block means of Q (PE heads) and K (groups with a PE
 // head), over the tokens each block holds (the last block may be partial).
+template <class R>
 __global__ void __launch_bounds__(256)
-pe_pool_kernel(Rows q, Rows k,
+pe_pool_kernel(R q, R k,
                const uint8_t* __restrict__ pattern, int n, int hq, int G,
                float* __restrict__ qbar, float* __restrict__ kbar)
 {
@@ -620,7 +621,6 @@ __device__ void radix_resolve(int pass, size_t total, const PeState& st, const u
 // state as pe_init_kernel does, which it replaces.  (Beyond this size the
 // passes over one work-group per head take longer than the multi-launch
 // path.)
-constexpr int kRadixSmall = 128 * 129 / 2;
 
 __global__ void __launch_bounds__(256)
 pe_radix_small_kernel(const uint8_t* __restrict__ pattern, int nb, float gamma,
@@ -914,7 +914,8 @@ expand_small_kernel(const uint8_t* __restrict__ pattern, int nb, const uint8_t* 
 
 }  // namespace
 
-hipError_t launch_select(Rows q, Rows k, const uint8_t* pattern,
+template <class R>
+hipError_t launch_select(R q, R k, const uint8_t* pattern,
                          const float* p_v, const float* p_s, int n, int hq, int hkv,
                          const VsRule& vs, float gamma, const SelectScratch& s, int32_t* sel_v,
                          int32_t* sel_s, int32_t* sel_counts, int32_t* row_ptr, int32_t* col_idx,
@@ -934,7 +935,7 @@ hipError_t launch_select(Rows q, Rows k, const uint8_t* pattern,
                            s.hist_mass, s.hist_count, s.pass_ctr, s.state);
         CRISP_CHECK_LAUNCH();
     }
-    hipLaunchKernelGGL(pe_pool_kernel, dim3(nb, hq + hkv), dim3(256), 0, stream, q, k, pattern, n,
+    hipLaunchKernelGGL(HIP_KERNEL_NAME(pe_pool_kernel<R>), dim3(nb, hq + hkv), dim3(256), 0, stream, q, k, pattern, n,
                        hq, G, s.qbar, s.kbar);
     CRISP_CHECK_LAUNCH();
     const float scale_log2 = kLog2e / sqrtf((float)kD);
@@ -978,5 +979,13 @@ hipError_t launch_select(Rows q, Rows k, const uint8_t* pattern,
 #undef CRISP_CHECK_LAUNCH
     return hipSuccess;
 }
+
+template hipError_t launch_select<Rows>(Rows, Rows, const uint8_t*, const float*, const float*, int,
+                                        int, int, const VsRule&, float, const SelectScratch&, int32_t*,
+                                        int32_t*, int32_t*, int32_t*, int32_t*, hipStream_t);
+template hipError_t launch_select<SeqRows>(SeqRows, SeqRows, const uint8_t*, const float*,
+                                           const float*, int, int, int, const VsRule&, float,
+                                           const SelectScratch&, int32_t*, int32_t*, int32_t*,
+                                           int32_t*, int32_t*, hipStream_t);
 
 }  // namespace crisp

@@ -212,3 +212,22 @@ def test_fused_batch_llama_heads():
             ref = torch.empty_like(q)
             crisp.crisp_prefill(q, k, v, 1.0, crisp.alloc_workspace(lens[b], hq, hkv), ref)
             assert same_bits(outs[b], ref), f"{path}: sequence {b} (n={lens[b]})"
+
+
+def test_fused_equal_lengths_group():
+    """Six packed [total, heads, d] sequences of one ragged length (1500
+    tokens): the single-launch path routes and selects them as one group of
+    6 x 4 query heads; each output equals crisp_prefill on that sequence."""
+    n, count = 1500, 6
+    inps = [gen(n, 500 + i) for i in range(count)]
+    cu = [i * n for i in range(count + 1)]
+    q = torch.cat([i.q.transpose(0, 1) for i in inps]).cuda()     # [total, H, d]
+    k = torch.cat([i.k.transpose(0, 1) for i in inps]).cuda()
+    v = torch.cat([i.v.transpose(0, 1) for i in inps]).cuda()
+    out = torch.full_like(q, float("nan"))
+    crisp.prefill_varlen(q, k, v, cu, out, 1.0, batch_ws([n] * count, "fused"))
+    torch.cuda.synchronize()
+    for b in range(count):
+        ref = single(inps[b].q.cuda(), inps[b].k.cuda(), inps[b].v.cuda())
+        assert same_bits(out[cu[b]:cu[b + 1]].transpose(0, 1), ref), f"sequence {b}"
+    oracle_check(inps[3], out[cu[3]:cu[4]].transpose(0, 1), tag="equal-length group seq 3")
