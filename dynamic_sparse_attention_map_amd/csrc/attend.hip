@@ -41,11 +41,16 @@ constexpr int kListWords = kMaxBlocks / 32;   // bitmap words per row
 // faster than 512 or 1024 at 4096.
 constexpr int kPairRun = 256;
 constexpr int kWholeHeadPairs = 512;
+// Pair-major order (below) while one KV head's K and V^T take at most this
+// many bytes (16384 tokens at head_dim 128).  Measured against head-major:
+// -7% at 8192 tokens, -3% at 16384, +4% at 32768, +13% at 131072.
+constexpr long long kPairMajorKvBytes = 8ll << 20;
 
 // Work items.  Pair p is query blocks Nb-1-2p and Nb-2-2p.  A chunk is `run`
 // consecutive pairs of the G query heads of one KV head: chunk c covers KV
 // head c % hkv and pairs run * (c / hkv) onward, and holds its G x run items
-// head-major (one head's run of pairs, then the next head's).  Item b belongs
+// head-major (one head's run of pairs, then the next head's), or for short
+// sequences pair-major (the G heads' pair p, then their pair p + 1).  Item b belongs
 // to XCD b % 8; its j = b / 8-th slot there is item j % (G run) of chunk
 // (j / (G run)) * 8 + b % 8.  So each XCD keeps whole GQA groups and walks
 // the pairs from the longest causal rows down in runs, and the work-groups of
@@ -57,22 +62,24 @@ constexpr int kWholeHeadPairs = 512;
 // scattered lists, miss L2 far more often than diffuse heads, and this keeps
 // the XCDs from all running them at the same time.  (Runs inside a chunk are
 // rotated, never reordered across chunks, so the walk from the longest rows
-// down is kept.)
+// down is kept.)  When a KV head's K and V fit in an XCD's L2
+// whatever the order, pair-major is the better schedule: it hands out the
+// longest items of all G heads first, so no head's long rows start late.
 __device__ __forceinline__ void
 attend_pair(int b, uint16_t* lds, uint32_t* list, Rows q, Rows k,
             const uint16_t* __restrict__ vt, const int32_t* __restrict__ row_ptr,
             const int32_t* __restrict__ col_idx, int n, int nb, int hkv, int G, int run,
-            float scale_log2, OutRows out)
+            bool pair_major, float scale_log2, OutRows out)
 {
     const int npairs = (nb + 1) >> 1;
     const int slot = b >> 3;
     const int per_chunk = G * run;
     const int chunk = (slot / per_chunk) * 8 + (b & 7);
     const int r = slot % per_chunk;
-    const int pair = (chunk / hkv) * run + r % run;
+    const int pair = (chunk / hkv) * run + (pair_major ? r / G : r % run);
     if (pair >= npairs) return;
     const int g = chunk % hkv;
-    const int h = g * G + (r / run + (b & 7)) % G;
+    const int h = g * G + ((pair_major ? r % G : r / run) + (b & 7)) % G;
     const int qb_hi = nb - 1 - 2 * pair;
     const int qb_lo = qb_hi - 1;                   // -1: no second block
 
@@ -386,7 +393,7 @@ __global__ void __launch_bounds__(kThreads)
 attend_kernel(Rows q, Rows k,
               const uint16_t* __restrict__ vt, const int32_t* __restrict__ row_ptr,
               const int32_t* __restrict__ col_idx, int n, int nb, int hkv, int G, int run,
-              float scale_log2, int per_xcd, int* __restrict__ ctr, OutRows out)
+              int pair_major, float scale_log2, int per_xcd, int* __restrict__ ctr, OutRows out)
 {
     __shared__ __attribute__((aligned(1024))) uint16_t lds[kStages * kStageBytes / 2];
     __shared__ uint32_t list[2 * kListWords + kMaxBlocks + 1];
@@ -408,8 +415,8 @@ attend_kernel(Rows q, Rows k,
         const int item = __builtin_amdgcn_readfirstlane(s_item);
         __syncthreads();
         if (item < 0) break;
-        attend_pair(item, lds, list, q, k, vt, row_ptr, col_idx, n, nb, hkv, G, run, scale_log2,
-                    out);
+        attend_pair(item, lds, list, q, k, vt, row_ptr, col_idx, n, nb, hkv, G, run,
+                    pair_major != 0, scale_log2, out);
     }
 }
 
@@ -447,7 +454,7 @@ attend_batch_kernel(const SeqDesc* __restrict__ seqs, const int* __restrict__ sl
         const int n = d.n;
         attend_pair(8 * (j - d.slot0) + (item & 7), lds, list, Rows{d.q, d.q_sh, d.q_st},
                     Rows{d.k, d.k_sh, d.k_st}, d.vt, d.row_ptr, d.col_idx, n, (n + kB - 1) / kB, hkv,
-                    G, d.run, scale_log2, OutRows{d.out, d.o_sh, d.o_st});
+                    G, d.run, d.pair_major != 0, scale_log2, OutRows{d.out, d.o_sh, d.o_st});
     }
 }
 
@@ -531,7 +538,7 @@ hipError_t launch_v_transpose(R v, int n, int hkv, uint16_t* vt, int* queue, hip
     return hipGetLastError();
 }
 
-void attend_plan(int n, int hq, int hkv, int* run_out, int* per_xcd_out)
+void attend_plan(int n, int hq, int hkv, int* run_out, int* per_xcd_out, int* pair_major_out)
 {
     const int nb = (n + kB - 1) / kB, G = hq / hkv;
     const int npairs = (nb + 1) / 2;
@@ -542,6 +549,7 @@ void attend_plan(int n, int hq, int hkv, int* run_out, int* per_xcd_out)
     const long long items = ((chunks + 7) / 8) * 8 * G * run;
     *run_out = run;
     *per_xcd_out = (int)(items / 8);
+    *pair_major_out = (long long)n * kD * 4 <= kPairMajorKvBytes;
 }
 
 namespace {
@@ -559,11 +567,12 @@ hipError_t launch_attend(Rows q, Rows k, const uint16_t* vt,
                          int* counters, OutRows out, hipStream_t stream)
 {
     const int nb = (n + kB - 1) / kB, G = hq / hkv;
-    int run, per_xcd;
-    attend_plan(n, hq, hkv, &run, &per_xcd);
+    int run, per_xcd, pair_major;
+    attend_plan(n, hq, hkv, &run, &per_xcd, &pair_major);
     const float scale_log2 = kLog2e / sqrtf((float)kD);
     hipLaunchKernelGGL(attend_kernel, dim3(resident_groups()), dim3(kThreads), 0, stream, q, k, vt,
-                       row_ptr, col_idx, n, nb, hkv, G, run, scale_log2, per_xcd, counters, out);
+                       row_ptr, col_idx, n, nb, hkv, G, run, pair_major, scale_log2, per_xcd,
+                       counters, out);
     return hipGetLastError();
 }
 

@@ -54,19 +54,23 @@ Layout make_layout(const Shape& s)
     L.part_up = take(part);
     L.jsd_kbar = take(hkv * nb * kD * sizeof(float));      // JSD router only
     L.jsd_qbar = take(hq * kD * sizeof(float));
-    L.seg_m = take(hq * kRouteSegs * kB * sizeof(float));
-    L.seg_l = take(hq * kRouteSegs * kB * sizeof(double));
-    L.row_mx = take(hq * kB * sizeof(float));
-    L.row_inv = take(hq * kB * sizeof(float));
-    L.tile_sums = take(hq * 4 * nb * sizeof(float));
+    // the multi-launch route reductions' scratch (unused up to kRouteSmall blocks)
+    const size_t rs = nb > (size_t)kRouteSmall ? 1 : 0;
+    L.seg_m = take(rs * hq * kRouteSegs * kB * sizeof(float));
+    L.seg_l = take(rs * hq * kRouteSegs * kB * sizeof(double));
+    L.row_mx = take(rs * hq * kB * sizeof(float));
+    L.row_inv = take(rs * hq * kB * sizeof(float));
+    L.tile_sums = take(rs * hq * 4 * nb * sizeof(float));
     L.route_end = o;
     o = 0;
     L.qbar = take(hq * nb * kD * sizeof(float));
     L.kbar = take(hkv * nb * kD * sizeof(float));
     L.abar = take(hq * tri * sizeof(float));
-    L.hist_mass = take(hq * kValPasses * kValBins * sizeof(unsigned long long));
-    L.hist_count = take(hq * kRadixPasses * kFlatBins * sizeof(uint32_t));
-    L.pass_ctr = take(hq * kRadixPasses * sizeof(uint32_t));
+    // the multi-launch radix select's histograms (unused for small maps)
+    const size_t rx = tri > (size_t)kRadixSmall ? 1 : 0;
+    L.hist_mass = take(rx * hq * kValPasses * kValBins * sizeof(unsigned long long));
+    L.hist_count = take(rx * hq * kRadixPasses * kFlatBins * sizeof(uint32_t));
+    L.pass_ctr = take(rx * hq * kRadixPasses * sizeof(uint32_t));
     L.state = take(hq * sizeof(PeState));
     L.bitmap = take(hq * 2 * nb);
     L.select_end = o;
@@ -282,7 +286,7 @@ struct BatchGroup {
 };
 struct BatchLayout {
     std::vector<BatchGroup> groups;
-    std::vector<int> run, per_xcd, slot0;   // per batch entry
+    std::vector<int> run, per_xcd, slot0, pair_major;   // per batch entry
     size_t table = 0, slot_seq = 0, counters = 0, total = 0;
     int total_per_xcd = 0;
 };
@@ -339,10 +343,11 @@ BatchLayout make_batch_layout(int batch, LenOf len_of, int hq, int hkv)
     B.run.assign(batch, 0);
     B.per_xcd.assign(batch, 0);
     B.slot0.assign(batch, 0);
+    B.pair_major.assign(batch, 0);
     for (int b = 0; b < batch; ++b) {
         const int n = len_of(b);
         if (n == 0) continue;
-        attend_plan(n, hq, hkv, &B.run[b], &B.per_xcd[b]);
+        attend_plan(n, hq, hkv, &B.run[b], &B.per_xcd[b], &B.pair_major[b]);
         B.slot0[b] = B.total_per_xcd;
         B.total_per_xcd += B.per_xcd[b];
     }
@@ -452,6 +457,7 @@ int run_prefill_batch_fused(const crisp_seq* seqs, int batch, const crisp_stride
             d.run = B.run[b];
             d.slot0 = B.slot0[b];
             d.per_xcd = B.per_xcd[b];
+            d.pair_major = B.pair_major[b];
             live[b] = 1;
         }
     }

@@ -72,6 +72,28 @@ __device__ __forceinline__ void wave_sum_n(double (&x)[N])
     }
 }
 
+// Float wave sums for short reductions (one value per lane, a 64-term sum)
+// without a round trip through the LDS crossbar for every step: lanes xor 1
+// and xor 2 by DPP quad permutes, xor 4, 8 and 16 by ds_swizzle (bit mode,
+// within 32 lanes), xor 32 by the lane-half swap.  Every lane ends with the
+// total; N independent sums run interleaved.  (The order of additions is
+// fixed, so the same inputs give the same bits in every kernel using it.)
+template <int N>
+__device__ __forceinline__ void wave_sum_fast_n(float (&x)[N])
+{
+    for (int j = 0; j < N; ++j)
+        x[j] += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x[j]), 0xB1, 0xF, 0xF, true));
+    for (int j = 0; j < N; ++j)
+        x[j] += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x[j]), 0x4E, 0xF, 0xF, true));
+    for (int j = 0; j < N; ++j)
+        x[j] += __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(x[j]), 0x101f));
+    for (int j = 0; j < N; ++j)
+        x[j] += __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(x[j]), 0x201f));
+    for (int j = 0; j < N; ++j)
+        x[j] += __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(x[j]), 0x401f));
+    for (int j = 0; j < N; ++j) x[j] += swap_half(x[j]);
+}
+
 __device__ __forceinline__ int wave_sum(int x)
 {
     for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);

@@ -137,12 +137,12 @@ struct SeqDesc {
     const int32_t* row_ptr;
     const int32_t* col_idx;
     long long q_sh, q_st, k_sh, k_st, o_sh, o_st;
-    int n, run, slot0, per_xcd;
+    int n, run, slot0, per_xcd, pair_major;
 };
 
-// Work-queue plan of one sequence's attention: pair-run length and slots per
-// XCD queue.
-void attend_plan(int n, int hq, int hkv, int* run, int* per_xcd);
+// Work-queue plan of one sequence's attention: pair-run length, slots per
+// XCD queue, and the order of a chunk's items (1: pair-major, 0: head-major).
+void attend_plan(int n, int hq, int hkv, int* run, int* per_xcd, int* pair_major);
 
 // Copies `count` host descriptors into the device table at table[first ..]
 // and marks their queue slots in slot_seq (kernel arguments only: no host

@@ -300,20 +300,21 @@ tile_mass_kernel(const float* __restrict__ part_m, const float* __restrict__ par
     const int lane = tid & 63;
     const int t = blockIdx.x * 16 + (tid >> 6);
     if (t >= nb) return;
-    double sv = 0.0, slo0 = 0.0, sup0 = 0.0, slo1 = 0.0, sup1 = 0.0;
+    float sv = 0.f, slo0 = 0.f, sup0 = 0.f, slo1 = 0.f, sup1 = 0.f;
     for (int i = lane; i < R; i += 64) {
         const size_t o = ((size_t)h * nb + t) * kB + i;
         const float mt = part_m[o];
         if (mt == -INFINITY) continue;
         const float wt = exp2f(mt - mx[i]) * inv[i];
         const float lo = part_lo[o] * wt, up = part_up[o] * wt;
-        sv += (double)lo + (double)up;
+        sv += lo + up;
         const int ei = nb - 1 - (q0 + i) / kB;
         if (ei == 0) { slo0 += lo; sup0 += up; }
         else { slo1 += lo; sup1 += up; }
     }
-    double r5[5] = {sv, slo0, sup0, slo1, sup1};
-    wave_sum_n(r5);
+    // 128-term sums: float, reduced without the LDS crossbar
+    float r5[5] = {sv, slo0, sup0, slo1, sup1};
+    wave_sum_fast_n(r5);
     if (lane == 0) {
         p_v[(size_t)h * nb + t] = (float)(r5[0] / R);
         float* ts = tile_sums + (size_t)h * 4 * nb;
@@ -442,17 +443,18 @@ route_small_kernel(const float* __restrict__ part_m, const float* __restrict__ p
                     vup[b][x] = part_up[o];
                 }
             }
-        // the five sums of each of the four tiles, reduced together
-        double r[20];
+        // the five sums of each of the four tiles, reduced together (as
+        // tile_mass_kernel: float, the same order)
+        float r[20];
         for (int b = 0; b < 4; ++b) {
-            double sv = 0.0, slo0 = 0.0, sup0 = 0.0, slo1 = 0.0, sup1 = 0.0;
+            float sv = 0.f, slo0 = 0.f, sup0 = 0.f, slo1 = 0.f, sup1 = 0.f;
             for (int x = 0; x < 2; ++x) {
                 const int i = lane + 64 * x;
                 const float mt = vm[b][x];
                 if (i >= R || mt == -INFINITY) continue;
                 const float wt = exp2f(mt - mx[i]) * inv[i];
                 const float lo = vlo[b][x] * wt, up = vup[b][x] * wt;
-                sv += (double)lo + (double)up;
+                sv += lo + up;
                 const int ei = nb - 1 - (q0 + i) / kB;
                 if (ei == 0) { slo0 += lo; sup0 += up; }
                 else { slo1 += lo; sup1 += up; }
@@ -463,7 +465,7 @@ route_small_kernel(const float* __restrict__ part_m, const float* __restrict__ p
             r[5 * b + 3] = slo1;
             r[5 * b + 4] = sup1;
         }
-        wave_sum_n(r);
+        wave_sum_fast_n(r);
         for (int b = 0; b < 4; ++b) {
             const int t = t4 + 16 * b;
             if (t >= nb) break;
@@ -612,9 +614,12 @@ hipError_t launch_route(QK q, QK k, int n, int hq, int hkv,
     const int nb = (n + kB - 1) / kB;
     const int G = hq / hkv;
     const float scale_log2 = kLog2e / sqrtf((float)kD);
-    // enough work-groups to fill 256 CUs a few times over
+    // about one work-group per CU, each walking its tiles with the next
+    // tile's copy in flight (at 131072 tokens 32 tiles per work-group,
+    // 0.210 against 0.225 ms with a quarter of that; at 8192 tokens two
+    // tiles, 0.030 against 0.034 ms)
     int tiles_per_wg = 1;
-    while (tiles_per_wg < 8 && (size_t)((nb + 2 * tiles_per_wg - 1) / (2 * tiles_per_wg)) * hkv >= 1024)
+    while (tiles_per_wg < 64 && (size_t)((nb + 2 * tiles_per_wg - 1) / (2 * tiles_per_wg)) * hkv * ((G + 3) / 4) >= 256)
         tiles_per_wg *= 2;
     dim3 grid((nb + tiles_per_wg - 1) / tiles_per_wg, hkv * ((G + 3) / 4));
     if (n % kB == 0)

@@ -427,19 +427,40 @@ pe_logits_kernel(const float* __restrict__ qbar, const float* __restrict__ kbar,
     if (live)
         for (int r = 0; r < 16; ++r) rows[(8 * (r >> 2) + 4 * hi + (r & 3)) * kP + kb] = acc[r] * scale_log2;
     __syncthreads();
-    for (int rl = w; rl < 32; rl += 4) {
-        const int qb = 32 * qt + rl;
-        if (qb >= nb) break;
-        const float* row = rows + rl * kP;
+    // the wavefront's eight rows (rl = w, w + 4, ..) with their wave
+    // reductions interleaved: each row's max and sum use the butterflies of
+    // wave_max / wave_sum, so the bits match pe_softmax_kernel's
+    float m8[8];
+    double l8[8];
+    for (int j = 0; j < 8; ++j) {
+        const int qb = 32 * qt + w + 4 * j;
+        const float* row = rows + (w + 4 * j) * kP;
         float m = -INFINITY;
-        for (int k2 = lane; k2 <= qb; k2 += 64) m = fmaxf(m, row[k2]);
-        m = wave_max(m);
+        if (qb < nb)
+            for (int k2 = lane; k2 <= qb; k2 += 64) m = fmaxf(m, row[k2]);
+        m8[j] = m;
+    }
+    for (int o = 32; o > 0; o >>= 1) {
+        float y[8];
+        for (int j = 0; j < 8; ++j) y[j] = __shfl_xor(m8[j], o);
+        for (int j = 0; j < 8; ++j) m8[j] = fmaxf(m8[j], y[j]);
+    }
+    for (int j = 0; j < 8; ++j) {
+        const int qb = 32 * qt + w + 4 * j;
+        const float* row = rows + (w + 4 * j) * kP;
         double l = 0.0;
-        for (int k2 = lane; k2 <= qb; k2 += 64) l += (double)exp2f(row[k2] - m);
-        l = wave_sum(l);
-        const double inv = 1.0 / (l * (double)nb);
+        if (qb < nb)
+            for (int k2 = lane; k2 <= qb; k2 += 64) l += (double)exp2f(row[k2] - m8[j]);
+        l8[j] = l;
+    }
+    wave_sum_n(l8);
+    for (int j = 0; j < 8; ++j) {
+        const int qb = 32 * qt + w + 4 * j;
+        if (qb >= nb) break;
+        const float* row = rows + (w + 4 * j) * kP;
+        const double inv = 1.0 / (l8[j] * (double)nb);
         float* out = abar + base + tri(qb);
-        for (int k2 = lane; k2 <= qb; k2 += 64) out[k2] = (float)((double)exp2f(row[k2] - m) * inv);
+        for (int k2 = lane; k2 <= qb; k2 += 64) out[k2] = (float)((double)exp2f(row[k2] - m8[j]) * inv);
     }
 }
 
