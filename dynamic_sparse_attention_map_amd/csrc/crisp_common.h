@@ -94,6 +94,50 @@ __device__ __forceinline__ void wave_sum_fast_n(float (&x)[N])
     for (int j = 0; j < N; ++j) x[j] += swap_half(x[j]);
 }
 
+// Inclusive prefix sums over the 64 lanes of a wavefront (every lane
+// active).  Within each row of 16 lanes, DPP row shifts by 1, 2, 4 and 8
+// (lanes shifted in from outside the row add 0); then the row totals are
+// carried across rows by DPP row broadcasts: lane 15 of each row to the
+// next row (written only into rows 1 and 3), then lane 31 to rows 2 and 3.
+template <int Ctrl, int RowMask>
+__device__ __forceinline__ uint32_t dpp_or_zero(uint32_t x)
+{
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, Ctrl, RowMask, 0xF, false);
+}
+
+template <int Ctrl, int RowMask>
+__device__ __forceinline__ unsigned long long dpp_or_zero(unsigned long long x)
+{
+    const uint32_t lo = dpp_or_zero<Ctrl, RowMask>((uint32_t)x);
+    const uint32_t hi = dpp_or_zero<Ctrl, RowMask>((uint32_t)(x >> 32));
+    return ((unsigned long long)hi << 32) | lo;
+}
+
+template <typename T>
+__device__ __forceinline__ T wave_scan_incl(T x)
+{
+    x += dpp_or_zero<0x111, 0xF>(x);     // row_shr:1
+    x += dpp_or_zero<0x112, 0xF>(x);     // row_shr:2
+    x += dpp_or_zero<0x114, 0xF>(x);     // row_shr:4
+    x += dpp_or_zero<0x118, 0xF>(x);     // row_shr:8
+    x += dpp_or_zero<0x142, 0xA>(x);     // row_bcast:15
+    x += dpp_or_zero<0x143, 0xC>(x);     // row_bcast:31
+    return x;
+}
+
+// Lane 63's value, in every lane (a wave-uniform result).
+__device__ __forceinline__ uint32_t last_lane(uint32_t x)
+{
+    return (uint32_t)__builtin_amdgcn_readlane((int)x, 63);
+}
+
+__device__ __forceinline__ unsigned long long last_lane(unsigned long long x)
+{
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)x, 63);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(x >> 32), 63);
+    return ((unsigned long long)hi << 32) | lo;
+}
+
 __device__ __forceinline__ int wave_sum(int x)
 {
     for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);

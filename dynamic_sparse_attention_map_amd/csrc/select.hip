@@ -1,6 +1,6 @@
 // Index selection and block-list expansion kernels.
 //
-//   vs_select_kernel   VS budget per direction: the sink-aware noise floor
+//   vs_select_*        VS budget per direction: the sink-aware noise floor
 //                      (Alg. 3; Eq. 3-4), the median floor
 //                      (Appendix H) or FlexPrefill's cumulative rule (Alg. 6),
 //                      with stream compaction
@@ -12,6 +12,9 @@
 //   expand_*_kernel    per-(head, query block) key-block lists (the block
 //                      mask M_S of Eq. 1), CSR with per-head worst-case bases:
 //                      row lengths, per-head scan, fill
+//   select_small_kernel  for N_b <= 128, everything after the pooled map in
+//                      one work-group per head: a VS head's budgets or a PE
+//                      head's cut-off, then its lists
 //
 // Decisions are taken in float in the order the paper writes them; the
 // pooled masses are summed in 2^-62 fixed point, which is exact and
@@ -34,19 +37,11 @@ __device__ __forceinline__ size_t tri(int qb) { return (size_t)qb * (qb + 1) / 2
 __device__ int block_scan_1024(int v, int* wsum, int* total)
 {
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    int x = v;
-    for (int o = 1; o < 64; o <<= 1) {
-        const int y = __shfl_up(x, o);
-        if (lane >= o) x += y;
-    }
+    const int x = (int)wave_scan_incl((uint32_t)v);
     if (lane == 63) wsum[w] = x;
     __syncthreads();
     if (w == 0) {
-        int s = (lane < 16) ? wsum[lane] : 0;
-        for (int o = 1; o < 16; o <<= 1) {
-            const int y = __shfl_up(s, o);
-            if (lane >= o) s += y;
-        }
+        const int s = (int)wave_scan_incl((uint32_t)((lane < 16) ? wsum[lane] : 0));
         if (lane < 16) wsum[lane] = s;
     }
     __syncthreads();
@@ -112,29 +107,36 @@ constexpr int kRankClip = 256;      // largest N_b whose k_min clip ranks all en
 // then clip(k, k_min, N_b) with top-k by (p desc, j asc) for rules 0 and 1
 // (N_b <= 2 keeps every block under them) and, for rule 2, at least k_min
 // entries of the same order.  Values are compared in float.
-__global__ void __launch_bounds__(1024)
-vs_select_kernel(const uint8_t* __restrict__ pattern, const float* __restrict__ p_v,
-                 const float* __restrict__ p_s, int nb, VsRule vr,
-                 int32_t* __restrict__ sel_v, int32_t* __restrict__ sel_s,
-                 int32_t* __restrict__ counts, uint8_t* __restrict__ bitmap)
-{
-    __shared__ int wsum[16];
-    __shared__ double wsum_d[16];
-    __shared__ float best_v[2][16];
-    __shared__ int best_i[2][16];
-    __shared__ int s_kk;
-    __shared__ uint8_t flag[kMaxBlocks];
-    __shared__ unsigned long long keys[kMaxBlocks];
+// LDS of one direction's budget selection; keys hold at least the power
+// of two at or above N_b.
+template <int KeyCap>
+struct VsLds {
+    int wsum[16];
+    double wsum_d[16];
+    float best_v[2][16];
+    int best_i[2][16];
+    int kk;
+    uint8_t flag[kMaxBlocks];
+    unsigned long long keys[KeyCap];
+};
 
-    const int h = blockIdx.x, dir = blockIdx.y, tid = threadIdx.x;
+// One direction of VS head h (p: its p_v or p_s row), by every thread of a
+// 1024-thread block: the kept blocks, ascending, into sel, their number into
+// counts[h * 3 + dir], and a 0/1 flag per block into bm (global or LDS).
+template <int KeyCap>
+__device__ void vs_select_dir(VsLds<KeyCap>& L, int h, int dir, const float* __restrict__ p, int nb,
+                              const VsRule& vr, int32_t* __restrict__ sel,
+                              int32_t* __restrict__ counts, uint8_t* bm)
+{
+    int* wsum = L.wsum;
+    double* wsum_d = L.wsum_d;
+    auto& best_v = L.best_v;
+    auto& best_i = L.best_i;
+    int& s_kk = L.kk;
+    uint8_t* flag = L.flag;
+    unsigned long long* keys = L.keys;
+    const int tid = threadIdx.x;
     const int lane = tid & 63, w = tid >> 6;
-    if (!pattern[h]) {
-        if (tid == 0) counts[h * 3 + dir] = 0;
-        return;
-    }
-    const float* p = (dir ? p_s : p_v) + (size_t)h * nb;
-    int32_t* sel = (dir ? sel_s : sel_v) + (size_t)h * nb;
-    uint8_t* bm = bitmap + ((size_t)h * 2 + dir) * nb;
     int np2 = 1;
     while (np2 < nb) np2 <<= 1;
 
@@ -272,6 +274,23 @@ vs_select_kernel(const uint8_t* __restrict__ pattern, const float* __restrict__ 
         if (flag[j]) sel[pos++] = j;
     }
     if (tid == 0) counts[h * 3 + dir] = kept;
+}
+
+__global__ void __launch_bounds__(1024)
+vs_select_kernel(const uint8_t* __restrict__ pattern, const float* __restrict__ p_v,
+                 const float* __restrict__ p_s, int nb, VsRule vr,
+                 int32_t* __restrict__ sel_v, int32_t* __restrict__ sel_s,
+                 int32_t* __restrict__ counts, uint8_t* __restrict__ bitmap)
+{
+    __shared__ VsLds<kMaxBlocks> L;
+    const int h = blockIdx.x, dir = blockIdx.y;
+    if (!pattern[h]) {
+        if (threadIdx.x == 0) counts[h * 3 + dir] = 0;
+        return;
+    }
+    vs_select_dir(L, h, dir, (dir ? p_s : p_v) + (size_t)h * nb, nb, vr,
+                  (dir ? sel_s : sel_v) + (size_t)h * nb, counts,
+                  bitmap + ((size_t)h * 2 + dir) * nb);
 }
 
 // grid (hq), 1024 threads: clear the head's radix histograms and pass
@@ -635,52 +654,187 @@ __device__ void radix_resolve(int pass, size_t total, const PeState& st, const u
     }
 }
 
-// grid hq, 256 threads: the whole cut-off of one head in one work-group,
-// for maps of at most kRadixSmall entries (N_b <= 128), read once into LDS.
-// The same five passes, digits and fixed-point masses as pe_radix_kernel
-// (so the same result), with the histograms in LDS only; it also seeds the
-// state as pe_init_kernel does, which it replaces.  (Beyond this size the
-// passes over one work-group per head take longer than the multi-launch
-// path.)
+// The gamma cut-off of one PE head whose triangular map (at most
+// kRadixSmall entries, N_b <= 128) starts at `base`, by one 1024-thread
+// block over an LDS copy of the map.  The sorted order, the fixed-point
+// masses and the tie rule define the cut-off uniquely, so this finds the
+// same (key_star, flat_star, K*) as the multi-launch passes, by a cheaper
+// route for small maps: four passes over 8-bit digits of the key, each
+// wavefront counting into its own LDS copy of the 256-bin histogram (so
+// atomics contend only inside a wavefront), and, only when the cut-off key
+// is shared by entries that are not all kept, one block scan for the tie
+// (entry order in the triangular map is flat order).  Every thread calls it
+// and gets the final state; the map stays in L.vals.
+constexpr int kSmallBins = 256;               // 8-bit digits
+constexpr int kSmallPasses = 4;
+constexpr int kFoldRounds = 4;
 
-__global__ void __launch_bounds__(256)
-pe_radix_small_kernel(const uint8_t* __restrict__ pattern, int nb, float gamma,
-                      const float* __restrict__ abar, PeState* __restrict__ state)
+struct SmallCutLds {
+    float vals[kRadixSmall];
+    uint32_t wcnt[16][kSmallBins];              // per wavefront
+    unsigned long long wmass[16][kSmallBins];
+    uint32_t pcnt[4][kSmallBins];               // sums of four copies each
+    unsigned long long pmass[4][kSmallBins];
+    PeState st;
+    uint32_t bin_count;                         // entries in the resolved bin
+    int scan[16];
+};
+
+__device__ PeState pe_cut_small(SmallCutLds& L, const float* __restrict__ base, int nb, float gamma)
 {
-    __shared__ uint32_t cnt[kFlatBins];
-    __shared__ unsigned long long mass[kValBins];
-    __shared__ unsigned long long wsum_m[4];
-    __shared__ uint32_t wsum_c[4];
-    __shared__ PeState s_st;
-    __shared__ float vals[kRadixSmall];
-    const int h = blockIdx.x, tid = threadIdx.x;
-    if (tid == 0) {
-        PeState st = {};
-        st.need = (unsigned long long)((double)gamma * kFix);
-        st.done = pattern[h] ? 1u : 0u;
-        s_st = st;
-    }
-    const size_t total = tri(nb);
-    const float* base = abar + (size_t)h * total;
-    if (!pattern[h])
-        for (size_t e = tid; e < total; e += 256) vals[e] = base[e];
-    __syncthreads();
-    for (int pass = 0; pass < kRadixPasses; ++pass) {
-        const PeState st = s_st;
-        if (st.done) break;
-        const int bins = 1 << pass_bits(pass);
-        for (int i = tid; i < bins; i += 256) {
-            cnt[i] = 0u;
-            if (pass < kValPasses) mass[i] = 0ull;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int total = nb * (nb + 1) / 2;
+    for (int e = tid; e < total; e += 1024) L.vals[e] = base[e];
+    PeState st = {};
+    st.need = (unsigned long long)((double)gamma * kFix);
+    // nothing reaches a zero need: only the always-kept blocks (K* = 0)
+    if (st.need == 0) return st;
+    if (tid == 0) L.st = st;
+    for (int pass = 0; pass < kSmallPasses; ++pass) {
+        const int shift = 24 - 8 * pass;
+        for (int i = lane; i < kSmallBins; i += 64) {
+            L.wcnt[w][i] = 0u;
+            L.wmass[w][i] = 0ull;
         }
         __syncthreads();
-        for (size_t e = tid; e < total; e += 256)
-            radix_add(pass, nb, st, e, vals[e], cnt, mass);
+        st = L.st;
+        if (st.done) break;
+        // The entries whose higher digits match the ones resolved so far.
+        // The values of a map span few binades, so in the first pass most
+        // lanes of a wavefront share one of a few digits: there the
+        // wavefront first folds up to kFoldRounds groups of lanes with equal
+        // digits, one lane adding each group's count and mass (its own
+        // histogram copy, so a plain update), and only the remaining lanes
+        // add atomically.  (The later passes' digits are mantissa bits,
+        // rarely shared: folding there cost more than it saved.)  Integer
+        // sums: the same totals in any order.
+        for (int e0 = 64 * w; e0 < total; e0 += 1024) {
+            const int e = e0 + lane;
+            bool act = false;
+            uint32_t d = 0;
+            unsigned long long fx = 0;
+            if (e < total) {
+                const float v = L.vals[e];
+                const uint32_t key = ~__float_as_uint(v);
+                act = pass == 0 || (key >> (shift + 8)) == st.key_prefix;
+                d = (key >> shift) & (kSmallBins - 1);
+                fx = to_fix(v);
+            }
+            unsigned long long pend = pass == 0 ? __ballot(act) : 0ull;
+            for (int r = 0; r < kFoldRounds && pend; ++r) {
+                const int leader = __builtin_ctzll(pend);
+                const uint32_t ld = (uint32_t)__builtin_amdgcn_readlane((int)d, leader);
+                const bool mt = act && d == ld;
+                const unsigned long long mm = __ballot(mt);
+                const unsigned long long sum = last_lane(wave_scan_incl(mt ? fx : 0ull));
+                if (lane == leader) {
+                    L.wcnt[w][ld] += (uint32_t)__popcll(mm);
+                    L.wmass[w][ld] += sum;
+                }
+                act = act && !mt;
+                pend &= ~mm;
+            }
+            if (act) {
+                atomicAdd(&L.wcnt[w][d], 1u);
+                atomicAdd(&L.wmass[w][d], fx);
+            }
+        }
         __syncthreads();
-        radix_resolve(pass, total, st, cnt, mass, wsum_c, wsum_m, &s_st);
+        {
+            const int bin = tid & (kSmallBins - 1), part = tid >> 8;
+            uint32_t c = 0;
+            unsigned long long m = 0;
+            for (int x = 4 * part; x < 4 * part + 4; ++x) {
+                c += L.wcnt[x][bin];
+                m += L.wmass[x][bin];
+            }
+            L.pcnt[part][bin] = c;
+            L.pmass[part][bin] = m;
+        }
         __syncthreads();
+        if (w == 0) {
+            // lane l holds bins 4l .. 4l + 3; scan the lanes' totals
+            uint32_t c[4], c_lane = 0;
+            unsigned long long m[4], m_lane = 0;
+            for (int j = 0; j < 4; ++j) {
+                const int bin = 4 * lane + j;
+                c[j] = (L.pcnt[0][bin] + L.pcnt[1][bin]) + (L.pcnt[2][bin] + L.pcnt[3][bin]);
+                m[j] = (L.pmass[0][bin] + L.pmass[1][bin]) + (L.pmass[2][bin] + L.pmass[3][bin]);
+                c_lane += c[j];
+                m_lane += m[j];
+            }
+            const uint32_t c_incl = wave_scan_incl(c_lane);
+            const unsigned long long m_incl = wave_scan_incl(m_lane);
+            const unsigned long long m_all = last_lane(m_incl);
+            uint32_t c_before = c_incl - c_lane;
+            unsigned long long m_before = m_incl - m_lane;
+            if (m_all < st.need) {
+                // (first pass only) the whole map never reaches gamma: keep
+                // every causal entry
+                if (lane == 0) {
+                    PeState nx = st;
+                    nx.key_star = 0xffffffffu;
+                    nx.flat_star = 0xffffffffu;
+                    nx.kstar = (uint32_t)total;
+                    nx.done = 1u;
+                    L.st = nx;
+                }
+            } else if (m_before < st.need && m_incl >= st.need) {
+                for (int j = 0; j < 4; ++j) {
+                    const unsigned long long incl = m_before + m[j];
+                    if (m_before < st.need && incl >= st.need) {
+                        PeState nx = st;
+                        nx.need = st.need - m_before;
+                        nx.before = st.before + c_before;
+                        nx.key_prefix = (st.key_prefix << 8) | (uint32_t)(4 * lane + j);
+                        L.st = nx;
+                        L.bin_count = c[j];
+                    }
+                    m_before = incl;
+                    c_before += c[j];
+                }
+            }
+        }
     }
-    if (tid == 0) state[h] = s_st;
+    __syncthreads();
+    st = L.st;
+    if (st.done) return st;
+    // key_prefix is now the whole cut-off key: take just enough of its
+    // equal-valued entries, in flat order
+    const uint32_t key_star = st.key_prefix;
+    const unsigned long long tf = to_fix(__uint_as_float(~key_star));
+    const unsigned long long ties = (st.need + tf - 1) / tf;
+    const uint32_t cnt = L.bin_count;
+    st.key_star = key_star;
+    st.tfix = tf;
+    st.done = 1u;
+    if (ties >= cnt) {
+        st.flat_star = 0xffffffffu;
+        st.kstar = st.before + cnt;
+        return st;
+    }
+    st.tie_need = (uint32_t)ties;
+    st.kstar = st.before + (uint32_t)ties;
+    const int per = (total + 1023) / 1024;
+    const int e0 = min(total, tid * per), e1 = min(total, e0 + per);
+    int mine = 0;
+    for (int e = e0; e < e1; ++e) mine += ~__float_as_uint(L.vals[e]) == key_star;
+    int all;
+    const int excl = block_scan_1024(mine, L.scan, &all);    // ends with a barrier
+    if (excl < (int)ties && excl + mine >= (int)ties) {
+        int seen = excl;
+        for (int e = e0; e < e1; ++e) {
+            if (~__float_as_uint(L.vals[e]) != key_star || ++seen < (int)ties) continue;
+            int qb = (int)((sqrtf(8.0f * (float)e + 1.0f) - 1.0f) * 0.5f);
+            while (tri(qb + 1) <= (size_t)e) ++qb;
+            while (tri(qb) > (size_t)e) --qb;
+            L.st.flat_star = (uint32_t)qb * (uint32_t)nb + (uint32_t)(e - (int)tri(qb));
+            break;
+        }
+    }
+    __syncthreads();
+    st.flat_star = st.flat_prefix = L.st.flat_star;
+    return st;
 }
 
 // grid (ceil(tri(Nb) / kRadixChunk), hq), 256 threads
@@ -876,23 +1030,19 @@ expand_fill_kernel(const uint8_t* __restrict__ pattern, int nb, const uint8_t* _
 }
 
 
-// grid hq, 1024 threads: expand_count, expand_scan and expand_fill for one
-// head in one work-group (N_b <= kExpandSmall), the row lengths kept in LDS.
-// The same rows, offsets and K* as the three kernels.
-constexpr int kExpandSmall = 128;
+// The block lists of head h under `rule` by one 1024-thread block
+// (N_b <= kSelectSmall): the row lengths, their exclusive scan into
+// absolute offsets (head h's lists start at h N_b (N_b + 1) / 2), then the
+// ascending key blocks of every row; K* (0 for VS heads) into counts.  The
+// same rows, offsets and K* as expand_count, expand_scan and expand_fill.
+constexpr int kSelectSmall = 128;
+static_assert(kSelectSmall * (kSelectSmall + 1) / 2 == kRadixSmall, "one small-map bound");
 
-__global__ void __launch_bounds__(1024)
-expand_small_kernel(const uint8_t* __restrict__ pattern, int nb, const uint8_t* __restrict__ bitmap,
-                    const float* __restrict__ abar, const PeState* __restrict__ state,
-                    int32_t* __restrict__ row_ptr, int32_t* __restrict__ col_idx,
-                    int32_t* __restrict__ counts)
+__device__ void expand_head(const RowRule& rule, int h, int nb, uint32_t kstar,
+                            int32_t* __restrict__ row_ptr, int32_t* __restrict__ col_idx,
+                            int32_t* __restrict__ counts, int* start, int* wsum)
 {
-    __shared__ uint8_t bmv[kExpandSmall];
-    __shared__ uint8_t bms[kExpandSmall];
-    __shared__ int start[kExpandSmall];
-    __shared__ int wsum[16];
-    const int h = blockIdx.x, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-    const RowRule rule = load_rule(pattern, nb, h, bitmap, abar, state, bmv, bms);
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     for (int qb = w; qb < nb; qb += 16) {
         int c = 0;
         for (int kb0 = 0; kb0 <= qb; kb0 += 64) c += __popcll(__ballot(rule.member(qb, kb0 + lane)));
@@ -918,7 +1068,7 @@ expand_small_kernel(const uint8_t* __restrict__ pattern, int nb, const uint8_t* 
     }
     if (tid == 0) {
         rp[nb] = (int32_t)(base + total);
-        counts[h * 3 + 2] = pattern[h] ? 0 : (int32_t)state[h].kstar;
+        counts[h * 3 + 2] = rule.vs ? 0 : (int32_t)kstar;
     }
     __syncthreads();
     const unsigned long long below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
@@ -931,6 +1081,62 @@ expand_small_kernel(const uint8_t* __restrict__ pattern, int nb, const uint8_t* 
             pos += __popcll(bal);
         }
     }
+}
+
+struct SelectSmallLds {
+    union {
+        SmallCutLds cut;
+        VsLds<kSelectSmall> vs;
+    } u;
+    uint8_t bmv[kSelectSmall];
+    uint8_t bms[kSelectSmall];
+    int start[kSelectSmall];
+    int wsum[16];
+};
+
+// grid hq, 1024 threads, N_b <= kSelectSmall: the whole selection of one
+// head in one work-group, after routing and the pooled map (pe_logits):
+// a VS head's two budget selections (as vs_select_kernel) or a PE head's
+// gamma cut-off (pe_cut_small; its state also goes to state[h]), then the
+// head's block lists (expand_head) from the LDS copies of the bitmaps or of
+// the map.  The same outputs as the multi-launch path.
+__global__ void __launch_bounds__(1024)
+select_small_kernel(const uint8_t* __restrict__ pattern, const float* __restrict__ p_v,
+                    const float* __restrict__ p_s, int nb, VsRule vr, float gamma,
+                    const float* __restrict__ abar, int32_t* __restrict__ sel_v,
+                    int32_t* __restrict__ sel_s, int32_t* __restrict__ counts,
+                    PeState* __restrict__ state, int32_t* __restrict__ row_ptr,
+                    int32_t* __restrict__ col_idx)
+{
+    __shared__ SelectSmallLds L;
+    const int h = blockIdx.x;
+    RowRule rule;
+    rule.vs = pattern[h] != 0;
+    rule.nb = nb;
+    rule.bmv = L.bmv;
+    rule.bms = L.bms;
+    rule.arow = L.u.cut.vals;
+    rule.key_star = rule.flat_star = 0;
+    uint32_t kstar = 0;
+    if (rule.vs) {
+        vs_select_dir(L.u.vs, h, 0, p_v + (size_t)h * nb, nb, vr, sel_v + (size_t)h * nb, counts,
+                      L.bmv);
+        __syncthreads();
+        vs_select_dir(L.u.vs, h, 1, p_s + (size_t)h * nb, nb, vr, sel_s + (size_t)h * nb, counts,
+                      L.bms);
+    } else {
+        const PeState st = pe_cut_small(L.u.cut, abar + (size_t)h * tri(nb), nb, gamma);
+        if (threadIdx.x == 0) {
+            state[h] = st;
+            counts[h * 3] = 0;
+            counts[h * 3 + 1] = 0;
+        }
+        rule.key_star = st.key_star;
+        rule.flat_star = st.flat_star;
+        kstar = st.kstar;
+    }
+    __syncthreads();
+    expand_head(rule, h, nb, kstar, row_ptr, col_idx, counts, L.start, L.wsum);
 }
 
 }  // namespace
@@ -946,12 +1152,11 @@ hipError_t launch_select(R q, R k, const uint8_t* pattern,
     hipError_t e;
 #define CRISP_CHECK_LAUNCH() \
     if ((e = hipGetLastError()) != hipSuccess) return e
-    hipLaunchKernelGGL(vs_select_kernel, dim3(hq, 2), dim3(1024), 0, stream, pattern, p_v, p_s, nb,
-                       vs, sel_v, sel_s, sel_counts, s.bitmap);
-    CRISP_CHECK_LAUNCH();
-    const long long tri_nb = (long long)nb * (nb + 1) / 2;
-    const bool small_map = tri_nb <= kRadixSmall;
-    if (!small_map) {
+    const bool small = nb <= kSelectSmall;
+    if (!small) {
+        hipLaunchKernelGGL(vs_select_kernel, dim3(hq, 2), dim3(1024), 0, stream, pattern, p_v, p_s,
+                           nb, vs, sel_v, sel_s, sel_counts, s.bitmap);
+        CRISP_CHECK_LAUNCH();
         hipLaunchKernelGGL(pe_init_kernel, dim3(hq), dim3(1024), 0, stream, pattern, gamma,
                            s.hist_mass, s.hist_count, s.pass_ctr, s.state);
         CRISP_CHECK_LAUNCH();
@@ -960,32 +1165,26 @@ hipError_t launch_select(R q, R k, const uint8_t* pattern,
                        hq, G, s.qbar, s.kbar);
     CRISP_CHECK_LAUNCH();
     const float scale_log2 = kLog2e / sqrtf((float)kD);
-    const int fuse_softmax = nb <= 128;          // one work-group per 32 whole rows
+    const int fuse_softmax = small;              // one work-group per 32 whole rows
     hipLaunchKernelGGL(pe_logits_kernel, dim3((nb + 31) / 32, (nb + 127) / 128, hq), dim3(256), 0,
                        stream, s.qbar, s.kbar, pattern, nb, G, scale_log2, fuse_softmax, s.abar);
     CRISP_CHECK_LAUNCH();
-    if (!fuse_softmax) {
-        hipLaunchKernelGGL(pe_softmax_kernel, dim3((nb + 3) / 4, hq), dim3(256), 0, stream, pattern,
-                           nb, s.abar);
-        CRISP_CHECK_LAUNCH();
-    }
-    if (small_map) {
-        hipLaunchKernelGGL(pe_radix_small_kernel, dim3(hq), dim3(256), 0, stream, pattern, nb, gamma,
-                           s.abar, s.state);
-        CRISP_CHECK_LAUNCH();
-    } else {
-        const dim3 radix_grid((unsigned)((tri_nb + kRadixChunk - 1) / kRadixChunk), hq);
-        for (int pass = 0; pass < kRadixPasses; ++pass) {
-            hipLaunchKernelGGL(pe_radix_kernel, radix_grid, dim3(256), 0, stream, nb, pass,
-                               s.abar, s.state, s.hist_mass, s.hist_count, s.pass_ctr);
-            CRISP_CHECK_LAUNCH();
-        }
-    }
-    if (nb <= kExpandSmall) {
-        hipLaunchKernelGGL(expand_small_kernel, dim3(hq), dim3(1024), 0, stream, pattern, nb,
-                           s.bitmap, s.abar, s.state, row_ptr, col_idx, sel_counts);
+    if (small) {
+        hipLaunchKernelGGL(select_small_kernel, dim3(hq), dim3(1024), 0, stream, pattern, p_v, p_s,
+                           nb, vs, gamma, s.abar, sel_v, sel_s, sel_counts, s.state, row_ptr,
+                           col_idx);
         CRISP_CHECK_LAUNCH();
         return hipSuccess;
+    }
+    hipLaunchKernelGGL(pe_softmax_kernel, dim3((nb + 3) / 4, hq), dim3(256), 0, stream, pattern, nb,
+                       s.abar);
+    CRISP_CHECK_LAUNCH();
+    const long long tri_nb = (long long)nb * (nb + 1) / 2;
+    const dim3 radix_grid((unsigned)((tri_nb + kRadixChunk - 1) / kRadixChunk), hq);
+    for (int pass = 0; pass < kRadixPasses; ++pass) {
+        hipLaunchKernelGGL(pe_radix_kernel, radix_grid, dim3(256), 0, stream, nb, pass, s.abar,
+                           s.state, s.hist_mass, s.hist_count, s.pass_ctr);
+        CRISP_CHECK_LAUNCH();
     }
     const dim3 rows_grid((nb + kRowsPerGroup - 1) / kRowsPerGroup, hq);
     hipLaunchKernelGGL(expand_count_kernel, rows_grid, dim3(1024), 0, stream, pattern, nb, s.bitmap,

@@ -196,6 +196,51 @@ def test_one_workgroup_path_boundaries(n):
     case(synth.generate(sp), rows=P.sample_rows(nb, 4, 8, seed=n % 11), tag=f" n={n}")
 
 
+@pytest.mark.parametrize("n,gamma", [(16 * B, 0.95), (64 * B, 0.95), (64 * B, 0.5),
+                                     (128 * B, 0.95), (129 * B, 0.95), (129 * B, 0.5)])
+def test_pe_cutoff_exact_ties(n, gamma):
+    """Pooled maps made of exact ties: constant queries, and keys constant
+    inside each key block with two values alternating by block, so every row
+    of the map holds two groups of equal values.  All heads are sent down the
+    PE path (pattern 0).  The gamma cut-off lands inside a group of equal
+    values and the flat-order tie rule decides which of them are kept, so K*
+    and the kept entries must equal the oracle's exactly: the threshold
+    exemption of the other tests would hide a wrong tie rule.  N_b = 16, 64
+    and 128 take the one-work-group cut-off, 129 the multi-launch passes."""
+    hq, hkv = 2, 1
+    nb = n // B
+    q = torch.full((hq, n, 128), 1.0, dtype=torch.bfloat16)
+    q[1] = 0.5
+    k = torch.zeros((hkv, n, 128), dtype=torch.bfloat16)
+    k.view(hkv, nb, B, 128)[:, 0::2] = 0.25
+    qd, kd = q.cuda(), k.cuda()
+    ws = crisp.alloc_workspace(n, hq, hkv)
+    z = torch.zeros(hq, nb, dtype=torch.float32, device="cuda")
+    r = dict(pattern=torch.zeros(hq, dtype=torch.uint8, device="cuda"), p_v=z, p_s=z)
+    gs = P.host(P.gpu_select(qd, kd, r, 1.0, ws, opts=crisp.default_opts(gamma=gamma)))
+    tri = nb * (nb + 1) // 2
+    keep = np.tril(np.eye(nb, dtype=bool))
+    keep[:, 0] = True
+    ties_cut = 0
+    for h in range(hq):
+        ab = O.pe_map(q, k, n, hq, hkv, 128, h)
+        s = O.pe_select(ab, gamma)
+        kv, ks, kp = gs["counts"][h]
+        assert (kv, ks) == (0, 0)
+        assert int(kp) == s.kstar, (h, int(kp), s.kstar)
+        M = P.rows_matrix(gs["row_ptr"][h], gs["col_idx"], nb)
+        assert gs["row_ptr"][h][0] == h * tri
+        want = s.mask.astype(bool) | keep
+        assert np.array_equal(M, want), (h, np.argwhere(M ^ want)[:10].tolist())
+        # heads whose cut-off value is shared by entries the cut keeps and
+        # entries it drops
+        cut = s.mask.astype(bool)
+        eq = (ab.astype(np.float32) == np.float32(s.vstar)) & np.tril(np.ones((nb, nb), dtype=bool))
+        ties_cut += int((eq & cut).any() and (eq & ~cut).any())
+    assert ties_cut >= 1, "the inputs no longer cut inside a tie group"
+    P.log(f"pe ties n={n} gamma={gamma}: K* {gs['counts'][:, 2].tolist()}, cut inside a tie group on {ties_cut} heads")
+
+
 _C2 = {}
 
 
