@@ -29,7 +29,7 @@ struct Shape {
 struct Layout {
     size_t part_m, part_lo, part_up, jsd_kbar, jsd_qbar;   // route (in S)
     size_t seg_m, seg_l, row_mx, row_inv, tile_sums;       // route reduction (in S)
-    size_t qbar, kbar, abar, hist_mass, hist_count, pass_ctr, state, bitmap;   // select (in S)
+    size_t qbar, kbar, abar, hist_mass, hist_count, pass_ctr, state, bitmap, rowmask;   // select (in S)
     size_t vt, queue;                                      // attend (in S)
     size_t route_end, select_end, attend_end;              // bytes of S each stage needs
     size_t pattern, c_struct, p_v, p_s, sel_v, sel_s, counts, row_ptr, col_idx;  // P
@@ -66,13 +66,15 @@ Layout make_layout(const Shape& s)
     L.qbar = take(hq * nb * kD * sizeof(float));
     L.kbar = take(hkv * nb * kD * sizeof(float));
     L.abar = take(hq * tri * sizeof(float));
-    // the multi-launch radix select's histograms (unused for small maps)
+    // the multi-launch radix select's histograms and the expansion's
+    // membership ballots (unused for small maps)
     const size_t rx = tri > (size_t)kRadixSmall ? 1 : 0;
     L.hist_mass = take(rx * hq * kValPasses * kValBins * sizeof(unsigned long long));
     L.hist_count = take(rx * hq * kRadixPasses * kFlatBins * sizeof(uint32_t));
     L.pass_ctr = take(rx * hq * kRadixPasses * sizeof(uint32_t));
     L.state = take(hq * sizeof(PeState));
     L.bitmap = take(hq * 2 * nb);
+    L.rowmask = take(rx * hq * nb * ((nb + 63) / 64) * sizeof(unsigned long long));
     L.select_end = o;
     o = 0;
     L.vt = take(hkv * kD * (nb * kB) * sizeof(uint16_t));     // V^T padded to N_b blocks
@@ -216,6 +218,7 @@ int do_select(const Shape& s, const Opts& op, float alpha, R q, R k,
     sc.pass_ctr = at<uint32_t>(ws, L.pass_ctr);
     sc.state = at<PeState>(ws, L.state);
     sc.bitmap = at<uint8_t>(ws, L.bitmap);
+    sc.rowmask = at<unsigned long long>(ws, L.rowmask);
     VsRule vr;
     vr.rule = op.vs_rule;
     vr.alpha = alpha;

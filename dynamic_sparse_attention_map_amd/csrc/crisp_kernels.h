@@ -104,6 +104,7 @@ struct SelectScratch {
     uint32_t* pass_ctr;             // [hq][kRadixPasses]
     PeState* state;                 // [hq]
     uint8_t* bitmap;                // [hq][2][Nb]
+    unsigned long long* rowmask;    // [hq][Nb][ceil(Nb/64)] list membership ballots
 };
 
 template <class R>

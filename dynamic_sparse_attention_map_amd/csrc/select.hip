@@ -958,20 +958,29 @@ __device__ RowRule load_rule(const uint8_t* __restrict__ pattern, int nb, int h,
 }
 
 // grid (ceil(Nb / 64), hq), 1024 threads: the length of each row, written
-// into row_ptr[h][qb] (scanned in place by expand_scan_kernel).
+// into row_ptr[h][qb] (scanned in place by expand_scan_kernel), and the
+// row's membership ballots, one 64-bit word per 64 key blocks, into
+// rowmask[h][qb][0 .. ceil((qb + 1) / 64)), so that expand_fill_kernel
+// neither reads the pooled map again nor re-evaluates the rule.
 __global__ void __launch_bounds__(1024)
 expand_count_kernel(const uint8_t* __restrict__ pattern, int nb, const uint8_t* __restrict__ bitmap,
                     const float* __restrict__ abar, const PeState* __restrict__ state,
-                    int32_t* __restrict__ row_ptr)
+                    int32_t* __restrict__ row_ptr, unsigned long long* __restrict__ rowmask)
 {
     __shared__ uint8_t bmv[kMaxBlocks];
     __shared__ uint8_t bms[kMaxBlocks];
     const int h = blockIdx.y, lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const RowRule rule = load_rule(pattern, nb, h, bitmap, abar, state, bmv, bms);
+    const int nw = (nb + 63) / 64;
     const int q0 = blockIdx.x * kRowsPerGroup, q1 = min(nb, q0 + kRowsPerGroup);
     for (int qb = q0 + w; qb < q1; qb += 16) {
+        unsigned long long* m = rowmask + ((size_t)h * nb + qb) * nw;
         int c = 0;
-        for (int kb0 = 0; kb0 <= qb; kb0 += 64) c += __popcll(__ballot(rule.member(qb, kb0 + lane)));
+        for (int kb0 = 0; kb0 <= qb; kb0 += 64) {
+            const unsigned long long bal = __ballot(rule.member(qb, kb0 + lane));
+            c += __popcll(bal);
+            if (lane == 0) m[kb0 >> 6] = bal;
+        }
         if (lane == 0) row_ptr[(size_t)h * (nb + 1) + qb] = c;
     }
 }
@@ -1006,29 +1015,26 @@ expand_scan_kernel(const uint8_t* __restrict__ pattern, int nb, const PeState* _
     }
 }
 
-// grid (ceil(Nb / 64), hq), 1024 threads: ascending key blocks of each row.
+// grid (ceil(Nb / 64), hq), 1024 threads: ascending key blocks of each row,
+// from the membership ballots expand_count_kernel stored.
 __global__ void __launch_bounds__(1024)
-expand_fill_kernel(const uint8_t* __restrict__ pattern, int nb, const uint8_t* __restrict__ bitmap,
-                   const float* __restrict__ abar, const PeState* __restrict__ state,
+expand_fill_kernel(int nb, const unsigned long long* __restrict__ rowmask,
                    const int32_t* __restrict__ row_ptr, int32_t* __restrict__ col_idx)
 {
-    __shared__ uint8_t bmv[kMaxBlocks];
-    __shared__ uint8_t bms[kMaxBlocks];
     const int h = blockIdx.y, lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    const RowRule rule = load_rule(pattern, nb, h, bitmap, abar, state, bmv, bms);
     const unsigned long long below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    const int nw = (nb + 63) / 64;
     const int q0 = blockIdx.x * kRowsPerGroup, q1 = min(nb, q0 + kRowsPerGroup);
     for (int qb = q0 + w; qb < q1; qb += 16) {
+        const unsigned long long* m = rowmask + ((size_t)h * nb + qb) * nw;
         size_t pos = (size_t)row_ptr[(size_t)h * (nb + 1) + qb];
         for (int kb0 = 0; kb0 <= qb; kb0 += 64) {
-            const bool mbr = rule.member(qb, kb0 + lane);
-            const unsigned long long bal = __ballot(mbr);
-            if (mbr) col_idx[pos + __popcll(bal & below)] = kb0 + lane;
+            const unsigned long long bal = m[kb0 >> 6];
+            if ((bal >> lane) & 1ull) col_idx[pos + __popcll(bal & below)] = kb0 + lane;
             pos += __popcll(bal);
         }
     }
 }
-
 
 // The block lists of head h under `rule` by one 1024-thread block
 // (N_b <= kSelectSmall): the row lengths, their exclusive scan into
@@ -1188,13 +1194,13 @@ hipError_t launch_select(R q, R k, const uint8_t* pattern,
     }
     const dim3 rows_grid((nb + kRowsPerGroup - 1) / kRowsPerGroup, hq);
     hipLaunchKernelGGL(expand_count_kernel, rows_grid, dim3(1024), 0, stream, pattern, nb, s.bitmap,
-                       s.abar, s.state, row_ptr);
+                       s.abar, s.state, row_ptr, s.rowmask);
     CRISP_CHECK_LAUNCH();
     hipLaunchKernelGGL(expand_scan_kernel, dim3(hq), dim3(1024), 0, stream, pattern, nb, s.state,
                        row_ptr, sel_counts);
     CRISP_CHECK_LAUNCH();
-    hipLaunchKernelGGL(expand_fill_kernel, rows_grid, dim3(1024), 0, stream, pattern, nb, s.bitmap,
-                       s.abar, s.state, row_ptr, col_idx);
+    hipLaunchKernelGGL(expand_fill_kernel, rows_grid, dim3(1024), 0, stream, nb, s.rowmask, row_ptr,
+                       col_idx);
     CRISP_CHECK_LAUNCH();
 #undef CRISP_CHECK_LAUNCH
     return hipSuccess;
