@@ -99,14 +99,6 @@ __device__ void bitonic_sort(unsigned long long* keys, int np2)
 
 constexpr int kRankClip = 256;      // largest N_b whose k_min clip ranks all entries
 
-// grid (hq, 2): direction 0 = vertical (p_v), 1 = slash (p_s).  Budget rule:
-//   0  p_j > alpha * r / (N_b - 2), r = max(1 - p_0 - p_{N_b-1}, 0)   (Eq. 3-4)
-//   1  p_j > alpha * median(p_1 .. p_{N_b-2})                          (App. H)
-//   2  the shortest prefix of (p desc, j asc) whose running sum, in
-//      double, reaches gamma_vs                                        (Alg. 6)
-// then clip(k, k_min, N_b) with top-k by (p desc, j asc) for rules 0 and 1
-// (N_b <= 2 keeps every block under them) and, for rule 2, at least k_min
-// entries of the same order.  Values are compared in float.
 // LDS of one direction's budget selection; keys hold at least the power
 // of two at or above N_b.
 template <int KeyCap>
@@ -123,6 +115,14 @@ struct VsLds {
 // One direction of VS head h (p: its p_v or p_s row), by every thread of a
 // 1024-thread block: the kept blocks, ascending, into sel, their number into
 // counts[h * 3 + dir], and a 0/1 flag per block into bm (global or LDS).
+// Budget rule:
+//   0  p_j > alpha * r / (N_b - 2), r = max(1 - p_0 - p_{N_b-1}, 0)   (Eq. 3-4)
+//   1  p_j > alpha * median(p_1 .. p_{N_b-2})                          (App. H)
+//   2  the shortest prefix of (p desc, j asc) whose running sum, in
+//      double, reaches gamma_vs                                        (Alg. 6)
+// then clip(k, k_min, N_b) with top-k by (p desc, j asc) for rules 0 and 1
+// (N_b <= 2 keeps every block under them) and, for rule 2, at least k_min
+// entries of the same order.  Values are compared in float.
 template <int KeyCap>
 __device__ void vs_select_dir(VsLds<KeyCap>& L, int h, int dir, const float* __restrict__ p, int nb,
                               const VsRule& vr, int32_t* __restrict__ sel,
@@ -276,6 +276,8 @@ __device__ void vs_select_dir(VsLds<KeyCap>& L, int h, int dir, const float* __r
     if (tid == 0) counts[h * 3 + dir] = kept;
 }
 
+// grid (hq, 2): direction 0 = vertical (p_v), 1 = slash (p_s); a PE head's
+// work-groups only zero its two counts.
 __global__ void __launch_bounds__(1024)
 vs_select_kernel(const uint8_t* __restrict__ pattern, const float* __restrict__ p_v,
                  const float* __restrict__ p_s, int nb, VsRule vr,
