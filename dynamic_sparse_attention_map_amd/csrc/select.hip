@@ -977,11 +977,21 @@ expand_count_kernel(const uint8_t* __restrict__ pattern, int nb, const uint8_t* 
     const int q0 = blockIdx.x * kRowsPerGroup, q1 = min(nb, q0 + kRowsPerGroup);
     for (int qb = q0 + w; qb < q1; qb += 16) {
         unsigned long long* m = rowmask + ((size_t)h * nb + qb) * nw;
+        const int chunks = (qb >> 6) + 1;
         int c = 0;
-        for (int kb0 = 0; kb0 <= qb; kb0 += 64) {
-            const unsigned long long bal = __ballot(rule.member(qb, kb0 + lane));
-            c += __popcll(bal);
-            if (lane == 0) m[kb0 >> 6] = bal;
+        // eight chunks' tests (map reads for PE heads) in flight before the
+        // ballots consume them
+        for (int c0 = 0; c0 < chunks; c0 += 8) {
+            bool mb[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) mb[j] = c0 + j < chunks && rule.member(qb, 64 * (c0 + j) + lane);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                if (c0 + j >= chunks) break;
+                const unsigned long long bal = __ballot(mb[j]);
+                c += __popcll(bal);
+                if (lane == 0) m[c0 + j] = bal;
+            }
         }
         if (lane == 0) row_ptr[(size_t)h * (nb + 1) + qb] = c;
     }
@@ -1029,10 +1039,15 @@ expand_fill_kernel(int nb, const unsigned long long* __restrict__ rowmask,
     const int q0 = blockIdx.x * kRowsPerGroup, q1 = min(nb, q0 + kRowsPerGroup);
     for (int qb = q0 + w; qb < q1; qb += 16) {
         const unsigned long long* m = rowmask + ((size_t)h * nb + qb) * nw;
+        const int chunks = (qb >> 6) + 1;                 // at most 64 (N_b <= 4096)
+        // lane j holds the row's ballot word j: one load for the whole row
+        const unsigned long long word = lane < chunks ? m[lane] : 0ull;
         size_t pos = (size_t)row_ptr[(size_t)h * (nb + 1) + qb];
-        for (int kb0 = 0; kb0 <= qb; kb0 += 64) {
-            const unsigned long long bal = m[kb0 >> 6];
-            if ((bal >> lane) & 1ull) col_idx[pos + __popcll(bal & below)] = kb0 + lane;
+        for (int j = 0; j < chunks; ++j) {
+            const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)word, j);
+            const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(word >> 32), j);
+            const unsigned long long bal = ((unsigned long long)hi << 32) | lo;
+            if ((bal >> lane) & 1ull) col_idx[pos + __popcll(bal & below)] = 64 * j + lane;
             pos += __popcll(bal);
         }
     }
