@@ -159,6 +159,34 @@ def test_alpha_extremes(alpha):
                 assert gs["row_ptr"][h][qb + 1] - gs["row_ptr"][h][qb] == qb + 1
 
 
+@pytest.mark.parametrize("n", [32 * B, 129 * B])
+@pytest.mark.parametrize("gamma", [1.0, 0.05])
+def test_gamma_extremes(n, gamma):
+    """The PE cut-off at gamma = 1 (the fixed-point mass of the whole map may
+    fall just short of it: then every causal entry is kept) and at a small
+    gamma (a handful kept), on the one-work-group path (N_b = 32) and the
+    multi-launch path (N_b = 129): routing bits, sets and K* against the
+    oracle (Alg. 4)."""
+    sp = synth.custom_spec(n, 4, 2, [synth.VS, synth.DIFFUSE, synth.DIFFUSE, synth.VS],
+                           seed_id=80 + n // B)
+    inp = synth.generate(sp)
+    q, k, _ = P.to_dev(inp)
+    ws = crisp.alloc_workspace(n, 4, 2)
+    opts = crisp.default_opts(gamma=gamma)
+    gr = P.gpu_route(q, k, ws, opts=opts)
+    orc = O.route(inp.q, inp.k, n, 4, 2)
+    grh = P.host(gr)
+    P.check_route(grh, orc)
+    gs = P.host(P.gpu_select(q, k, gr, 1.0, ws, opts=opts))
+    rep = P.check_select(inp, grh, gs, 1.0, orc, gamma=gamma)
+    P.log(rep.line() + f" gamma={gamma} K*={gs['counts'][:, 2].tolist()}")
+    if gamma == 1.0:
+        nb = n // B
+        for h in range(4):
+            if not orc.pattern[h]:
+                assert gs["counts"][h][2] >= nb * (nb + 1) // 2 - 2, (h, gs["counts"][h])
+
+
 @pytest.mark.parametrize("alpha", [0.75, 1.25, 1.5])
 def test_alpha_sweep_values(alpha):
     """The other alpha settings the paper evaluates (Sec. 5 setup, App. E)."""
