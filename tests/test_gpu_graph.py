@@ -1,4 +1,5 @@
-"""crisp_prefill and crisp_attend_dense inside a captured HIP graph (needs an
+"""crisp_prefill, crisp_attend_dense, crisp_prefill_batch (single-launch
+path) and crisp_prefill_noalloc inside a captured HIP graph (needs an
 MI355X).
 
 Every call is asynchronous on the caller's stream and the library never
@@ -87,4 +88,68 @@ def test_dense_graph_replays_equal_eager():
         torch.cuda.synchronize()
         assert torch.equal(bits(out), bits(want)), f"replay {rep} differs from the eager call"
         crisp.crisp_prefill(q, k, v, 1.0, ws, torch.empty_like(q))
+        torch.cuda.synchronize()
+
+
+def capture(fn):
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g, stream=side):
+            fn()
+    torch.cuda.synchronize()
+    return g
+
+
+def test_batch_graph_replays_equal_eager():
+    """The single-launch batch path (sequences of one length routed and
+    selected as one layer, one attention launch, its tables written from
+    kernel arguments) captured and replayed."""
+    lens = [3000, 2048, 2048, 640]
+    devs = [dev(n, 700 + i) for i, n in enumerate(lens)]
+    others = [dev(n, 720 + i) for i, n in enumerate(lens)]
+    ws = crisp.alloc_batch_workspace(lens, HQ, HKV)
+    ws2 = crisp.alloc_batch_workspace(lens, HQ, HKV)
+    cols = lambda ds, j: [d[j] for d in ds]
+    want = [torch.empty_like(d[0]) for d in devs]
+    crisp.crisp_prefill_batch(cols(devs, 0), cols(devs, 1), cols(devs, 2), want, 1.0, ws)
+    torch.cuda.synchronize()
+    outs = [torch.zeros_like(d[0]) for d in devs]
+    g = capture(lambda: crisp.crisp_prefill_batch(cols(devs, 0), cols(devs, 1), cols(devs, 2),
+                                                  outs, 1.0, ws))
+    scratch = [torch.empty_like(d[0]) for d in devs]
+    for rep in range(3):
+        for o in outs:
+            o.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for b in range(len(lens)):
+            assert torch.equal(bits(outs[b]), bits(want[b])), f"replay {rep}, sequence {b}"
+        crisp.crisp_prefill_batch(cols(others, 0), cols(others, 1), cols(others, 2), scratch, 1.0, ws2)
+        crisp.crisp_prefill_batch(cols(others, 0), cols(others, 1), cols(others, 2), scratch, 1.0, ws)
+        torch.cuda.synchronize()
+
+
+def test_noalloc_graph_replays_equal_eager():
+    """crisp_prefill_noalloc, meant for callers under graph capture: replays
+    equal the eager call, with eager calls on other inputs in between that
+    use the same static scratch array."""
+    n = 8192 + 300
+    q, k, v = dev(n, 740)
+    q2, k2, v2 = dev(n, 741)
+    want = torch.empty_like(q)
+    crisp.crisp_prefill_noalloc(q, k, v, 1.0, want)      # also resolves the scratch address
+    torch.cuda.synchronize()
+    out = torch.zeros_like(q)
+    g = capture(lambda: crisp.crisp_prefill_noalloc(q, k, v, 1.0, out))
+    other = torch.empty_like(q2)
+    for rep in range(3):
+        out.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(bits(out), bits(want)), f"replay {rep} differs from the eager call"
+        crisp.crisp_prefill_noalloc(q2, k2, v2, 2.0, other)
         torch.cuda.synchronize()
