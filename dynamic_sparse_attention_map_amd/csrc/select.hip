@@ -666,27 +666,120 @@ __device__ void radix_resolve(int pass, size_t total, const PeState& st, const u
 // atomics contend only inside a wavefront), and, only when the cut-off key
 // is shared by entries that are not all kept, one block scan for the tie
 // (entry order in the triangular map is flat order).  Every thread calls it
-// and gets the final state; the map stays in L.vals.
+// and gets the final state; the map stays in L.vals (base == nullptr: it is
+// there already).
 constexpr int kSmallBins = 256;               // 8-bit digits
 constexpr int kSmallPasses = 4;
 constexpr int kFoldRounds = 4;
 
+constexpr int kMapSmall = 64;                 // N_b up to which the map is built here too
+constexpr int kMapPitch = kD + 1;             // LDS pitch of a pooled row (floats)
+
 struct SmallCutLds {
     float vals[kRadixSmall];
-    uint32_t wcnt[16][kSmallBins];              // per wavefront
-    unsigned long long wmass[16][kSmallBins];
-    uint32_t pcnt[4][kSmallBins];               // sums of four copies each
-    unsigned long long pmass[4][kSmallBins];
+    union {
+        struct {                                // the cut-off's histograms
+            uint32_t wcnt[16][kSmallBins];      // per wavefront
+            unsigned long long wmass[16][kSmallBins];
+            uint32_t pcnt[4][kSmallBins];       // sums of four copies each
+            unsigned long long pmass[4][kSmallBins];
+        } h;
+        struct {                                // pe_map_small's pooled rows
+            float q[kMapSmall * kMapPitch];
+            float k[kMapSmall * kMapPitch];     // then the scaled logits rows
+        } m;
+    } x;
     PeState st;
     uint32_t bin_count;                         // entries in the resolved bin
     int scan[16];
 };
 
+// The normalised pooled map of one PE head for N_b <= kMapSmall, built in
+// LDS (L.vals, triangular rows) by one 1024-thread block from its pooled
+// query rows and its KV head's pooled key rows: the same tiles, MFMA steps
+// and row reductions as pe_logits_kernel with its fused softmax, so the
+// same bits, without the map's round trip through memory or a launch of
+// its own.  Ends with a barrier.
+__device__ void pe_map_small(SmallCutLds& L, const float* __restrict__ qrows,
+                             const float* __restrict__ krows, int nb, float scale_log2)
+{
+    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, l32 = lane & 31, hi = lane >> 5;
+    constexpr int kP = kMapPitch;
+    float* qs = L.x.m.q;
+    float* ks = L.x.m.k;
+    for (int j = 0; j < 2; ++j) {               // 64 rows x 32 float4 per operand
+        const int e = tid + 1024 * j, r = e >> 5, c = 4 * (e & 31);
+        const f32x4 qv = (r < nb) ? *reinterpret_cast<const f32x4*>(qrows + (size_t)r * kD + c)
+                                  : f32x4{0.f, 0.f, 0.f, 0.f};
+        const f32x4 kv = (r < nb) ? *reinterpret_cast<const f32x4*>(krows + (size_t)r * kD + c)
+                                  : f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int x = 0; x < 4; ++x) {
+            qs[r * kP + c + x] = qv[x];
+            ks[r * kP + c + x] = kv[x];
+        }
+    }
+    __syncthreads();
+    // the causal 32 x 32 tiles (qt, kt), kt <= qt: wavefronts 0, 1, 2
+    const int tiles = nb > 32 ? 3 : 1;
+    const int qt = w == 0 ? 0 : 1, kt = w == 2 ? 1 : 0;
+    f32x16 acc = f32x16{}, acc1 = f32x16{};
+    if (w < tiles) {
+        const float* qa = qs + (32 * qt + l32) * kP + hi;
+        const float* kb_ = ks + (32 * kt + l32) * kP + hi;
+        for (int s = 0; s < kD / 2; s += 2) {
+            acc = __builtin_amdgcn_mfma_f32_32x32x2f32(qa[2 * s], kb_[2 * s], acc, 0, 0, 0);
+            acc1 = __builtin_amdgcn_mfma_f32_32x32x2f32(qa[2 * s + 2], kb_[2 * s + 2], acc1, 0, 0, 0);
+        }
+        acc += acc1;
+    }
+    __syncthreads();                              // ks is free: the logits rows
+    float* rows = ks;
+    if (w < tiles)
+        for (int r = 0; r < 16; ++r)
+            rows[(32 * qt + 8 * (r >> 2) + 4 * hi + (r & 3)) * kP + 32 * kt + l32] = acc[r] * scale_log2;
+    __syncthreads();
+    // rows w, w + 16, w + 32, w + 48, each reduced as pe_logits_kernel does
+    float m4[4];
+    double l4[4];
+    for (int j = 0; j < 4; ++j) {
+        const int qb = w + 16 * j;
+        const float* row = rows + qb * kP;
+        float m = -INFINITY;
+        if (qb < nb)
+            for (int k2 = lane; k2 <= qb; k2 += 64) m = fmaxf(m, row[k2]);
+        m4[j] = m;
+    }
+    for (int o = 32; o > 0; o >>= 1) {
+        float y[4];
+        for (int j = 0; j < 4; ++j) y[j] = __shfl_xor(m4[j], o);
+        for (int j = 0; j < 4; ++j) m4[j] = fmaxf(m4[j], y[j]);
+    }
+    for (int j = 0; j < 4; ++j) {
+        const int qb = w + 16 * j;
+        const float* row = rows + qb * kP;
+        double l = 0.0;
+        if (qb < nb)
+            for (int k2 = lane; k2 <= qb; k2 += 64) l += (double)exp2f(row[k2] - m4[j]);
+        l4[j] = l;
+    }
+    wave_sum_n(l4);
+    for (int j = 0; j < 4; ++j) {
+        const int qb = w + 16 * j;
+        if (qb >= nb) break;
+        const float* row = rows + qb * kP;
+        const double inv = 1.0 / (l4[j] * (double)nb);
+        float* out = L.vals + tri(qb);
+        for (int k2 = lane; k2 <= qb; k2 += 64) out[k2] = (float)((double)exp2f(row[k2] - m4[j]) * inv);
+    }
+    __syncthreads();                              // the histograms reuse qs / ks
+}
+
 __device__ PeState pe_cut_small(SmallCutLds& L, const float* __restrict__ base, int nb, float gamma)
 {
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int total = nb * (nb + 1) / 2;
-    for (int e = tid; e < total; e += 1024) L.vals[e] = base[e];
+    if (base)                                   // else the map is in L.vals already
+        for (int e = tid; e < total; e += 1024) L.vals[e] = base[e];
     PeState st = {};
     st.need = (unsigned long long)((double)gamma * kFix);
     // nothing reaches a zero need: only the always-kept blocks (K* = 0)
@@ -695,8 +788,8 @@ __device__ PeState pe_cut_small(SmallCutLds& L, const float* __restrict__ base, 
     for (int pass = 0; pass < kSmallPasses; ++pass) {
         const int shift = 24 - 8 * pass;
         for (int i = lane; i < kSmallBins; i += 64) {
-            L.wcnt[w][i] = 0u;
-            L.wmass[w][i] = 0ull;
+            L.x.h.wcnt[w][i] = 0u;
+            L.x.h.wmass[w][i] = 0ull;
         }
         __syncthreads();
         st = L.st;
@@ -730,15 +823,15 @@ __device__ PeState pe_cut_small(SmallCutLds& L, const float* __restrict__ base, 
                 const unsigned long long mm = __ballot(mt);
                 const unsigned long long sum = last_lane(wave_scan_incl(mt ? fx : 0ull));
                 if (lane == leader) {
-                    L.wcnt[w][ld] += (uint32_t)__popcll(mm);
-                    L.wmass[w][ld] += sum;
+                    L.x.h.wcnt[w][ld] += (uint32_t)__popcll(mm);
+                    L.x.h.wmass[w][ld] += sum;
                 }
                 act = act && !mt;
                 pend &= ~mm;
             }
             if (act) {
-                atomicAdd(&L.wcnt[w][d], 1u);
-                atomicAdd(&L.wmass[w][d], fx);
+                atomicAdd(&L.x.h.wcnt[w][d], 1u);
+                atomicAdd(&L.x.h.wmass[w][d], fx);
             }
         }
         __syncthreads();
@@ -747,11 +840,11 @@ __device__ PeState pe_cut_small(SmallCutLds& L, const float* __restrict__ base, 
             uint32_t c = 0;
             unsigned long long m = 0;
             for (int x = 4 * part; x < 4 * part + 4; ++x) {
-                c += L.wcnt[x][bin];
-                m += L.wmass[x][bin];
+                c += L.x.h.wcnt[x][bin];
+                m += L.x.h.wmass[x][bin];
             }
-            L.pcnt[part][bin] = c;
-            L.pmass[part][bin] = m;
+            L.x.h.pcnt[part][bin] = c;
+            L.x.h.pmass[part][bin] = m;
         }
         __syncthreads();
         if (w == 0) {
@@ -760,8 +853,8 @@ __device__ PeState pe_cut_small(SmallCutLds& L, const float* __restrict__ base, 
             unsigned long long m[4], m_lane = 0;
             for (int j = 0; j < 4; ++j) {
                 const int bin = 4 * lane + j;
-                c[j] = (L.pcnt[0][bin] + L.pcnt[1][bin]) + (L.pcnt[2][bin] + L.pcnt[3][bin]);
-                m[j] = (L.pmass[0][bin] + L.pmass[1][bin]) + (L.pmass[2][bin] + L.pmass[3][bin]);
+                c[j] = (L.x.h.pcnt[0][bin] + L.x.h.pcnt[1][bin]) + (L.x.h.pcnt[2][bin] + L.x.h.pcnt[3][bin]);
+                m[j] = (L.x.h.pmass[0][bin] + L.x.h.pmass[1][bin]) + (L.x.h.pmass[2][bin] + L.x.h.pmass[3][bin]);
                 c_lane += c[j];
                 m_lane += m[j];
             }
@@ -1118,15 +1211,18 @@ struct SelectSmallLds {
 };
 
 // grid hq, 1024 threads, N_b <= kSelectSmall: the whole selection of one
-// head in one work-group, after routing and the pooled map (pe_logits):
-// a VS head's two budget selections (as vs_select_kernel) or a PE head's
-// gamma cut-off (pe_cut_small; its state also goes to state[h]), then the
-// head's block lists (expand_head) from the LDS copies of the bitmaps or of
-// the map.  The same outputs as the multi-launch path.
+// head in one work-group, after routing and pooling (and, for N_b >
+// kMapSmall, the pooled map from pe_logits_kernel): a VS head's two budget
+// selections (as vs_select_kernel), or a PE head's pooled map (built here
+// for N_b <= kMapSmall, pe_map_small) and gamma cut-off (pe_cut_small; its
+// state also goes to state[h]), then the head's block lists (expand_head)
+// from the LDS copies of the bitmaps or of the map.  The same outputs as
+// the multi-launch path.
 __global__ void __launch_bounds__(1024)
 select_small_kernel(const uint8_t* __restrict__ pattern, const float* __restrict__ p_v,
                     const float* __restrict__ p_s, int nb, VsRule vr, float gamma,
-                    const float* __restrict__ abar, int32_t* __restrict__ sel_v,
+                    const float* __restrict__ qbar, const float* __restrict__ kbar, int G,
+                    float scale_log2, const float* __restrict__ abar, int32_t* __restrict__ sel_v,
                     int32_t* __restrict__ sel_s, int32_t* __restrict__ counts,
                     PeState* __restrict__ state, int32_t* __restrict__ row_ptr,
                     int32_t* __restrict__ col_idx)
@@ -1148,7 +1244,13 @@ select_small_kernel(const uint8_t* __restrict__ pattern, const float* __restrict
         vs_select_dir(L.u.vs, h, 1, p_s + (size_t)h * nb, nb, vr, sel_s + (size_t)h * nb, counts,
                       L.bms);
     } else {
-        const PeState st = pe_cut_small(L.u.cut, abar + (size_t)h * tri(nb), nb, gamma);
+        const float* map = abar + (size_t)h * tri(nb);
+        if (nb <= kMapSmall) {
+            pe_map_small(L.u.cut, qbar + (size_t)h * nb * kD, kbar + (size_t)(h / G) * nb * kD, nb,
+                         scale_log2);
+            map = nullptr;
+        }
+        const PeState st = pe_cut_small(L.u.cut, map, nb, gamma);
         if (threadIdx.x == 0) {
             state[h] = st;
             counts[h * 3] = 0;
@@ -1189,13 +1291,15 @@ hipError_t launch_select(R q, R k, const uint8_t* pattern,
     CRISP_CHECK_LAUNCH();
     const float scale_log2 = kLog2e / sqrtf((float)kD);
     const int fuse_softmax = small;              // one work-group per 32 whole rows
-    hipLaunchKernelGGL(pe_logits_kernel, dim3((nb + 31) / 32, (nb + 127) / 128, hq), dim3(256), 0,
-                       stream, s.qbar, s.kbar, pattern, nb, G, scale_log2, fuse_softmax, s.abar);
-    CRISP_CHECK_LAUNCH();
+    if (nb > kMapSmall) {                        // else select_small_kernel builds the map
+        hipLaunchKernelGGL(pe_logits_kernel, dim3((nb + 31) / 32, (nb + 127) / 128, hq), dim3(256), 0,
+                           stream, s.qbar, s.kbar, pattern, nb, G, scale_log2, fuse_softmax, s.abar);
+        CRISP_CHECK_LAUNCH();
+    }
     if (small) {
         hipLaunchKernelGGL(select_small_kernel, dim3(hq), dim3(1024), 0, stream, pattern, p_v, p_s,
-                           nb, vs, gamma, s.abar, sel_v, sel_s, sel_counts, s.state, row_ptr,
-                           col_idx);
+                           nb, vs, gamma, s.qbar, s.kbar, G, scale_log2, s.abar, sel_v, sel_s,
+                           sel_counts, s.state, row_ptr, col_idx);
         CRISP_CHECK_LAUNCH();
         return hipSuccess;
     }
