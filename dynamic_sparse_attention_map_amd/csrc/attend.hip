@@ -28,6 +28,7 @@ namespace {
 
 constexpr int kKT = 64;                   // keys per sub-tile
 constexpr int kImg = kKT * kD;            // one K or V^T sub-tile image, bf16 elements (16 KiB)
+static_assert(kImg == kVImage, "V^T image size");
 constexpr int kStageBytes = 4 * kImg;     // K image, then V^T image
 constexpr int kStages = 4;                // LDS ring depth
 
@@ -175,7 +176,7 @@ attend_pair(int b, uint16_t* lds, uint32_t* list, Rows q, Rows k,
     //   K    [64 keys][16 chunks]:  chunk c of key r at slot c ^ (r & 15)
     //   V^T  [128 d][8 chunks]:     chunk c of row d at slot c ^ ((d >> 1) & 7)
     // K is swizzled by the per-lane source address; V^T is stored in HBM as
-    // these images already (v_transpose_kernel), so its copy is contiguous.
+    // these images already (v_image_write), so its copy is contiguous.
     // Copies take a wave-uniform base (scalar registers) and a 32-bit byte
     // offset per lane.  K: lane l of copy j holds key 4 (2w + j) + l / 16 of
     // the sub-tile, chunk (l % 16) ^ (key & 15).
@@ -497,43 +498,19 @@ seq_table_kernel(SeqChunk c, SeqDesc* __restrict__ table, int* __restrict__ slot
     if (j < d.per_xcd) slot_seq[d.slot0 + j] = c.first + i;
 }
 
-// V^T as LDS-ready images, one per 64-key sub-tile: image i of KV head g
-// (keys 64 i .. 64 i + 63) holds row d (the 64 keys' values
-// of head dimension d) as 8 chunks of 8 keys, chunk c at slot c ^ ((d >> 1) & 7), and inside
-// every group of 16 keys bits 2 and 3 of the key index are swapped.  A
-// lane's 8 keys of a PV operand fragment, {4h .. 4h+3, 8+4h .. 8+4h+3} of a
-// group for lane half h (the order the S^T accumulator holds them in), are
-// then one 16-byte chunk.  Keys past n are zero.  The first work-group also
-// clears the attention kernel's eight per-XCD queue counters.
-// grid (N_b * 2, hkv), 256 threads.
+// The V^T images (layout at v_image_stage), one per work-group.  The first
+// work-group also clears the attention kernel's eight per-XCD queue
+// counters.  grid (N_b * 2, hkv), 256 threads.
 template <class R>
 __global__ void __launch_bounds__(256)
 v_transpose_kernel(R v, int n, int n_img, uint16_t* __restrict__ vt, int* __restrict__ queue)
 {
-    __shared__ uint16_t tile[64][kD + 8];
-    const int g = blockIdx.y, key0 = blockIdx.x * 64, tid = threadIdx.x;
-    if (blockIdx.x == 0 && g == 0 && tid < 8) queue[tid] = 0;
-    const uint16_t* src = v.row(g, key0);
-    for (int i = 0; i < 4; ++i) {
-        const int e = tid + 256 * i;
-        const int row = e >> 4, ch = e & 15;
-        u32x4 val = {0u, 0u, 0u, 0u};
-        if (key0 + row < n) val = *reinterpret_cast<const u32x4*>(src + row * v.st + 8 * ch);
-        *reinterpret_cast<u32x4*>(&tile[row][8 * ch]) = val;
-    }
+    __shared__ uint16_t tile[64][kVPitch];
+    const int g = blockIdx.y, i = blockIdx.x, tid = threadIdx.x;
+    if (i == 0 && g == 0 && tid < 8) queue[tid] = 0;
+    v_image_stage(v, n, g, i, tile, tid);
     __syncthreads();
-    uint16_t* dst = vt + ((size_t)g * n_img + blockIdx.x) * kImg;
-    for (int i = 0; i < 4; ++i) {
-        const int e = tid + 256 * i;                    // slot e & 7 of row d
-        const int d = e >> 3, c = (e & 7) ^ ((d >> 1) & 7);
-        u32x4 val;
-        for (int x = 0; x < 4; ++x) {
-            const int p0 = 8 * c + 2 * x;               // positions p0, p0 + 1
-            const int k0 = (p0 & ~12) | ((p0 & 4) << 1) | ((p0 & 8) >> 1);
-            val[x] = (uint32_t)tile[k0][d] | ((uint32_t)tile[k0 + 1][d] << 16);
-        }
-        *reinterpret_cast<u32x4*>(dst + 8 * e) = val;
-    }
+    v_image_write(tile, vt + ((size_t)g * n_img + i) * kVImage, tid);
 }
 
 }  // namespace

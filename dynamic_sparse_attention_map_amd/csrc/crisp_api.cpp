@@ -25,12 +25,16 @@ struct Shape {
 
 // Workspace layout.  The scratch region S is shared by the route partials,
 // the select scratch and the transposed V (stages run in that order on one
-// stream); region P after it holds crisp_prefill's intermediates.
+// stream); region P after it holds crisp_prefill's intermediates.  Up to
+// kSelectSmall key blocks crisp_prefill lays V^T out during the selection
+// launch, so its V^T (vt_pf, queue_pf) then follows the selection scratch;
+// the attention-only calls keep theirs at the start of S.
 struct Layout {
     size_t part_m, part_lo, part_up, jsd_kbar, jsd_qbar;   // route (in S)
     size_t seg_m, seg_l, row_mx, row_inv, tile_sums;       // route reduction (in S)
     size_t qbar, kbar, abar, hist_mass, hist_count, pass_ctr, state, bitmap, rowmask;   // select (in S)
     size_t vt, queue;                                      // attend (in S)
+    size_t vt_pf, queue_pf;                                // crisp_prefill's attend (in S)
     size_t route_end, select_end, attend_end;              // bytes of S each stage needs
     size_t pattern, c_struct, p_v, p_s, sel_v, sel_s, counts, row_ptr, col_idx;  // P
     size_t total;
@@ -80,9 +84,26 @@ Layout make_layout(const Shape& s)
     L.vt = take(hkv * kD * (nb * kB) * sizeof(uint16_t));     // V^T padded to N_b blocks
     L.queue = take(8 * sizeof(int));
     L.attend_end = o;
-    o = L.route_end;
+    if (select_lays_out_v(s.nb)) {
+        o = L.select_end;
+        L.vt_pf = take(hkv * kD * (nb * kB) * sizeof(uint16_t));
+        L.queue_pf = take(8 * sizeof(int));
+    } else {
+        L.vt_pf = L.vt;
+        L.queue_pf = L.queue;
+    }
+    o = std::max(o, L.route_end);
     if (L.select_end > o) o = L.select_end;
     if (L.attend_end > o) o = L.attend_end;
+    if (s.nb > kSelectSmall) {
+        // never less than a shorter layer needs (a workspace sized for the
+        // longest sequence serves every shorter one): at least S of N_b =
+        // kSelectSmall, where V^T follows the selection scratch
+        Shape t = s;
+        t.nb = kSelectSmall;
+        t.n = kSelectSmall * kB;
+        o = std::max(o, make_layout(t).pattern);
+    }
     L.pattern = take(hq);
     L.c_struct = take(hq * sizeof(float));
     L.p_v = take(hq * nb * sizeof(float));
@@ -207,7 +228,7 @@ template <class R>
 int do_select(const Shape& s, const Opts& op, float alpha, R q, R k,
               const uint8_t* pattern, const float* p_v, const float* p_s, void* ws,
               const Layout& L, int32_t* sel_v, int32_t* sel_s, int32_t* counts,
-              int32_t* row_ptr, int32_t* col_idx, hipStream_t stream)
+              int32_t* row_ptr, int32_t* col_idx, const VtJob<R>& vt, hipStream_t stream)
 {
     SelectScratch sc;
     sc.qbar = at<float>(ws, L.qbar);
@@ -225,21 +246,29 @@ int do_select(const Shape& s, const Opts& op, float alpha, R q, R k,
     vr.gamma_vs = op.gamma_vs;
     vr.kmin_blocks = op.kmin_blocks;
     return hip_status(launch_select(q, k, pattern, p_v, p_s, s.n, s.hq, s.hkv, vr, op.gamma, sc,
-                                    sel_v, sel_s, counts, row_ptr, col_idx, stream));
+                                    sel_v, sel_s, counts, row_ptr, col_idx, vt, stream));
+}
+
+// vt_ready: V^T and the cleared queue are already in place (the selection
+// launch laid them out).
+int do_attend(const Shape& s, const Operands& x, const int32_t* row_ptr, const int32_t* col_idx,
+              uint16_t* vt, int* queue, bool vt_ready, hipStream_t stream)
+{
+    mark(2, stream);
+    hipError_t e = hipSuccess;
+    if (!vt_ready && (e = launch_v_transpose(x.v, s.n, s.hkv, vt, queue, stream)) != hipSuccess)
+        return CRISP_ERR_HIP;
+    mark(3, stream);
+    e = launch_attend(x.q, x.k, vt, row_ptr, col_idx, s.n, s.hq, s.hkv, queue, x.out, stream);
+    mark(4, stream);
+    return hip_status(e);
 }
 
 int do_attend(const Shape& s, const Operands& x, const int32_t* row_ptr, const int32_t* col_idx,
               void* ws, const Layout& L, hipStream_t stream)
 {
-    uint16_t* vt = at<uint16_t>(ws, L.vt);
-    mark(2, stream);
-    hipError_t e = launch_v_transpose(x.v, s.n, s.hkv, vt, at<int>(ws, L.queue), stream);
-    if (e != hipSuccess) return CRISP_ERR_HIP;
-    mark(3, stream);
-    e = launch_attend(x.q, x.k, vt, row_ptr, col_idx, s.n, s.hq, s.hkv, at<int>(ws, L.queue), x.out,
-                      stream);
-    mark(4, stream);
-    return hip_status(e);
+    return do_attend(s, x, row_ptr, col_idx, at<uint16_t>(ws, L.vt), at<int>(ws, L.queue), false,
+                     stream);
 }
 
 // Alg. 1 for one sequence: route, select, attend; or, below the gating
@@ -261,10 +290,14 @@ int run_prefill(const Shape& s, const Opts& op, float alpha, const Operands& x, 
     int rc = do_route(s, op, x.q, x.k, ws, L, pattern, at<float>(ws, L.c_struct), p_v, p_s, st);
     if (rc) return rc;
     mark(1, st);
+    uint16_t* vt = at<uint16_t>(ws, L.vt_pf);
+    int* queue = at<int>(ws, L.queue_pf);
+    const bool fused = select_lays_out_v(s.nb);
+    const VtJob<Rows> job{x.v, fused ? vt : nullptr, queue};
     rc = do_select(s, op, alpha, x.q, x.k, pattern, p_v, p_s, ws, L, at<int32_t>(ws, L.sel_v),
-                   at<int32_t>(ws, L.sel_s), at<int32_t>(ws, L.counts), row_ptr, col_idx, st);
+                   at<int32_t>(ws, L.sel_s), at<int32_t>(ws, L.counts), row_ptr, col_idx, job, st);
     if (rc) return rc;
-    return do_attend(s, x, row_ptr, col_idx, ws, L, st);
+    return do_attend(s, x, row_ptr, col_idx, vt, queue, fused, st);
 }
 
 // element strides: positive, rows 16-byte aligned
@@ -414,25 +447,29 @@ int run_prefill_batch_fused(const crisp_seq* seqs, int batch, const crisp_stride
                            at<float>(ws, pp(i, L.p_s)), st)))
             return rc;
     }
+    int* counters = at<int>(ws, B.counters);
+    // small sparse groups lay out V^T (and clear the counters) in their selection launch
+    auto fused = [&](size_t i) { return sparse(i) && select_lays_out_v(gs[i].nb); };
     mark(1, st);
     for (size_t i = 0; i < ng; ++i) {
         if (!sparse(i)) continue;
         const Layout& L = gl[i];
+        const VtJob<SeqRows> job{gv[i], fused(i) ? at<uint16_t>(ws, B.groups[i].vt_base) : nullptr,
+                                 counters};
         if ((rc = do_select(gs[i], op, alpha, gq[i], gk[i], at<uint8_t>(ws, pp(i, L.pattern)),
                             at<float>(ws, pp(i, L.p_v)), at<float>(ws, pp(i, L.p_s)), ws, L,
                             at<int32_t>(ws, pp(i, L.sel_v)), at<int32_t>(ws, pp(i, L.sel_s)),
                             at<int32_t>(ws, pp(i, L.counts)), at<int32_t>(ws, pp(i, L.row_ptr)),
-                            at<int32_t>(ws, pp(i, L.col_idx)), st)))
+                            at<int32_t>(ws, pp(i, L.col_idx)), job, st)))
             return rc;
     }
     mark(2, st);
-    int* counters = at<int>(ws, B.counters);
     std::vector<SeqDesc> descs(batch);
     std::vector<int> live(batch, 0);
     for (size_t i = 0; i < ng; ++i) {
         const BatchGroup& g = B.groups[i];
         uint16_t* vt = at<uint16_t>(ws, g.vt_base);
-        if (launch_v_transpose(gv[i], g.n, gs[i].hkv, vt, counters, st) != hipSuccess)
+        if (!fused(i) && launch_v_transpose(gv[i], g.n, gs[i].hkv, vt, counters, st) != hipSuccess)
             return CRISP_ERR_HIP;
         const int nb = gs[i].nb;
         for (size_t j = 0; j < g.seqs.size(); ++j) {
@@ -613,7 +650,7 @@ int crisp_select(const void* q, const void* k, const uint8_t* pattern, const flo
     hipStream_t st = static_cast<hipStream_t>(stream);
     mark(1, st);
     rc = do_select(s, op, alpha, packed(q, s.n), packed(k, s.n), pattern, p_v, p_s, ws, L, sel_v,
-                   sel_s, sel_counts, row_ptr, col_idx, st);
+                   sel_s, sel_counts, row_ptr, col_idx, VtJob<Rows>{}, st);
     mark(2, st);
     return rc;
 }

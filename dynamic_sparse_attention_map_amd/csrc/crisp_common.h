@@ -186,4 +186,47 @@ __device__ __forceinline__ uint32_t lds_address(T* p)
     return (uint32_t)(uintptr_t)((__attribute__((address_space(3))) T*)p);
 }
 
+// V^T as LDS-ready images, one per 64-key sub-tile: image i of KV head g
+// (keys 64 i .. 64 i + 63, at vt + (g n_img + i) kVImage) holds row d (the
+// 64 keys' values of head dimension d) as 8 chunks of 8 keys, chunk c at
+// slot c ^ ((d >> 1) & 7), and inside every group of 16 keys bits 2 and 3 of
+// the key index are swapped.  A lane's 8 keys of a PV operand fragment,
+// {4h .. 4h+3, 8+4h .. 8+4h+3} of a group for lane half h (the order the
+// S^T accumulator holds them in), are then one 16-byte chunk.  Keys past n
+// are zero.  One image takes 256 threads (tid 0..255) and a 64 x kVPitch
+// LDS tile: v_image_stage reads the keys, and after a barrier
+// v_image_write stores the image.
+constexpr int kVPitch = kD + 8;
+
+template <class R>
+__device__ __forceinline__ void v_image_stage(const R& v, int n, int g, int i,
+                                              uint16_t (*tile)[kVPitch], int tid)
+{
+    const int key0 = 64 * i;
+    const uint16_t* src = v.row(g, key0);
+    for (int x = 0; x < 4; ++x) {
+        const int e = tid + 256 * x;
+        const int row = e >> 4, ch = e & 15;
+        u32x4 val = {0u, 0u, 0u, 0u};
+        if (key0 + row < n) val = *reinterpret_cast<const u32x4*>(src + row * v.st + 8 * ch);
+        *reinterpret_cast<u32x4*>(&tile[row][8 * ch]) = val;
+    }
+}
+
+__device__ __forceinline__ void v_image_write(const uint16_t (*tile)[kVPitch], uint16_t* __restrict__ img,
+                                              int tid)
+{
+    for (int x = 0; x < 4; ++x) {
+        const int e = tid + 256 * x;                    // slot e & 7 of row d
+        const int d = e >> 3, c = (e & 7) ^ ((d >> 1) & 7);
+        u32x4 val;
+        for (int y = 0; y < 4; ++y) {
+            const int p0 = 8 * c + 2 * y;               // positions p0, p0 + 1
+            const int k0 = (p0 & ~12) | ((p0 & 4) << 1) | ((p0 & 8) >> 1);
+            val[y] = (uint32_t)tile[k0][d] | ((uint32_t)tile[k0 + 1][d] << 16);
+        }
+        *reinterpret_cast<u32x4*>(img + 8 * e) = val;
+    }
+}
+
 }  // namespace crisp

@@ -18,6 +18,14 @@ constexpr int kRouteSegs = 64;     // tile segments per head in the routing row 
 // map entries (N_b <= 128).  The multi-launch scratch is not needed below.
 constexpr int kRouteSmall = 64;
 constexpr int kRadixSmall = 128 * 129 / 2;
+// Up to kSelectSmall key blocks the selection after pooling is one launch
+// of one work-group per head, which leaves most of the chip idle; that
+// launch also lays out V^T (launch_select's vt job) in work-groups of its
+// own, so the V^T images must not overlap the selection scratch there.
+constexpr int kSelectSmall = 128;
+inline bool select_lays_out_v(int nb) { return nb > 0 && nb <= kSelectSmall; }
+// V^T image of 64 keys of one KV head (bf16 elements); N_b blocks take 2 N_b.
+constexpr int kVImage = 64 * kD;
 
 // A bf16 operand [heads][tokens][128] with arbitrary head and token strides
 // in elements; the 128 head-dimension values of one row are contiguous.
@@ -107,12 +115,22 @@ struct SelectScratch {
     unsigned long long* rowmask;    // [hq][Nb][ceil(Nb/64)] list membership ballots
 };
 
+// V^T layout for the attention kernel riding on the selection launch
+// (vt == nullptr: none).  Done only when select_lays_out_v(N_b); it then
+// also clears queue (the attention kernel's 8 ints), as launch_v_transpose.
+template <class R>
+struct VtJob {
+    R v;
+    uint16_t* vt;
+    int* queue;
+};
+
 template <class R>
 hipError_t launch_select(R q, R k, const uint8_t* pattern,
                          const float* p_v, const float* p_s, int n, int hq, int hkv,
                          const VsRule& vs, float gamma, const SelectScratch& s, int32_t* sel_v,
                          int32_t* sel_s, int32_t* sel_counts, int32_t* row_ptr, int32_t* col_idx,
-                         hipStream_t stream);
+                         const VtJob<R>& vt, hipStream_t stream);
 
 // queue: the attention kernel's 8 ints of device scratch, cleared here.
 template <class R>

@@ -1151,7 +1151,6 @@ expand_fill_kernel(int nb, const unsigned long long* __restrict__ rowmask,
 // absolute offsets (head h's lists start at h N_b (N_b + 1) / 2), then the
 // ascending key blocks of every row; K* (0 for VS heads) into counts.  The
 // same rows, offsets and K* as expand_count, expand_scan and expand_fill.
-constexpr int kSelectSmall = 128;
 static_assert(kSelectSmall * (kSelectSmall + 1) / 2 == kRadixSmall, "one small-map bound");
 
 __device__ void expand_head(const RowRule& rule, int h, int nb, uint32_t kstar,
@@ -1210,14 +1209,25 @@ struct SelectSmallLds {
     int wsum[16];
 };
 
-// grid hq, 1024 threads, N_b <= kSelectSmall: the whole selection of one
-// head in one work-group, after routing and pooling (and, for N_b >
-// kMapSmall, the pooled map from pe_logits_kernel): a VS head's two budget
-// selections (as vs_select_kernel), or a PE head's pooled map (built here
-// for N_b <= kMapSmall, pe_map_small) and gamma cut-off (pe_cut_small; its
-// state also goes to state[h]), then the head's block lists (expand_head)
-// from the LDS copies of the bitmaps or of the map.  The same outputs as
-// the multi-launch path.
+// V^T images per work-group of select_small_kernel's layout part: one per
+// 256 threads, staged in the selection's LDS.
+constexpr int kVtPerGroup = 4;
+static_assert(kVtPerGroup * 64 * kVPitch * sizeof(uint16_t) <= sizeof(SelectSmallLds), "V^T tiles fit");
+
+// grid hq (+ the V^T layout's work-groups), 1024 threads, N_b <=
+// kSelectSmall: the whole selection of one head in one work-group, after
+// routing and pooling (and, for N_b > kMapSmall, the pooled map from
+// pe_logits_kernel): a VS head's two budget selections (as
+// vs_select_kernel), or a PE head's pooled map (built here for N_b <=
+// kMapSmall, pe_map_small) and gamma cut-off (pe_cut_small; its state also
+// goes to state[h]), then the head's block lists (expand_head) from the
+// LDS copies of the bitmaps or of the map.  The same outputs as the
+// multi-launch path.  The hq selection work-groups occupy hq compute
+// units for the launch's whole length; work-groups hq onward lay out V^T
+// meanwhile on the rest of the chip (the images v_transpose_kernel writes,
+// kVtPerGroup each; the first also clears queue), so that layout costs no
+// launch of its own.
+template <class R>
 __global__ void __launch_bounds__(1024)
 select_small_kernel(const uint8_t* __restrict__ pattern, const float* __restrict__ p_v,
                     const float* __restrict__ p_s, int nb, VsRule vr, float gamma,
@@ -1225,9 +1235,22 @@ select_small_kernel(const uint8_t* __restrict__ pattern, const float* __restrict
                     float scale_log2, const float* __restrict__ abar, int32_t* __restrict__ sel_v,
                     int32_t* __restrict__ sel_s, int32_t* __restrict__ counts,
                     PeState* __restrict__ state, int32_t* __restrict__ row_ptr,
-                    int32_t* __restrict__ col_idx)
+                    int32_t* __restrict__ col_idx, int hq, R v, int n, int hkv,
+                    uint16_t* __restrict__ vt, int* __restrict__ queue)
 {
     __shared__ SelectSmallLds L;
+    if ((int)blockIdx.x >= hq) {                 // V^T layout work-group
+        const int tid = threadIdx.x & 255, part = threadIdx.x >> 8;
+        const int n_img = 2 * nb;
+        const int img = ((int)blockIdx.x - hq) * kVtPerGroup + part;    // g n_img + i
+        uint16_t (*tile)[kVPitch] = reinterpret_cast<uint16_t (*)[kVPitch]>(&L) + 64 * part;
+        if (blockIdx.x == (unsigned)hq && threadIdx.x < 8) queue[threadIdx.x] = 0;
+        const bool live = img < hkv * n_img;
+        if (live) v_image_stage(v, n, img / n_img, img % n_img, tile, tid);
+        __syncthreads();
+        if (live) v_image_write(tile, vt + (size_t)img * kVImage, tid);
+        return;
+    }
     const int h = blockIdx.x;
     RowRule rule;
     rule.vs = pattern[h] != 0;
@@ -1271,7 +1294,7 @@ hipError_t launch_select(R q, R k, const uint8_t* pattern,
                          const float* p_v, const float* p_s, int n, int hq, int hkv,
                          const VsRule& vs, float gamma, const SelectScratch& s, int32_t* sel_v,
                          int32_t* sel_s, int32_t* sel_counts, int32_t* row_ptr, int32_t* col_idx,
-                         hipStream_t stream)
+                         const VtJob<R>& vt, hipStream_t stream)
 {
     const int nb = (n + kB - 1) / kB, G = hq / hkv;
     hipError_t e;
@@ -1297,9 +1320,11 @@ hipError_t launch_select(R q, R k, const uint8_t* pattern,
         CRISP_CHECK_LAUNCH();
     }
     if (small) {
-        hipLaunchKernelGGL(select_small_kernel, dim3(hq), dim3(1024), 0, stream, pattern, p_v, p_s,
-                           nb, vs, gamma, s.qbar, s.kbar, G, scale_log2, s.abar, sel_v, sel_s,
-                           sel_counts, s.state, row_ptr, col_idx);
+        const int vt_groups = vt.vt ? (hkv * 2 * nb + kVtPerGroup - 1) / kVtPerGroup : 0;
+        hipLaunchKernelGGL(HIP_KERNEL_NAME(select_small_kernel<R>), dim3(hq + vt_groups), dim3(1024), 0,
+                           stream, pattern, p_v, p_s, nb, vs, gamma, s.qbar, s.kbar, G, scale_log2,
+                           s.abar, sel_v, sel_s, sel_counts, s.state, row_ptr, col_idx, hq, vt.v, n,
+                           hkv, vt.vt, vt.queue);
         CRISP_CHECK_LAUNCH();
         return hipSuccess;
     }
@@ -1329,10 +1354,11 @@ hipError_t launch_select(R q, R k, const uint8_t* pattern,
 
 template hipError_t launch_select<Rows>(Rows, Rows, const uint8_t*, const float*, const float*, int,
                                         int, int, const VsRule&, float, const SelectScratch&, int32_t*,
-                                        int32_t*, int32_t*, int32_t*, int32_t*, hipStream_t);
+                                        int32_t*, int32_t*, int32_t*, int32_t*, const VtJob<Rows>&,
+                                        hipStream_t);
 template hipError_t launch_select<SeqRows>(SeqRows, SeqRows, const uint8_t*, const float*,
                                            const float*, int, int, int, const VsRule&, float,
                                            const SelectScratch&, int32_t*, int32_t*, int32_t*,
-                                           int32_t*, int32_t*, hipStream_t);
+                                           int32_t*, int32_t*, const VtJob<SeqRows>&, hipStream_t);
 
 }  // namespace crisp

@@ -50,8 +50,12 @@ def test_workspace_size_ragged(n):
     assert ws % 256 == 0
 
 
-def test_workspace_size_monotone_and_empty():
-    sizes = [ws_size(n)[1] for n in (1, 128, 129, 1000, 10000)]
+@pytest.mark.parametrize("hq,hkv", [(32, 8), (4, 1), (64, 64)])
+def test_workspace_size_monotone_and_empty(hq, hkv):
+    # also across N_b = 128 / 129, where the V^T layout moves (a batch run
+    # one sequence at a time sizes its workspace by the longest sequence)
+    lens = (1, 128, 129, 1000, 10000, 16256, 16384, 16385, 16512, 18000, 20000, 40000)
+    sizes = [ws_size(n, hq, hkv)[1] for n in lens]
     assert sizes == sorted(sizes)
     rc, ws, cap = ws_size(0)
     assert rc == OK and cap == 0
