@@ -116,7 +116,9 @@ const char *crisp_status_string(int code);
 /*
  * Worst-case sizes for one layer shape, so that no call needs a host sync.
  *   ws_bytes      workspace for crisp_prefill; it also suffices for every
- *                 other call of the same shape
+ *                 other call of the same shape, and it never decreases as
+ *                 seq_len grows (a workspace sized for the longest sequence
+ *                 serves every shorter one with the same heads)
  *   csr_capacity  col_idx entries crisp_select may write:
  *                 n_heads * N_b * (N_b + 1) / 2
  * Host-only, pure.  Returns CRISP_ERR_SHAPE / _UNSUPPORTED like the others.
