@@ -93,6 +93,25 @@ def test_c1_prefill_equals_stages():
     assert torch.equal(out.view(torch.int16), staged.view(torch.int16))
 
 
+@pytest.mark.parametrize("n,hq,hkv", [(3 * B - 5, 3, 3), (101 * B + 77, 4, 2),
+                                       (128 * B, 8, 2), (128 * B + 1, 4, 2)])
+def test_prefill_equals_stages_across_vt_switch(n, hq, hkv):
+    """Up to N_b = 128 crisp_prefill lays V^T out inside the selection launch
+    (four images per extra work-group; 3 KV heads x 6 images leave the last
+    one partial), beyond it in a launch of its own, as crisp_attend always
+    does: the same lists give the same output bits either way."""
+    pat = [synth.VS, synth.DIFFUSE] * (hq // 2) + [synth.VS] * (hq % 2)
+    inp = synth.generate(synth.custom_spec(n, hq, hkv, pat, seed_id=400 + n % 97))
+    P.log(f"prefill vs stages n={n} hq={hq} hkv={hkv}")
+    q, k, v = P.to_dev(inp)
+    ws = crisp.alloc_workspace(n, hq, hkv)
+    out = torch.empty_like(q)
+    crisp.crisp_prefill(q, k, v, 1.0, ws, out)
+    gs = P.gpu_select(q, k, P.gpu_route(q, k, ws), 1.0, ws)
+    staged = P.gpu_attend(q, k, v, gs["row_ptr"], gs["col_idx"], crisp.alloc_workspace(n, hq, hkv))
+    assert torch.equal(out.view(torch.int16), staged.view(torch.int16))
+
+
 @pytest.mark.parametrize("n", [128, 256, 384, 640])
 def test_tiny_sequences(n):
     """N_b = 1, 2 (every block kept), 3 and 5 (ragged proxy tiles)."""
