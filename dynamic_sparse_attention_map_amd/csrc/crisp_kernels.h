@@ -138,8 +138,8 @@ hipError_t launch_v_transpose(R v, int n, int hkv, uint16_t* vt, int* queue,
                               hipStream_t stream);
 
 // row_ptr / col_idx == nullptr: dense causal lists.
-// counters: 8 ints of device scratch, zero on entry (launch_v_transpose
-// clears them on the same stream).
+// counters: 8 ints of device scratch, zero on entry (launch_v_transpose, or
+// launch_select's V^T job, clears them on the same stream).
 hipError_t launch_attend(Rows q, Rows k, const uint16_t* vt,
                          const int32_t* row_ptr, const int32_t* col_idx, int n, int hq, int hkv,
                          int* counters, OutRows out, hipStream_t stream);

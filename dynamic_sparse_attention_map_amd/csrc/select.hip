@@ -12,9 +12,11 @@
 //   expand_*_kernel    per-(head, query block) key-block lists (the block
 //                      mask M_S of Eq. 1), CSR with per-head worst-case bases:
 //                      row lengths, per-head scan, fill
-//   select_small_kernel  for N_b <= 128, everything after the pooled map in
-//                      one work-group per head: a VS head's budgets or a PE
-//                      head's cut-off, then its lists
+//   select_small_kernel  for N_b <= 128, everything after pooling in one
+//                      work-group per head: a VS head's budgets, or a PE
+//                      head's map (built here for N_b <= 64) and cut-off,
+//                      then its lists; extra work-groups lay out the
+//                      attention's V^T meanwhile
 //
 // Decisions are taken in float in the order the paper writes them; the
 // pooled masses are summed in 2^-62 fixed point, which is exact and
