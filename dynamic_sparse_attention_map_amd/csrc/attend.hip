@@ -21,6 +21,7 @@
 // below).
 #include "crisp_common.h"
 #include "crisp_kernels.h"
+#include "work_order.h"
 
 namespace crisp {
 
@@ -35,65 +36,18 @@ constexpr int kStages = 4;                // LDS ring depth
 constexpr int kThreads = 512;             // 8 wavefronts: two query blocks x 4
 
 constexpr int kListWords = kMaxBlocks / 32;   // bitmap words per row
-// Run length of one head's pairs on an XCD: a whole head when it has at most
-// kWholeHeadPairs pairs, else kPairRun; never so long that an XCD is left
-// without a chunk of its own (fewer KV heads than XCDs).  Measured at 1024
-// and 4096 blocks: whole heads were 0.9% faster at 1024, runs of 256 0.2%
-// faster than 512 or 1024 at 4096.
-constexpr int kPairRun = 256;
-constexpr int kWholeHeadPairs = 512;
-// Pair-major order (below) while one KV head's K and V^T take at most this
-// many bytes (16384 tokens at head_dim 128).  Measured against head-major:
-// -7% at 8192 tokens, -3% at 16384, +4% at 32768, +13% at 131072.
-constexpr long long kPairMajorKvBytes = 8ll << 20;
-// Pair-major runs are this many pairs, and chunk c takes KV head
-// (c + c / hkv) % hkv (below), so that each XCD walks the KV groups in turn
-// instead of serving one group for the whole launch: with few items per
-// work-group, the groups' unequal totals otherwise leave some XCDs idle at
-// the end.  Measured against one run per head: -0.5% at 4096 tokens, -1.6%
-// at 8192, -3.4% at 12288, -2.1% at 16384 (runs of 4: -0.8%, -2.0%, -3.1%,
-// -1.3%).  Head-major order keeps each group on its XCD: the same rotation
-// there, with runs of 64-256 pairs, was 0.5-1.4% slower at 65536 and
-// 131072 tokens (L2 reuse within a group counts more there).
-constexpr int kPairMajorRun = 8;
 
-// Work items.  Pair p is query blocks Nb-1-2p and Nb-2-2p.  A chunk is `run`
-// consecutive pairs of the G query heads of one KV head: chunk c covers KV
-// head c % hkv (pair-major: (c % hkv + c / hkv) % hkv) and pairs
-// run * (c / hkv) onward, and holds its G x run items
-// head-major (one head's run of pairs, then the next head's), or for short
-// sequences pair-major (the G heads' pair p, then their pair p + 1).  Item b belongs
-// to XCD b % 8; its j = b / 8-th slot there is item j % (G run) of chunk
-// (j / (G run)) * 8 + b % 8.  In head-major order each XCD keeps whole GQA
-// groups and walks the pairs from the longest causal rows down in runs, and
-// the work-groups of an XCD start one head's adjacent pairs close together
-// in time: their lists
-// are alike, they walk them in step, and all but the first find most K/V
-// tiles in L2.  (Interleaving the heads instead, pair by pair, leaves almost
-// no reuse: the long rows of diffuse heads start far apart in time.)  XCD x
-// starts its chunks' heads at head x % G: vertical-slash heads, with short,
-// scattered lists, miss L2 far more often than diffuse heads, and this keeps
-// the XCDs from all running them at the same time.  (Runs inside a chunk are
-// rotated, never reordered across chunks, so the walk from the longest rows
-// down is kept.)  When a KV head's K and V fit in an XCD's L2
-// whatever the order, pair-major is the better schedule: it hands out the
-// longest items of all G heads first, so no head's long rows start late;
-// its chunks are short and rotate over the KV groups (kPairMajorRun).
+// One work item: the two query blocks of pair it.pair of head it.h (the
+// order is in work_order.h).
 __device__ __forceinline__ void
 attend_pair(int b, uint16_t* lds, uint32_t* list, Rows q, Rows k,
             const uint16_t* __restrict__ vt, const int32_t* __restrict__ row_ptr,
             const int32_t* __restrict__ col_idx, int n, int nb, int hkv, int G, int run,
             bool pair_major, float scale_log2, OutRows out)
 {
-    const int npairs = (nb + 1) >> 1;
-    const int slot = b >> 3;
-    const int per_chunk = G * run;
-    const int chunk = (slot / per_chunk) * 8 + (b & 7);
-    const int r = slot % per_chunk;
-    const int pair = (chunk / hkv) * run + (pair_major ? r / G : r % run);
-    if (pair >= npairs) return;
-    const int g = (chunk % hkv + (pair_major ? chunk / hkv : 0)) % hkv;
-    const int h = g * G + ((pair_major ? r % G : r / run) + (b & 7)) % G;
+    WorkItem it;
+    if (!work_item(b, nb, hkv, G, run, pair_major, &it)) return;
+    const int pair = it.pair, g = it.g, h = it.h;
     const int qb_hi = nb - 1 - 2 * pair;
     const int qb_lo = qb_hi - 1;                   // -1: no second block
 
@@ -539,18 +493,10 @@ hipError_t launch_v_transpose(R v, int n, int hkv, uint16_t* vt, int* queue, hip
 
 void attend_plan(int n, int hq, int hkv, int* run_out, int* per_xcd_out, int* pair_major_out)
 {
-    const int nb = (n + kB - 1) / kB, G = hq / hkv;
-    const int npairs = (nb + 1) / 2;
-    const bool pair_major = (long long)n * kD * 4 <= kPairMajorKvBytes;
-    int run = npairs <= kWholeHeadPairs ? npairs : kPairRun;
-    if (pair_major && run > kPairMajorRun) run = kPairMajorRun;
-    if (run > npairs * hkv / 8) run = npairs * hkv / 8;
-    if (run < 1) run = 1;
-    const long long chunks = (long long)((npairs + run - 1) / run) * hkv;
-    const long long items = ((chunks + 7) / 8) * 8 * G * run;
-    *run_out = run;
-    *per_xcd_out = (int)(items / 8);
-    *pair_major_out = pair_major;
+    const WorkPlan w = work_plan(n, hq, hkv);
+    *run_out = w.run;
+    *per_xcd_out = w.per_xcd;
+    *pair_major_out = w.pair_major;
 }
 
 namespace {
