@@ -8,8 +8,9 @@
 // permuted so that each operand fragment is one 16-byte read; both with
 // XOR-swizzled chunks), and each wavefront whose block lists the tile runs
 //     S^T = K Q^T          (32x32x16 bf16 MFMA, fp32 accumulate)
-//     online softmax       (exp2 domain, fp32 running max / sum)
+//     online softmax       (exp2 domain, fp32 running max)
 //     O^T += V^T P^T       (P rounded to bf16, fp32 accumulate)
+//     l   += SEL P^T       (row sums of the same bf16 P, 16x16x32 MFMA)
 // Computing S^T rather than S leaves each lane holding one query's scores
 // in exactly the register order the P^T operand of the second product
 // needs, so P never leaves registers.  The causal mask is applied only on
@@ -129,7 +130,24 @@ attend_pair(int b, uint16_t* lds, uint32_t* list, Rows q, Rows k,
 
     f32x16 o[4];
     for (int dt = 0; dt < 4; ++dt) o[dt] = f32x16{};
-    float m_run = -INFINITY, l_run = 0.f;
+    float m_run = -INFINITY;
+    // Row sums on the matrix cores, so that the vector phase (the co-bound
+    // with the products) has no additions: lsum += SEL P^T with P^T[u] as a
+    // 32x16 operand of a 16x16x32 product.  Its k-slots 8 (l / 16) .. +7 are
+    // lane l's eight probabilities of query l % 32, so the k-groups 0 and 2
+    // hold queries 0-15 (both key halves) and the groups 1 and 3 queries
+    // 16-31.  SEL row 0 is 1 on groups 0 and 2, row 1 on groups 1 and 3 and
+    // every other row 0: lane q < 16 then holds the sum of query q in
+    // lsum[0] and of query q + 16 in lsum[1], and every other element stays
+    // 0.  These are sums of the bf16 probabilities the PV product uses, so
+    // the weights of a row sum to one exactly as the products see them.
+    f32x4 lsum = f32x4{};
+    bf16x8 sel;
+    {
+        const int m = lane & 15, par = (lane >> 4) & 1;
+        const __bf16 one = (__bf16)(((m == 0 && par == 0) || (m == 1 && par == 1)) ? 1.0f : 0.0f);
+        for (int j = 0; j < 8; ++j) sel[j] = one;
+    }
     const float rescale_gap = 8.0f / scale_log2;   // 2^8 in probability
 
     const uint16_t* kg = k.row(g, 0);
@@ -250,7 +268,8 @@ attend_pair(int b, uint16_t* lds, uint32_t* list, Rows q, Rows k,
             const float alpha = (m_run == -INFINITY) ? 0.f
                               : __builtin_amdgcn_exp2f((m_run - m_new) * scale_log2);
             m_run = m_new;
-            l_run *= alpha;
+            lsum[0] *= alpha;                          // query l32 (lanes < 16)
+            lsum[1] *= __shfl_down(alpha, 16);         // query l32 + 16
             for (int dt = 0; dt < 4; ++dt)
                 for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
         }
@@ -261,14 +280,9 @@ attend_pair(int b, uint16_t* lds, uint32_t* list, Rows q, Rows k,
     bf16x8 pf[4];
     auto probs = [&]() {
         const float neg_mc = (m_run == -INFINITY) ? 0.f : -m_run * scale_log2;
-        float acc[4] = {0.f, 0.f, 0.f, 0.f};
         for (int u = 0; u < 4; ++u)            // key group u: s[u >> 1][8 (u & 1) .. +7]
-            for (int j = 0; j < 8; ++j) {
-                const float p = __builtin_amdgcn_exp2f(fmaf(s[u >> 1][8 * (u & 1) + j], scale_log2, neg_mc));
-                acc[j & 3] += p;
-                pf[u][j] = (__bf16)p;
-            }
-        l_run += (acc[0] + acc[1]) + (acc[2] + acc[3]);
+            for (int j = 0; j < 8; ++j)
+                pf[u][j] = (__bf16)__builtin_amdgcn_exp2f(fmaf(s[u >> 1][8 * (u & 1) + j], scale_log2, neg_mc));
     };
     // O^T += V^T P^T for the tile in `stage`
     auto pv_mfma = [&](int stage) {
@@ -277,14 +291,16 @@ attend_pair(int b, uint16_t* lds, uint32_t* list, Rows q, Rows k,
         for (int u = 0; u < 4; ++u)
             for (int dt = 0; dt < 4; ++dt)
                 vf[4 * u + dt] = *reinterpret_cast<const bf16x8*>(vbase + 32 * dt * kKT + 8 * ((2 * u + hi) ^ vx));
-        for (int u = 0; u < 4; ++u)
+        for (int u = 0; u < 4; ++u) {
+            lsum = mfma16(sel, pf[u], lsum);
             for (int dt = 0; dt < 4; ++dt) o[dt] = mfma32(vf[4 * u + dt], pf[u], o[dt]);
+        }
         __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 6, 0);
         for (int i = 0; i < 10; ++i) {
             __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
             __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
         }
-        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 6, 0);
+        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 10, 0);
     };
 
     // Schedule.  Per tile t every wavefront runs a matrix phase M_t = PV(t-1)
@@ -347,7 +363,9 @@ attend_pair(int b, uint16_t* lds, uint32_t* list, Rows q, Rows k,
     }
 
     if (!active) return;
-    const float l = l_run + swap_half(l_run);
+    // the row sum of query l32 from the lane that holds it
+    const float l0 = __shfl(lsum[0], l32 & 15), l1 = __shfl(lsum[1], l32 & 15);
+    const float l = (l32 < 16) ? l0 : l1;
     if (!q_valid) return;             // after the wave-wide exchange above
     const float inv = (l > 0.f) ? 1.0f / l : 0.f;
     uint16_t* orow = out.row(h, qpos);

@@ -34,6 +34,15 @@ __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c)
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
+// D = A(16x32) * B(32x16) + C on the bf16 matrix cores.  Operand layout
+// (checked on gfx950): lane l holds A[l%16][8*(l/16) .. +7] and
+// B[8*(l/16) .. +7][l%16]; C/D register r of lane l is element
+// (4*(l/16) + r, l%16).
+__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
 // Value held by lane l ^ 32 (the other half of the wavefront).
 __device__ __forceinline__ float swap_half(float x)
 {
