@@ -223,7 +223,7 @@ attend_pair(int b, uint16_t* lds, uint32_t* list, Rows q, Rows k,
     const int kx = l32 & 15, vx = (l32 >> 1) & 7;   // this lane's swizzles
     f32x16 s[2];
     // S^T = K Q^T for the tile in `stage`.  The 16 K fragments are read in
-    // the order the matrix cores consume them, six reads ahead.
+    // the order the matrix cores consume them, four reads ahead.
     auto qk = [&](int stage) {
         const uint16_t* kbase = lds + stage * (kStageBytes / 2) + l32 * kD;
         bf16x8 kf[16];
@@ -234,12 +234,12 @@ attend_pair(int b, uint16_t* lds, uint32_t* list, Rows q, Rows k,
         s[0] = f32x16{};
         s[1] = f32x16{};
         for (int i = 0; i < 16; ++i) s[i & 1] = mfma32(kf[i], qf[i >> 1], s[i & 1]);
-        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 6, 0);
-        for (int i = 0; i < 10; ++i) {
+        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 4, 0);
+        for (int i = 0; i < 12; ++i) {
             __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
             __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
         }
-        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 6, 0);
+        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 4, 0);
     };
     // causal mask on the diagonal block (wave-uniform branch around it)
     auto mask = [&](int sub) {
@@ -284,23 +284,25 @@ attend_pair(int b, uint16_t* lds, uint32_t* list, Rows q, Rows k,
             for (int j = 0; j < 8; ++j)
                 pf[u][j] = (__bf16)__builtin_amdgcn_exp2f(fmaf(s[u >> 1][8 * (u & 1) + j], scale_log2, neg_mc));
     };
-    // O^T += V^T P^T for the tile in `stage`
+    // O^T += V^T P^T for the tile in `stage`, and the row sums.  The four
+    // row-sum products need no LDS operand, so they go first and cover the
+    // latency of the first V^T fragment reads (then four reads ahead).
     auto pv_mfma = [&](int stage) {
         const uint16_t* vbase = lds + stage * (kStageBytes / 2) + kImg + l32 * kKT;
         bf16x8 vf[16];                       // vf[4 u + dt]
         for (int u = 0; u < 4; ++u)
             for (int dt = 0; dt < 4; ++dt)
                 vf[4 * u + dt] = *reinterpret_cast<const bf16x8*>(vbase + 32 * dt * kKT + 8 * ((2 * u + hi) ^ vx));
-        for (int u = 0; u < 4; ++u) {
-            lsum = mfma16(sel, pf[u], lsum);
+        for (int u = 0; u < 4; ++u) lsum = mfma16(sel, pf[u], lsum);
+        for (int u = 0; u < 4; ++u)
             for (int dt = 0; dt < 4; ++dt) o[dt] = mfma32(vf[4 * u + dt], pf[u], o[dt]);
-        }
-        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 6, 0);
-        for (int i = 0; i < 10; ++i) {
+        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 4, 0);
+        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 4, 0);
+        for (int i = 0; i < 12; ++i) {
             __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
             __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
         }
-        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 10, 0);
+        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 4, 0);
     };
 
     // Schedule.  Per tile t every wavefront runs a matrix phase M_t = PV(t-1)
