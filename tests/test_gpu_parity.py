@@ -81,6 +81,43 @@ def test_c1_dense_matches_oracle():
     assert torch.equal(out.view(torch.int16), out2.view(torch.int16))
 
 
+@pytest.mark.parametrize("beta", [1.2, 0.5])
+def test_running_max_rescale(beta):
+    """Scores that grow along the keys: q_i . k_j is close to f_i * beta * j,
+    with f_i from 0.6 to 1.4 by the row's position i % 32 within its
+    wavefront's 32 queries.  The running max of a row then grows by about
+    f_i * beta * 64 raw units per 64-key sub-tile: with beta = 1.2 that is
+    46-108 units around the 2^8 lazy-rescale gap (about 63), with beta = 0.5
+    19-45 units, so rows are rescaled on every sub-tile, every other one or
+    less often, with probabilities up to 2^8 in between, and the rescale
+    factors differ between the rows q and q + 16 whose row sums one lane
+    holds.  Dense attention against the oracle on every row."""
+    n, hq, hkv = 2048, 4, 1
+    nb = n // B
+    rng = np.random.default_rng(1234 + int(beta * 10))
+    u = rng.standard_normal(128)
+    u /= np.linalg.norm(u)
+    f = 0.6 + 0.8 * (np.arange(n) % 32) / 31.0
+    q = (8.0 * f)[None, :, None] * u[None, None, :] + 0.01 * rng.standard_normal((hq, n, 128))
+    j = np.arange(n, dtype=np.float64)
+    k = (beta * j / 8.0)[None, :, None] * u[None, None, :] + 0.01 * rng.standard_normal((hkv, n, 128))
+    v = rng.standard_normal((hkv, n, 128))
+    qt, kt, vt = (torch.from_numpy(x).to(torch.bfloat16) for x in (q, k, v))
+    dq, dk, dv = qt.cuda(), kt.cuda(), vt.cuda()
+    ws = crisp.alloc_workspace(n, hq, hkv)
+    out = torch.empty_like(dq)
+    crisp.crisp_attend_dense(dq, dk, dv, ws, out)
+    rp, ci = O.full_causal_lists(hq, nb)
+    rows = np.arange(hq * nb, dtype=np.int32)
+    want = O.attend(qt, kt, vt, n, hq, hkv, 128, rp, ci, rows)
+    got = out.float().cpu().numpy().reshape(hq * nb, B, 128)
+    P.check_outputs(got, want, f"rescale beta={beta}")
+    # the weights of a late row spread over several keys (not one key alone)
+    sc = (q[0, n - 1] @ k[0].T) / np.sqrt(128.0)
+    w = np.exp(sc - sc.max())
+    assert (w / w.sum()).max() < 0.5
+
+
 def test_c1_prefill_equals_stages():
     inp = synth.generate(synth.config_spec("c1"))
     r = case(inp)
