@@ -369,6 +369,27 @@ def generate(spec: Spec, threads: int = 8) -> Inputs:
     return Inputs(q, k, v, spec, stripe_pos, cluster, boosts)
 
 
+def growing_scores(n: int, hq: int, hkv: int, beta: float, seed: int):
+    """Q, K, V (CPU bfloat16, [heads, n, 128]) whose logits grow along the keys:
+    q_i . k_j is close to f_i * beta * j, with f_i from 0.6 to 1.4 by the
+    row's position i % 32 (so neighbouring rows of a 32-row group grow at
+    different rates).  All queries and keys point along one random unit
+    direction u (query norms 8 f_i, key norms beta * j / 8), plus i.i.d. noise
+    of 0.01 per channel; V is i.i.d. N(0, 1).  A row's largest logit among
+    keys 0 .. i is then near its last key, so a block-by-block pass over the
+    keys sees the running maximum grow at every step."""
+    import torch
+    rng = np.random.default_rng(seed)
+    u = rng.standard_normal(D)
+    u /= np.linalg.norm(u)
+    f = 0.6 + 0.8 * (np.arange(n) % 32) / 31.0
+    q = (8.0 * f)[None, :, None] * u[None, None, :] + 0.01 * rng.standard_normal((hq, n, D))
+    j = np.arange(n, dtype=np.float64)
+    k = (beta * j / 8.0)[None, :, None] * u[None, None, :] + 0.01 * rng.standard_normal((hkv, n, D))
+    v = rng.standard_normal((hkv, n, D))
+    return tuple(torch.from_numpy(x).to(torch.bfloat16) for x in (q, k, v))
+
+
 def bf16_bits(t):
     """Raw bf16 bit patterns of a CPU bfloat16 tensor as a uint16 numpy array."""
     import torch

@@ -138,3 +138,24 @@ def test_noise_accumulation_grows_with_n(cliff_sweep):
     # alpha = 0.5 puts the floor under the background: everything passes
     e = cliff_sweep[NS[0]]
     assert len(O.vs_select(e["route"].p_v[1], 0.5).sel) == NS[0] // B
+
+
+@pytest.mark.parametrize("beta,lo,hi", [(1.2, 5.5, 14.0), (0.5, 2.2, 6.0)])
+def test_growing_scores_premise(beta, lo, hi):
+    """The inputs of the running-max rescale test: per 64-key step a row's
+    largest logit grows by f_i * beta * 64 raw units, i.e. between lo and hi
+    in log2 units (the kernel rescales when the growth passes 8), the rates
+    of rows q and q + 16 of a 32-row group differ, and a late row's softmax
+    spreads over several keys."""
+    n = 2048
+    q, k, _ = synth.growing_scores(n, 4, 1, beta, seed=1234 + int(beta * 10))
+    qf, kf = q[0].double().numpy(), k[0].double().numpy()
+    c = np.log2(np.e) / np.sqrt(128.0)
+    g = np.array([(qf[i] @ kf[64 * 20] - qf[i] @ kf[64 * 19]) * c for i in range(32)])
+    assert g.min() > lo and g.max() < hi, (g.min(), g.max())
+    assert np.all(g[16:] - g[:16] > 0.3)
+    if beta > 1:
+        assert g.max() > 8.0 and g.min() < 8.0      # some rows rescale on every step, some not
+    sc = (qf[n - 1] @ kf.T) / np.sqrt(128.0)
+    w = np.exp(sc - sc.max())
+    assert (w / w.sum()).max() < 0.5
